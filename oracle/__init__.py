@@ -1,0 +1,241 @@
+"""CPU oracle of the FIFO send/recv data plane (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  It wraps ``oracle.c`` (plain C, built with gcc
+into ``liboracle.so`` next to it) through ctypes and shares no code with the
+GPU library.  See the header comment of ``oracle.c`` for what is modelled and
+for every reading taken where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+SIMPLE, LL, ZC = 0, 1, 2
+PROTO_NAMES = {"simple": SIMPLE, "ll": LL, "zc": ZC, "zerocopy": ZC}
+
+OP_RECV_SETUP, OP_SEND_SETUP, OP_CONNECT_BATCH = 0, 1, 2
+
+MUT = {
+    "none": 0,
+    "weak_credit": 1,
+    "early_tail": 2,
+    "no_acquire": 3,
+    "torn_line": 4,
+    "zc_no_wait": 5,
+    "zc_no_reset": 6,
+    "early_head": 7,
+}
+VIOLATIONS = {
+    0: "ok",
+    1: "overwrite",
+    2: "read_unfilled",
+    3: "read_early",
+    4: "window",
+    5: "wrong_ptr",
+    6: "deadlock",
+    7: "result",
+    8: "counters",
+    9: "confluence",
+    10: "state_limit",
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc."""
+    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+        return LIB
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-o", tmp, SRC]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+class _EnumResult(C.Structure):
+    _fields_ = [
+        ("states", C.c_uint64),
+        ("terminals", C.c_uint64),
+        ("transitions", C.c_uint64),
+        ("violation", C.c_int),
+        ("channel", C.c_int),
+        ("msg", C.c_char * 256),
+    ]
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+                build()
+            L = C.CDLL(LIB)
+            u64p = C.POINTER(C.c_uint64)
+            ip = C.POINTER(C.c_int)
+            vp = C.c_void_p
+            L.orc_peers.argtypes = [C.c_int, C.c_int, C.c_int, ip, ip]
+            L.orc_ring_masks.argtypes = [C.c_int, C.c_int, C.c_int, u64p, u64p]
+            L.orc_plan.argtypes = [C.c_int, C.c_int, u64p, u64p, C.c_int, ip, C.c_int, ip]
+            L.orc_step_bytes.argtypes = [C.c_int, C.c_uint64]
+            L.orc_step_bytes.restype = C.c_uint64
+            L.orc_partition.argtypes = [C.c_uint64, C.c_int, u64p, u64p]
+            L.orc_conn_new.argtypes = [C.c_int, C.c_int, C.c_int, C.c_uint64]
+            L.orc_conn_new.restype = vp
+            L.orc_conn_free.argtypes = [vp]
+            L.orc_conn_set_mutation.argtypes = [vp, C.c_int]
+            L.orc_run.argtypes = [vp, vp, vp, C.c_uint64]
+            L.orc_run_pingpong.argtypes = [vp, vp, vp, vp, vp, C.c_uint64, C.c_int]
+            L.orc_conn_state.argtypes = [vp, C.c_int, u64p]
+            L.orc_conn_fifo.argtypes = [vp, C.c_int, u64p]
+            L.orc_conn_fifo.restype = vp
+            L.orc_enumerate.argtypes = [C.c_int, C.c_int, C.c_int, C.c_uint64, vp, C.c_uint64,
+                                        C.c_int, C.c_int, C.c_uint64, C.POINTER(_EnumResult)]
+            _lib = L
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        name = VIOLATIONS.get(rc, "error %d" % rc)
+        raise OracleError("%s failed: %s (%d)" % (what, name, rc))
+
+
+def _proto(p) -> int:
+    return PROTO_NAMES[p] if isinstance(p, str) else int(p)
+
+
+def _ptr(a: np.ndarray):
+    return C.c_void_p(a.ctypes.data) if a.size else C.c_void_p(0)
+
+
+# ---------------------------------------------------------------- schedule
+def peers(rank: int, nranks: int, i: int) -> tuple[int, int]:
+    r, s = C.c_int(), C.c_int()
+    _check(lib().orc_peers(rank, nranks, i, C.byref(r), C.byref(s)), "orc_peers")
+    return r.value, s.value
+
+
+def ring_masks(rank: int, nranks: int, nchannels: int) -> tuple[np.ndarray, np.ndarray]:
+    rm = np.zeros(nranks, dtype=np.uint64)
+    sm = np.zeros(nranks, dtype=np.uint64)
+    u64p = C.POINTER(C.c_uint64)
+    _check(lib().orc_ring_masks(rank, nranks, nchannels, rm.ctypes.data_as(u64p),
+                                sm.ctypes.data_as(u64p)), "orc_ring_masks")
+    return rm, sm
+
+
+def plan(rank: int, nranks: int, recv_mask, send_mask, max_peers: int = 128) -> list[tuple[int, int, int]]:
+    rm = np.ascontiguousarray(recv_mask, dtype=np.uint64)
+    sm = np.ascontiguousarray(send_mask, dtype=np.uint64)
+    u64p = C.POINTER(C.c_uint64)
+    n = C.c_int()
+    rc = lib().orc_plan(rank, nranks, rm.ctypes.data_as(u64p), sm.ctypes.data_as(u64p), max_peers,
+                        None, 0, C.byref(n))
+    if rc not in (0, -4):
+        _check(rc, "orc_plan")
+    ops = np.zeros(3 * max(n.value, 1), dtype=np.int32)
+    _check(lib().orc_plan(rank, nranks, rm.ctypes.data_as(u64p), sm.ctypes.data_as(u64p), max_peers,
+                          ops.ctypes.data_as(C.POINTER(C.c_int)), n.value, C.byref(n)), "orc_plan")
+    return [tuple(int(x) for x in ops[3 * k:3 * k + 3]) for k in range(n.value)]
+
+
+# ---------------------------------------------------------------- partition
+def step_bytes(proto, slot_bytes: int) -> int:
+    return int(lib().orc_step_bytes(_proto(proto), slot_bytes))
+
+
+def partition(nbytes: int, nchannels: int) -> tuple[list[int], list[int]]:
+    b = np.zeros(nchannels, dtype=np.uint64)
+    ln = np.zeros(nchannels, dtype=np.uint64)
+    u64p = C.POINTER(C.c_uint64)
+    _check(lib().orc_partition(nbytes, nchannels, b.ctypes.data_as(u64p), ln.ctypes.data_as(u64p)),
+           "orc_partition")
+    return [int(x) for x in b], [int(x) for x in ln]
+
+
+# ---------------------------------------------------------------- protocol
+class Conn:
+    """A simulated connection; its counters and FIFO persist across runs."""
+
+    def __init__(self, proto, nchannels: int, nslots: int, slot_bytes: int):
+        self.proto = _proto(proto)
+        self.nchannels = nchannels
+        self.nslots = nslots
+        self.slot_bytes = slot_bytes
+        self._h = lib().orc_conn_new(self.proto, nchannels, nslots, slot_bytes)
+        if not self._h:
+            raise OracleError("orc_conn_new rejected its arguments")
+
+    def close(self) -> None:
+        if self._h:
+            lib().orc_conn_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_mutation(self, name: str) -> None:
+        lib().orc_conn_set_mutation(self._h, MUT[name])
+
+    def run(self, A: np.ndarray, B: np.ndarray, nbytes: int | None = None) -> None:
+        """Transfer A[:n] into B[:n] (both uint8 arrays, modified in place)."""
+        n = A.size if nbytes is None else int(nbytes)
+        assert A.dtype == np.uint8 and B.dtype == np.uint8 and A.size >= n and B.size >= n
+        assert A.flags.c_contiguous and B.flags.c_contiguous
+        _check(lib().orc_run(self._h, _ptr(A), _ptr(B), n), "orc_run")
+
+    def state(self, channel: int) -> dict:
+        out = (C.c_uint64 * 4)()
+        _check(lib().orc_conn_state(self._h, channel, out), "orc_conn_state")
+        return {"head": out[0], "tail": out[1], "ptr_exchange": out[2], "steps": out[3]}
+
+    def fifo(self, channel: int) -> np.ndarray:
+        n = C.c_uint64()
+        p = lib().orc_conn_fifo(self._h, channel, C.byref(n))
+        if not p:
+            return np.zeros(0, dtype=np.uint8)
+        return np.ctypeslib.as_array((C.c_uint8 * n.value).from_address(p)).copy()
+
+
+def run_pingpong(fwd: Conn, rev: Conn, a: np.ndarray, b: np.ndarray, c: np.ndarray,
+                 nbytes: int, iters: int) -> None:
+    _check(lib().orc_run_pingpong(fwd._h, rev._h, _ptr(a), _ptr(b), _ptr(c), nbytes, iters),
+           "orc_run_pingpong")
+
+
+def enumerate_interleavings(proto, nchannels: int, nslots: int, slot_bytes: int, A: np.ndarray,
+                            mutation: str = "none", prior_runs: int = 0,
+                            max_states: int = 2_000_000) -> dict:
+    """Every interleaving of one transfer of A; returns counts and the first violation."""
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    res = _EnumResult()
+    rc = lib().orc_enumerate(_proto(proto), nchannels, nslots, slot_bytes, _ptr(A), A.size,
+                             MUT[mutation], prior_runs, max_states, C.byref(res))
+    if rc != 0:
+        raise OracleError("orc_enumerate error %d" % rc)
+    return {
+        "states": res.states,
+        "terminals": res.terminals,
+        "transitions": res.transitions,
+        "violation": VIOLATIONS.get(res.violation, str(res.violation)),
+        "channel": res.channel,
+        "msg": res.msg.decode(),
+    }

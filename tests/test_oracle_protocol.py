@@ -1,0 +1,278 @@
+"""Pins of the oracle's protocol simulation.
+
+What fixes the expected values (none of them comes from the GPU library):
+  * the result of every mode is a plain copy, B[0:n] == A[0:n], with the
+    bytes around B untouched;
+  * closed forms for the counters: head == tail == the number of steps,
+    ceil(len_c / S) summed per channel over the transfers so far;
+    the 4 MiB / 128 KiB single-channel SIMPLE workload takes 32 steps;
+  * the FIFO bytes by replay: each slot position holds the last step that
+    wrote it, and an LL line's flag is that step's 1-based number;
+  * every interleaving of producer and consumer actions on tiny inputs keeps
+    the protocol's invariants and ends in one state, and each deliberate
+    protocol mistake is caught.
+Sources: "【NCCL】transport数据传输（二）" (p2pTransport zero-copy and copy
+sequences; shmTransport normal mode), "Intra-Node Transport (P2P)" section 4
+(POST / POLL), "RDMA and GPUDirect" section 四.1 (flag carried in the data).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+
+def _chunks(n, nch, S):
+    """Brute-force list of (channel, step-in-run, offset, length): the channel
+    ranges tile [0, n) in order with 16-byte-aligned starts and equal sizes
+    except the tail, and every channel cuts its range into S-byte steps."""
+    beg, ln = oracle.partition(n, nch)
+    out = []
+    for c in range(nch):
+        j, off = 0, beg[c]
+        while off < beg[c] + ln[c]:
+            L = min(S, beg[c] + ln[c] - off)
+            out.append((c, j, off, L))
+            off += L
+            j += 1
+    return out
+
+
+def _steps_per_channel(n, nch, S):
+    cnt = [0] * nch
+    for c, _, _, _ in _chunks(n, nch, S):
+        cnt[c] += 1
+    return cnt
+
+
+@pytest.mark.parametrize("n", [0, 1, 15, 16, 17, 100, 4096, 65535, 1 << 20, (1 << 20) + 3])
+@pytest.mark.parametrize("nch", [1, 2, 3, 7, 32, 64])
+def test_partition_properties(n, nch):
+    beg, ln = oracle.partition(n, nch)
+    assert sum(ln) == n
+    pos = 0
+    sizes = []
+    for c in range(nch):
+        assert beg[c] == pos  # contiguous, in channel order
+        assert beg[c] % 16 == 0 or ln[c] == 0
+        pos += ln[c]
+        sizes.append(ln[c])
+    nonempty = [s for s in sizes if s]
+    if len(nonempty) >= 2:
+        per = nonempty[0]
+        # every non-empty channel but the last carries the same multiple of 16 ...
+        assert per % 16 == 0 and all(s == per for s in nonempty[:-1])
+        assert 0 < nonempty[-1] <= per
+        # ... which is the smallest such size that fits n into nch channels
+        assert per * nch >= n and (per - 16) * nch < n
+    elif nonempty:
+        # one channel holds everything only when no 16-multiple below n fits n into nch
+        assert sizes[0] == n
+        assert all(p * nch < n for p in range(16, n, 16))
+    # empty channels only at the end
+    k = len(nonempty)
+    assert all(s == 0 for s in sizes[k:]) and all(s > 0 for s in sizes[:k])
+
+
+def test_workload_one_closed_form():
+    """SIMPLE, 1 channel, 8 x 128 KiB FIFO, 4 MiB: B == A and head == tail == 32."""
+    A = synth.uint8_uniform(4 << 20, synth.workload_seed(1))
+    B = np.zeros_like(A)
+    c = oracle.Conn("simple", 1, 8, 128 << 10)
+    c.run(A, B)
+    assert np.array_equal(A, B)
+    st = c.state(0)
+    assert st == {"head": 32, "tail": 32, "ptr_exchange": 0, "steps": 32}
+
+
+def _replay_fifo(proto, nslots, slot_bytes, transfers, nch):
+    """Writes every chunk of every transfer into its slot, in step order,
+    without any protocol: the FIFO a correct protocol must leave behind."""
+    S = oracle.step_bytes(proto, slot_bytes)
+    fifo = [bytearray(nslots * slot_bytes) for _ in range(nch)]
+    base = [0] * nch
+    for A in transfers:
+        A = bytes(A)
+        for c, j, off, L in _chunks(len(A), nch, S):
+            g = base[c] + j
+            s0 = (g % nslots) * slot_bytes
+            if proto == oracle.SIMPLE:
+                fifo[c][s0:s0 + L] = A[off:off + L]
+            else:
+                for i in range(0, L, 4):
+                    word = A[off + i:off + min(i + 4, L)].ljust(4, b"\0")
+                    fifo[c][s0 + 2 * i:s0 + 2 * i + 4] = word
+                    fifo[c][s0 + 2 * i + 4:s0 + 2 * i + 8] = (g + 1).to_bytes(4, "little")
+        for c, k in enumerate(_steps_per_channel(len(A), nch, S)):
+            base[c] += k
+    return fifo, base
+
+
+CASES = [
+    # proto, nch, nslots, slot_bytes, sizes of consecutive transfers
+    ("simple", 1, 8, 128, [4096]),
+    ("simple", 1, 3, 48, [1, 47, 48, 49, 500]),
+    ("simple", 3, 2, 32, [1000, 17, 0, 333]),
+    ("simple", 4, 8, 64, [4096 + 5, 64]),
+    ("ll", 1, 8, 64, [8, 9, 31, 32, 33, 1000]),
+    ("ll", 2, 3, 24, [77, 5, 256]),
+    ("ll", 5, 1, 8, [100, 3]),
+    ("zc", 1, 8, 64, [1000, 1]),
+    ("zc", 3, 1, 16, [555, 16, 0]),
+]
+
+
+@pytest.mark.parametrize("proto,nch,nslots,slot_bytes,sizes", CASES)
+def test_counters_result_and_fifo_by_replay(proto, nch, nslots, slot_bytes, sizes):
+    conn = oracle.Conn(proto, nch, nslots, slot_bytes)
+    transfers = []
+    for t, n in enumerate(sizes):
+        A = synth.uint8_uniform(n, 100 + t)
+        guard = 64
+        Bfull = synth.guard_pattern(n + 2 * guard, seed=t)
+        before = Bfull.copy()
+        conn.run(A, Bfull[guard:guard + n] if n else Bfull[guard:guard], n)
+        assert np.array_equal(Bfull[guard:guard + n], A)
+        assert np.array_equal(Bfull[:guard], before[:guard])
+        assert np.array_equal(Bfull[guard + n:], before[guard + n:])
+        transfers.append(A)
+    pid = oracle.PROTO_NAMES[proto]
+    fifo, base = _replay_fifo(pid, nslots, slot_bytes, transfers, nch)
+    for c in range(nch):
+        st = conn.state(c)
+        assert st["head"] == st["tail"] == st["steps"] == base[c]
+        assert st["ptr_exchange"] == 0
+        if pid == oracle.ZC:
+            assert conn.fifo(c).size == 0
+        else:
+            assert bytes(conn.fifo(c)) == bytes(fifo[c])
+
+
+def test_simple_fifo_is_the_payload_when_it_fits():
+    """A single transfer no longer than the FIFO leaves the payload laid out
+    verbatim in a fresh FIFO (slots in step order), the rest still zero."""
+    A = synth.uint8_uniform(8 * 64 - 5, 3)
+    c = oracle.Conn("simple", 1, 8, 64)
+    c.run(A, np.zeros_like(A))
+    f = c.fifo(0)
+    assert np.array_equal(f[:A.size], A) and not f[A.size:].any()
+
+
+def test_ll_lines_interleave_payload_and_step_flags():
+    """LL on a fresh FIFO: word w of the payload sits in line w, with the
+    1-based number of its step as the flag; a trailing partial word is
+    zero-padded.  The 16-byte slot below carries 8 payload bytes per step."""
+    A = np.arange(1, 24, dtype=np.uint8)  # 23 bytes -> 3 steps of 8, 8, 7
+    c = oracle.Conn("ll", 1, 4, 16)
+    c.run(A, np.zeros_like(A))
+    f = c.fifo(0).view(np.uint32).reshape(-1, 2)  # (data, flag) per line
+    want_flags = [1, 1, 2, 2, 3, 3, 0, 0]
+    assert list(f[:, 1]) == want_flags
+    words = np.frombuffer(np.concatenate([A, [0]]).astype(np.uint8).tobytes(), dtype=np.uint32)
+    assert list(f[:6, 0]) == list(words)
+    assert c.state(0)["head"] == c.state(0)["tail"] == 3
+
+
+@pytest.mark.parametrize("proto,slot_sizes", [("simple", [16, 32, 48]), ("ll", [8, 24]),
+                                              ("zc", [16, 48])])
+def test_edge_sizes_brute_force(proto, slot_sizes):
+    pid = oracle.PROTO_NAMES[proto]
+    for slot_bytes in slot_sizes:
+        S = oracle.step_bytes(pid, slot_bytes)
+        for nslots in (1, 2, 3):
+            for nch in (1, 2, 3):
+                conn = oracle.Conn(proto, nch, nslots, slot_bytes)
+                total = [0] * nch
+                for n in range(0, 4 * nslots * S + 18, 1 if S <= 16 else 3):
+                    A = synth.uint8_uniform(n, n)
+                    B = np.zeros(n, dtype=np.uint8)
+                    conn.run(A, B)
+                    assert np.array_equal(A, B)
+                    for c, k in enumerate(_steps_per_channel(n, nch, S)):
+                        total[c] += k
+                for c in range(nch):
+                    st = conn.state(c)
+                    assert st["head"] == st["tail"] == st["steps"] == total[c]
+
+
+def test_pingpong_composes_two_connections():
+    a = synth.int32_uniform_bytes(1000, 9)
+    b = np.zeros_like(a)
+    cc = np.zeros_like(a)
+    fwd = oracle.Conn("ll", 1, 8, 32 << 10)
+    rev = oracle.Conn("ll", 1, 8, 32 << 10)
+    oracle.run_pingpong(fwd, rev, a, b, cc, a.size, 25)
+    assert np.array_equal(a, b) and np.array_equal(a, cc)
+    for conn in (fwd, rev):
+        st = conn.state(0)
+        assert st["head"] == st["tail"] == 25
+
+
+# ------------------------------------------------------------ interleavings
+ENUM_CASES = []
+for _p, _slots in (("simple", (16, 32)), ("ll", (8, 16)), ("zc", (16,))):
+    for _ns in (1, 2, 3):
+        for _sb in _slots:
+            for _nch in (1, 2):
+                ENUM_CASES.append((_p, _nch, _ns, _sb))
+
+
+@pytest.mark.parametrize("proto,nch,nslots,slot_bytes", ENUM_CASES)
+def test_every_interleaving_is_safe_and_confluent(proto, nch, nslots, slot_bytes):
+    pid = oracle.PROTO_NAMES[proto]
+    S = oracle.step_bytes(pid, slot_bytes)
+    # up to 6 steps per channel (fewer with two channels or per-line LL actions)
+    max_steps = 6 if nch == 1 else 3
+    if pid == oracle.LL:
+        max_steps = min(max_steps, 4 if nch == 1 else 2)
+    for n in sorted({1, S - 1, S, S + 1, max_steps * S * nch - 3, max_steps * S * nch}):
+        if n <= 0:
+            continue
+        A = synth.uint8_uniform(n, 1000 + n)
+        for prior in (0, 1):
+            r = oracle.enumerate_interleavings(proto, nch, nslots, slot_bytes, A, prior_runs=prior)
+            assert r["violation"] == "ok", (n, prior, r)
+            assert r["terminals"] == 1, r
+            assert r["states"] > 1
+
+
+MUTATION_CASES = [
+    ("simple", "weak_credit", {"window", "overwrite"}),
+    ("simple", "early_tail", {"read_unfilled"}),
+    ("simple", "no_acquire", {"read_unfilled", "read_early"}),
+    ("simple", "early_head", {"overwrite"}),
+    ("ll", "weak_credit", {"window", "overwrite"}),
+    ("ll", "torn_line", {"read_unfilled"}),
+    ("ll", "early_head", {"overwrite", "deadlock"}),
+    ("zc", "zc_no_wait", {"wrong_ptr"}),
+    ("zc", "zc_no_reset", {"wrong_ptr", "counters"}),
+]
+
+
+@pytest.mark.parametrize("proto,mutation,expected", MUTATION_CASES)
+@pytest.mark.parametrize("nslots", [1, 2])
+def test_enumerator_catches_each_broken_rule(proto, mutation, expected, nslots):
+    pid = oracle.PROTO_NAMES[proto]
+    slot_bytes = 16 if pid != oracle.LL else 8
+    S = oracle.step_bytes(pid, slot_bytes)
+    A = synth.uint8_uniform(4 * S + 3, 77)
+    r = oracle.enumerate_interleavings(proto, 1, nslots, slot_bytes, A, mutation=mutation)
+    assert r["violation"] in expected, r
+
+
+def test_correct_protocol_is_clean_under_the_same_inputs_as_the_mutations():
+    for proto in ("simple", "ll", "zc"):
+        pid = oracle.PROTO_NAMES[proto]
+        slot_bytes = 16 if pid != oracle.LL else 8
+        S = oracle.step_bytes(pid, slot_bytes)
+        A = synth.uint8_uniform(4 * S + 3, 77)
+        for nslots in (1, 2):
+            r = oracle.enumerate_interleavings(proto, 1, nslots, slot_bytes, A)
+            assert r["violation"] == "ok" and r["terminals"] == 1
+
+
+def test_conn_rejects_bad_shapes():
+    for args in [("simple", 0, 8, 16), ("simple", 65, 8, 16), ("simple", 1, 0, 16),
+                 ("simple", 1, 8, 24), ("ll", 1, 8, 12), ("zc", 1, 8, 8)]:
+        with pytest.raises(oracle.OracleError):
+            oracle.Conn(*args)
