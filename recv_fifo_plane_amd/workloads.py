@@ -1,0 +1,96 @@
+"""Launch configurations of the five workloads, shared by the benchmark and
+the GPU parity tests (so the tests check exactly what the benchmark times).
+
+W1  SIMPLE, 1 channel, 8 x 128 KiB HBM FIFO, one producer/consumer pair, 4 MiB.
+W2  LL, 1 channel, 8 x 32 KiB, messages 8 B .. 64 KiB, in-kernel ping-pong.
+W3  SIMPLE, 32 channels x 8 x 512 KiB HBM, 1 GiB, 4 workgroups per channel side.
+W4  zero-copy through ptrExchange: one pair on 128 MiB, and a ring of 8
+    logical endpoints built by the host schedule, endpoint r sending its
+    128 MiB slice to (r + 1) mod 8, all edges in one launch.
+W5  host FIFO: 16 channels x 8 x 256 KiB in pinned host memory, 2 GiB of
+    messages with log-uniform sizes 1 KiB .. 64 MiB at consecutive offsets.
+"""
+from __future__ import annotations
+
+from . import xfer as X
+
+W1 = dict(name="simple_1ch_4MiB", proto="simple", nchannels=1, nslots=8, slot_bytes=128 << 10,
+          fifo_loc="device", wgs_per_channel=1, block_threads=256, nbytes=4 << 20)
+
+W2 = dict(name="ll_pingpong", proto="ll", nchannels=1, nslots=8, slot_bytes=32 << 10,
+          fifo_loc="device", wgs_per_channel=1, block_threads=256, iters=10000)
+W2_SIZES = [8 << i for i in range(14)]  # 8 B .. 64 KiB
+
+W3 = dict(name="simple_32ch_1GiB", proto="simple", nchannels=32, nslots=8, slot_bytes=512 << 10,
+          fifo_loc="device", wgs_per_channel=4, block_threads=256, nbytes=1 << 30)
+
+W4_PAIR = dict(name="zc_pair_128MiB", proto="zc", nchannels=4, nslots=1, slot_bytes=512 << 10,
+               fifo_loc="device", wgs_per_channel=4, block_threads=256, nbytes=128 << 20)
+
+W4_RING = dict(name="zc_ring_8x128MiB", proto="zc", endpoints=8, channels_per_edge=4,
+               nslots=1, slot_bytes=512 << 10, fifo_loc="device", wgs_per_channel=4,
+               block_threads=256, slice_bytes=128 << 20, max_peers=128)
+
+W5 = dict(name="host_fifo_16ch_2GiB", proto="simple", nchannels=16, nslots=8,
+          slot_bytes=256 << 10, fifo_loc="host", wgs_per_channel=2, block_threads=256,
+          total_bytes=2 << 30)
+
+_ATTRS = ("wgs_per_channel", "block_threads", "ctrl_loc", "timeout_ms", "xcd_pairing")
+
+
+def make_conn(cfg: dict, **override) -> X.Conn:
+    c = dict(cfg, **override)
+    attrs = {k: c[k] for k in _ATTRS if k in c}
+    return X.Conn(c["proto"], c.get("nchannels", 1), c["nslots"], c["slot_bytes"], c["fifo_loc"],
+                  **attrs)
+
+
+def _addr(t) -> int:
+    return t if isinstance(t, int) else int(t.data_ptr())
+
+
+class Ring:
+    """Logical endpoints on one GPU connected by the host schedule's ring
+    plan; one edge per (r, (r + 1) mod n), each with its own channels."""
+
+    def __init__(self, cfg: dict):
+        import numpy as np
+        n = cfg["endpoints"]
+        rm = np.zeros((n, n), dtype=np.uint64)
+        sm = np.zeros((n, n), dtype=np.uint64)
+        for r in range(n):
+            rm[r], sm[r] = X.sched_ring_masks(r, n, cfg["channels_per_edge"])
+        attrs = {k: cfg[k] for k in _ATTRS if k in cfg}
+        self.n = n
+        self.slice = cfg["slice_bytes"]
+        self.edges = X.endpoints_connect(n, rm, sm, cfg.get("max_peers", 128), cfg["proto"],
+                                         cfg["nslots"], cfg["slot_bytes"], cfg["fifo_loc"], **attrs)
+
+    def run(self, a, b, stream=None) -> None:
+        """Endpoint r's slice of a goes to endpoint (r+1) mod n's slice of b."""
+        keys = sorted(self.edges)
+        conns = [self.edges[k] for k in keys]
+        src = [_addr(a) + s * self.slice for s, _ in keys]
+        dst = [_addr(b) + d * self.slice for _, d in keys]
+        X.run_batch(conns, src, dst, [self.slice] * len(keys), stream)
+
+    def close(self) -> None:
+        for c in self.edges.values():
+            c.close()
+
+
+def make_ring(cfg: dict) -> Ring:
+    return Ring(cfg)
+
+
+def run_pingpong(fwd: X.Conn, rev: X.Conn, a, b, c, nbytes: int, iters: int, stream=None) -> None:
+    X.run_pingpong(fwd, rev, a, b, c, nbytes, iters, stream)
+
+
+def run_messages(conn: X.Conn, a, b, sizes, stream=None) -> None:
+    """One transfer per message, at consecutive offsets of a and b."""
+    off = 0
+    pa, pb = _addr(a), _addr(b)
+    for s in sizes:
+        conn.run(pa + off, pb + off, s, stream)
+        off += s

@@ -1,0 +1,307 @@
+"""ctypes binding of libxfer.so: the C ABI declared in include/xfer.h.
+
+Argument marshalling only: every step of a transfer runs in the library's
+HIP kernels.  PyTorch is used for device memory (tensors' data_ptr()) and
+streams (cuda_stream handles).  The library must be built (``build.py``);
+loading fails loudly when it is missing and cannot be built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+from . import build as _build
+
+XFER_OK = 0
+XFER_ERR_INVALID_ARG = 1
+XFER_ERR_NO_MEMORY = 2
+XFER_ERR_HIP = 3
+XFER_ERR_INTERNAL = 4
+XFER_ERR_TIMEOUT = 5
+XFER_ERR_ABORTED = 6
+XFER_ERR_RANGE = 7
+XFER_ERR_STATE = 8
+
+XFER_PROTO_SIMPLE = 0
+XFER_PROTO_LL = 1
+XFER_PROTO_ZEROCOPY = 2
+XFER_FIFO_DEVICE = 0
+XFER_FIFO_HOST = 1
+XFER_CTRL_DEFAULT = 0
+XFER_CTRL_DEVICE = 1
+XFER_CTRL_HOST = 2
+XFER_OP_RECV_SETUP = 0
+XFER_OP_SEND_SETUP = 1
+XFER_OP_CONNECT_BATCH = 2
+XFER_MAX_BATCH = 16
+
+PROTOS = {"simple": XFER_PROTO_SIMPLE, "ll": XFER_PROTO_LL, "zc": XFER_PROTO_ZEROCOPY,
+          "zerocopy": XFER_PROTO_ZEROCOPY}
+FIFO_LOCS = {"device": XFER_FIFO_DEVICE, "host": XFER_FIFO_HOST}
+
+
+class xfer_attr(C.Structure):
+    _fields_ = [
+        ("wgs_per_channel", C.c_int),
+        ("block_threads", C.c_int),
+        ("ctrl_loc", C.c_int),
+        ("timeout_ms", C.c_uint32),
+        ("xcd_pairing", C.c_int),
+        ("roles", C.c_int),
+        ("reserved", C.c_int * 2),
+    ]
+
+
+class xfer_chan_state(C.Structure):
+    _fields_ = [
+        ("head", C.c_uint64),
+        ("tail", C.c_uint64),
+        ("ptr_exchange", C.c_uint64),
+        ("steps", C.c_uint64),
+        ("lanes", C.c_int),
+        ("lanes_agree", C.c_int),
+        ("error", C.c_int),
+        ("reserved", C.c_int),
+    ]
+
+
+class xfer_setup_op(C.Structure):
+    _fields_ = [("kind", C.c_int), ("peer", C.c_int), ("channel", C.c_int)]
+
+
+# Every symbol include/xfer.h declares, with its ctypes signature.
+_vp = C.c_void_p
+_u64p = C.POINTER(C.c_uint64)
+_ip = C.POINTER(C.c_int)
+SIGNATURES = {
+    "xfer_conn_create": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_size_t, C.c_int, C.POINTER(_vp)]),
+    "xfer_conn_create_ex": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_size_t, C.c_int,
+                                      C.POINTER(xfer_attr), C.POINTER(_vp)]),
+    "xfer_conn_destroy": (C.c_int, [_vp]),
+    "xfer_run": (C.c_int, [_vp, _vp, _vp, C.c_size_t, _vp]),
+    "xfer_run_batch": (C.c_int, [C.POINTER(_vp), C.POINTER(_vp), C.POINTER(_vp),
+                                 C.POINTER(C.c_size_t), C.c_int, _vp]),
+    "xfer_run_loop": (C.c_int, [_vp, _vp, _vp, C.c_size_t, C.c_int, _vp]),
+    "xfer_run_pingpong": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_size_t, C.c_int, _vp]),
+    "xfer_conn_query": (C.c_int, [_vp, C.c_int, C.POINTER(xfer_chan_state)]),
+    "xfer_conn_fifo": (C.c_int, [_vp, C.c_int, C.POINTER(_vp), C.POINTER(C.c_size_t)]),
+    "xfer_conn_read_fifo": (C.c_int, [_vp, C.c_int, _vp, C.c_size_t]),
+    "xfer_conn_abort": (C.c_int, [_vp]),
+    "xfer_conn_launch_shape": (C.c_int, [_vp, _ip, _ip]),
+    "xfer_last_error": (C.c_char_p, []),
+    "xfer_status_string": (C.c_char_p, [C.c_int]),
+    "xfer_sched_peers": (C.c_int, [C.c_int, C.c_int, C.c_int, _ip, _ip]),
+    "xfer_sched_ring_masks": (C.c_int, [C.c_int, C.c_int, C.c_int, _u64p, _u64p]),
+    "xfer_sched_plan": (C.c_int, [C.c_int, C.c_int, _u64p, _u64p, C.c_int,
+                                  C.POINTER(xfer_setup_op), C.c_int, _ip]),
+    "xfer_endpoints_connect": (C.c_int, [C.c_int, _u64p, _u64p, C.c_int, C.c_int, C.c_int,
+                                         C.c_size_t, C.c_int, C.POINTER(xfer_attr),
+                                         C.POINTER(_vp), _ip]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Loads libxfer.so (building it first only if it does not exist)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_build.LIB):
+                _build.build()
+            L = C.CDLL(_build.LIB)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = L
+    return _lib
+
+
+class XferError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (status_string(status), msg))
+        self.status = status
+
+
+def status_string(s: int) -> str:
+    return lib().xfer_status_string(int(s)).decode()
+
+
+def last_error() -> str:
+    return lib().xfer_last_error().decode()
+
+
+def check(rc: int) -> None:
+    if rc != XFER_OK:
+        raise XferError(rc, last_error())
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        try:
+            import torch
+            return torch.cuda.current_stream().cuda_stream or None
+        except Exception:
+            return None
+    if isinstance(stream, int):
+        return stream or None
+    return getattr(stream, "cuda_stream", stream) or None
+
+
+def _addr(buf) -> int:
+    """Device address of a torch tensor, or an integer address."""
+    if buf is None:
+        return 0
+    if isinstance(buf, int):
+        return buf
+    return int(buf.data_ptr())
+
+
+class Conn:
+    """One connection (xfer_conn).  Destroy it only after its streams are idle."""
+
+    def __init__(self, proto="simple", nchannels=1, nslots=8, slot_bytes=128 << 10,
+                 fifo_loc="device", wgs_per_channel=0, block_threads=0, ctrl_loc=0,
+                 timeout_ms=0, xcd_pairing=0, roles=0, _handle=None):
+        self.proto = PROTOS[proto] if isinstance(proto, str) else int(proto)
+        self.nchannels = int(nchannels)
+        self.nslots = int(nslots)
+        self.slot_bytes = int(slot_bytes)
+        self.fifo_loc = FIFO_LOCS[fifo_loc] if isinstance(fifo_loc, str) else int(fifo_loc)
+        self._h = None
+        if _handle is not None:
+            self._h = _handle
+            return
+        attr = xfer_attr(int(wgs_per_channel), int(block_threads), int(ctrl_loc), int(timeout_ms),
+                         int(xcd_pairing), int(roles))
+        h = _vp()
+        check(lib().xfer_conn_create_ex(self.proto, self.nchannels, self.nslots, self.slot_bytes,
+                                        self.fifo_loc, C.byref(attr), C.byref(h)))
+        self._h = h.value
+
+    @property
+    def handle(self) -> int:
+        return self._h
+
+    def close(self) -> None:
+        if self._h:
+            lib().xfer_conn_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def run(self, src, dst, nbytes: int, stream=None) -> None:
+        check(lib().xfer_run(self._h, _addr(src), _addr(dst), int(nbytes), _stream_handle(stream)))
+
+    def run_loop(self, src, dst, nbytes: int, iters: int, stream=None) -> None:
+        check(lib().xfer_run_loop(self._h, _addr(src), _addr(dst), int(nbytes), int(iters),
+                                  _stream_handle(stream)))
+
+    def query(self, channel: int) -> dict:
+        st = xfer_chan_state()
+        check(lib().xfer_conn_query(self._h, int(channel), C.byref(st)))
+        return {"head": st.head, "tail": st.tail, "ptr_exchange": st.ptr_exchange,
+                "steps": st.steps, "lanes": st.lanes, "lanes_agree": bool(st.lanes_agree),
+                "error": st.error}
+
+    def fifo_bytes(self, channel: int) -> int:
+        p, n = _vp(), C.c_size_t()
+        check(lib().xfer_conn_fifo(self._h, int(channel), C.byref(p), C.byref(n)))
+        return n.value
+
+    def read_fifo(self, channel: int):
+        import numpy as np
+        n = self.fifo_bytes(channel)
+        out = np.zeros(n, dtype=np.uint8)
+        if n:
+            check(lib().xfer_conn_read_fifo(self._h, int(channel), out.ctypes.data, n))
+        return out
+
+    def abort(self) -> None:
+        check(lib().xfer_conn_abort(self._h))
+
+    def launch_shape(self) -> tuple[int, int]:
+        g, b = C.c_int(), C.c_int()
+        check(lib().xfer_conn_launch_shape(self._h, C.byref(g), C.byref(b)))
+        return g.value, b.value
+
+
+def run_batch(conns, srcs, dsts, nbytes, stream=None) -> None:
+    n = len(conns)
+    hs = (_vp * n)(*[c.handle for c in conns])
+    ss = (_vp * n)(*[_addr(s) for s in srcs])
+    ds = (_vp * n)(*[_addr(d) for d in dsts])
+    ns = (C.c_size_t * n)(*[int(x) for x in nbytes])
+    check(lib().xfer_run_batch(hs, ss, ds, ns, n, _stream_handle(stream)))
+
+
+def run_pingpong(fwd: Conn, rev: Conn, a, b, c, nbytes: int, iters: int, stream=None) -> None:
+    check(lib().xfer_run_pingpong(fwd.handle, rev.handle, _addr(a), _addr(b), _addr(c),
+                                  int(nbytes), int(iters), _stream_handle(stream)))
+
+
+# ---------------------------------------------------------------- schedule
+def sched_peers(rank: int, nranks: int, i: int) -> tuple[int, int]:
+    r, s = C.c_int(), C.c_int()
+    check(lib().xfer_sched_peers(rank, nranks, i, C.byref(r), C.byref(s)))
+    return r.value, s.value
+
+
+def sched_ring_masks(rank: int, nranks: int, nchannels: int):
+    import numpy as np
+    rm = np.zeros(nranks, dtype=np.uint64)
+    sm = np.zeros(nranks, dtype=np.uint64)
+    check(lib().xfer_sched_ring_masks(rank, nranks, nchannels, rm.ctypes.data_as(_u64p),
+                                      sm.ctypes.data_as(_u64p)))
+    return rm, sm
+
+
+def sched_plan(rank: int, nranks: int, recv_mask, send_mask, max_peers: int = 128):
+    import numpy as np
+    rm = np.ascontiguousarray(recv_mask, dtype=np.uint64)
+    sm = np.ascontiguousarray(send_mask, dtype=np.uint64)
+    n = C.c_int()
+    rc = lib().xfer_sched_plan(rank, nranks, rm.ctypes.data_as(_u64p), sm.ctypes.data_as(_u64p),
+                               max_peers, None, 0, C.byref(n))
+    if rc not in (XFER_OK, XFER_ERR_INVALID_ARG) or n.value < 0:
+        check(rc)
+    if rc == XFER_ERR_INVALID_ARG and n.value == 0:
+        check(rc)
+    ops = (xfer_setup_op * max(n.value, 1))()
+    check(lib().xfer_sched_plan(rank, nranks, rm.ctypes.data_as(_u64p), sm.ctypes.data_as(_u64p),
+                                max_peers, ops, n.value, C.byref(n)))
+    return [(ops[k].kind, ops[k].peer, ops[k].channel) for k in range(n.value)]
+
+
+def endpoints_connect(nranks: int, recv_masks, send_masks, max_peers: int = 128, proto="zc",
+                      nslots: int = 8, slot_bytes: int = 512 << 10, fifo_loc="device",
+                      **attr) -> dict:
+    """Connections of every directed edge the ranks' plans declare: {(s, d): Conn}."""
+    import numpy as np
+    rm = np.ascontiguousarray(recv_masks, dtype=np.uint64).reshape(nranks, nranks)
+    sm = np.ascontiguousarray(send_masks, dtype=np.uint64).reshape(nranks, nranks)
+    p = PROTOS[proto] if isinstance(proto, str) else int(proto)
+    fl = FIFO_LOCS[fifo_loc] if isinstance(fifo_loc, str) else int(fifo_loc)
+    a = xfer_attr(int(attr.get("wgs_per_channel", 0)), int(attr.get("block_threads", 0)),
+                  int(attr.get("ctrl_loc", 0)), int(attr.get("timeout_ms", 0)),
+                  int(attr.get("xcd_pairing", 0)), int(attr.get("roles", 0)))
+    edges = (_vp * (nranks * nranks))()
+    ne = C.c_int()
+    check(lib().xfer_endpoints_connect(nranks, rm.ctypes.data_as(_u64p), sm.ctypes.data_as(_u64p),
+                                       max_peers, p, nslots, slot_bytes, fl, C.byref(a), edges,
+                                       C.byref(ne)))
+    out = {}
+    for s in range(nranks):
+        for d in range(nranks):
+            h = edges[s * nranks + d]
+            if h:
+                nch = bin(int(sm[s, d])).count("1")
+                out[(s, d)] = Conn(p, nch, nslots, slot_bytes, fl, _handle=h)
+    return out

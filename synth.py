@@ -3,9 +3,10 @@
 Both the CPU oracle's tests and the GPU path's tests and benchmark draw their
 inputs from here, so the two sides always see the same bytes.  This module
 holds none of the protocol's arithmetic: it only produces payloads and
-message-size lists.  Every generator is a numpy PCG64 stream
-(``numpy.random.default_rng(seed)``); the workload seeds are 1000 + the
-workload number.
+message-size lists.  Every payload is drawn from numpy PCG64 streams in blocks of 2**24 values,
+block b from ``numpy.random.default_rng([seed, b])``; message-size lists
+come from ``numpy.random.default_rng(seed)``.  The workload seeds are
+1000 + the workload number.
 """
 from __future__ import annotations
 
@@ -19,9 +20,33 @@ def workload_seed(k: int) -> int:
     return SEED_BASE + int(k)
 
 
+BLOCK = 1 << 24
+
+
+def _blocked(n: int, dtype, seed: int, draw) -> np.ndarray:
+    """n values of dtype; block b (BLOCK values) comes from default_rng([seed, b]),
+    so large inputs are generated on several threads with a fixed result."""
+    out = np.empty(int(n), dtype=dtype)
+    nblocks = (int(n) + BLOCK - 1) // BLOCK
+
+    def fill(b: int) -> None:
+        s = b * BLOCK
+        e = min(int(n), s + BLOCK)
+        out[s:e] = draw(np.random.default_rng([seed, b]), e - s)
+
+    if nblocks > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(8, nblocks)) as ex:
+            list(ex.map(fill, range(nblocks)))
+    elif nblocks:
+        fill(0)
+    return out
+
+
 def uint8_uniform(nbytes: int, seed: int) -> np.ndarray:
     """``nbytes`` uniform random bytes."""
-    return np.random.default_rng(seed).integers(0, 256, size=int(nbytes), dtype=np.uint8)
+    return _blocked(nbytes, np.uint8, seed,
+                    lambda g, m: g.integers(0, 256, size=m, dtype=np.uint8))
 
 
 def int32_uniform_bytes(nbytes: int, seed: int) -> np.ndarray:
@@ -31,8 +56,19 @@ def int32_uniform_bytes(nbytes: int, seed: int) -> np.ndarray:
     ceil(nbytes/4) and the byte view is cut to ``nbytes``.
     """
     nwords = (int(nbytes) + 3) // 4
-    w = np.random.default_rng(seed).integers(-(2**31), 2**31, size=nwords, dtype=np.int64)
-    return w.astype(np.int32).view(np.uint8)[: int(nbytes)].copy()
+    w = _blocked(nwords, np.int32, seed,
+                 lambda g, m: g.integers(-(2**31), 2**31, size=m, dtype=np.int64).astype(np.int32))
+    return w.view(np.uint8)[: int(nbytes)].copy()
+
+
+def _bf16_rne(g, m: int) -> np.ndarray:
+    u = g.standard_normal(m, dtype=np.float32).view(np.uint32)
+    # finite fp32 bit patterns stay below 2**32 after adding at most 0x8000
+    lsb = (u >> 16) & 1
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= 16
+    return u
 
 
 def bf16_normal_bytes(nbytes: int, seed: int) -> np.ndarray:
@@ -43,16 +79,7 @@ def bf16_normal_bytes(nbytes: int, seed: int) -> np.ndarray:
     bits matter to a byte copy; the payload type is opaque to the protocol.
     """
     nbytes = int(nbytes)
-    n = (nbytes + 1) // 2
-    rng = np.random.default_rng(seed)
-    out = np.empty(n, dtype=np.uint16)
-    block = 1 << 24
-    for s in range(0, n, block):
-        e = min(n, s + block)
-        f = rng.standard_normal(e - s, dtype=np.float32)
-        u = f.view(np.uint32).astype(np.uint64)
-        u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-        out[s:e] = u.astype(np.uint16)
+    out = _blocked((nbytes + 1) // 2, np.uint16, seed, _bf16_rne)
     return out.view(np.uint8)[:nbytes].copy()
 
 
@@ -61,8 +88,9 @@ def fp32_uniform_bytes(nbytes: int, seed: int, lo: float = -1.0, hi: float = 1.0
     nbytes = int(nbytes)
     if nbytes % 4:
         raise ValueError("fp32 payload must be a whole number of words")
-    f = np.random.default_rng(seed).uniform(lo, hi, size=nbytes // 4).astype(np.float32)
-    return f.view(np.uint8).copy()
+    f = _blocked(nbytes // 4, np.float32, seed,
+                 lambda g, m: g.uniform(lo, hi, size=m).astype(np.float32))
+    return f.view(np.uint8)
 
 
 def log_uniform_message_sizes(total: int, seed: int, lo_exp: float = 10.0,

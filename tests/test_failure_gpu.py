@@ -1,0 +1,93 @@
+"""Failure handling, forced from the host so every kernel still exits
+normally: one side switched off makes the other side's bounded wait end
+with XFER_ERR_TIMEOUT (or XFER_ERR_ABORTED once the host abort word is set);
+the connection then refuses further runs."""
+import time
+
+import pytest
+
+import recv_fifo_plane_amd as xf
+from recv_fifo_plane_amd import xfer as X
+from gpu_cases import log
+
+pytestmark = pytest.mark.gpu
+
+
+def _bufs(n):
+    import torch
+    return torch.zeros(n, dtype=torch.uint8, device="cuda"), torch.zeros(n, dtype=torch.uint8,
+                                                                          device="cuda")
+
+
+@pytest.mark.parametrize("proto", ["simple", "ll", "zc"])
+@pytest.mark.parametrize("roles", [1, 2])
+def test_lone_side_times_out(proto, roles):
+    import torch
+    log("case: lone side %s roles=%d" % (proto, roles))
+    c = xf.Conn(proto, 2, 2, 4096, timeout_ms=20, roles=roles)
+    a, b = _bufs(1 << 16)
+    t0 = time.time()
+    c.run(a, b, 1 << 16)
+    torch.cuda.synchronize()
+    assert time.time() - t0 < 5.0
+    # a lone producer runs out of credit (16 steps per channel, 2 slots) or
+    # waits for an address; a lone consumer waits for data
+    assert c.query(0)["error"] == X.XFER_ERR_TIMEOUT
+    with pytest.raises(xf.XferError) as e:
+        c.run(a, b, 1 << 16)
+    assert e.value.status == X.XFER_ERR_STATE
+    c.close()
+
+
+@pytest.mark.parametrize("proto", ["simple", "ll", "zc"])
+def test_abort_word_ends_waits(proto):
+    import torch
+    log("case: abort %s" % proto)
+    c = xf.Conn(proto, 1, 2, 4096, timeout_ms=4000, roles=2)
+    a, b = _bufs(1 << 14)
+    c.abort()
+    t0 = time.time()
+    c.run(a, b, 1 << 14)
+    torch.cuda.synchronize()
+    assert time.time() - t0 < 3.0  # well before the 4 s timeout
+    assert c.query(0)["error"] == X.XFER_ERR_ABORTED
+    c.close()
+
+
+def test_healthy_connection_unaffected_by_a_failed_one():
+    import torch
+    bad = xf.Conn("simple", 1, 2, 4096, timeout_ms=10, roles=2)
+    good = xf.Conn("simple", 1, 2, 4096)
+    a, b = _bufs(1 << 15)
+    a.random_(0, 255)
+    bad.run(a, b, 1 << 15)
+    torch.cuda.synchronize()
+    good.run(a, b, 1 << 15)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert good.query(0)["error"] == 0 and bad.query(0)["error"] == X.XFER_ERR_TIMEOUT
+    bad.close()
+    good.close()
+
+
+def test_run_validation_on_device_buffers():
+    c = xf.Conn("simple", 1, 2, 4096)
+    a, b = _bufs(4096)
+    with pytest.raises(xf.XferError) as e:
+        c.run(a.data_ptr(), a.data_ptr() + 100, 1000)  # overlap
+    assert e.value.status == X.XFER_ERR_INVALID_ARG
+    with pytest.raises(xf.XferError):
+        c.run(0, b, 10)
+    c.run(0, 0, 0)  # nothing to move: no launch
+    c.close()
+
+
+def test_grid_that_cannot_be_resident_is_refused():
+    c = xf.Conn("simple", 64, 1, 4096, wgs_per_channel=16, block_threads=1024)
+    a, b = _bufs(1 << 20)
+    g, blk = c.launch_shape()
+    assert (g, blk) == (64 * 16 * 2, 1024)
+    with pytest.raises(xf.XferError) as e:
+        c.run(a, b, 1 << 20)
+    assert e.value.status == X.XFER_ERR_INVALID_ARG
+    c.close()

@@ -1,0 +1,56 @@
+"""GPU parity on seeded small cases: every protocol x FIFO location, several
+tiles and a ragged tail, misaligned buffers, 1..4 channels, 1..3 lanes,
+1..8 slots; the destination (with guard bytes), counters and FIFO bytes must
+equal the oracle's with 0 differing bytes."""
+import pytest
+
+from gpu_cases import run_transfers
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [0, 1, 15, 16, 17, 255, 4095, 4096, 4097, 65536 + 13, 300_001]
+
+
+@pytest.mark.parametrize("fifo_loc", ["device", "host"])
+@pytest.mark.parametrize("nch,nslots,lanes", [(1, 1, 1), (1, 2, 2), (3, 3, 1), (4, 8, 3)])
+def test_simple(fifo_loc, nch, nslots, lanes):
+    run_transfers("simple", nch, nslots, 4096, SIZES, fifo_loc=fifo_loc, lanes=lanes)
+
+
+@pytest.mark.parametrize("fifo_loc", ["device", "host"])
+@pytest.mark.parametrize("nch,nslots,lanes", [(1, 1, 1), (1, 3, 2), (2, 8, 1), (4, 2, 3)])
+def test_ll(fifo_loc, nch, nslots, lanes):
+    run_transfers("ll", nch, nslots, 2048, SIZES, fifo_loc=fifo_loc, lanes=lanes, kind="int32")
+
+
+@pytest.mark.parametrize("fifo_loc", ["device", "host"])
+@pytest.mark.parametrize("nch,lanes", [(1, 1), (2, 2), (4, 3)])
+def test_zerocopy(fifo_loc, nch, lanes):
+    run_transfers("zc", nch, 8, 4096, SIZES, fifo_loc=fifo_loc, lanes=lanes)
+
+
+@pytest.mark.parametrize("proto", ["simple", "ll", "zc"])
+@pytest.mark.parametrize("src_off,dst_off", [(1, 0), (0, 3), (5, 11), (8, 8), (15, 1)])
+def test_misaligned(proto, src_off, dst_off):
+    run_transfers(proto, 2, 3, 512, [1, 100, 5000, 33333], src_off=src_off, dst_off=dst_off,
+                  lanes=2)
+
+
+@pytest.mark.parametrize("block", [64, 512, 1024])
+def test_block_sizes(block):
+    for proto in ("simple", "ll", "zc"):
+        run_transfers(proto, 2, 4, 8192, [100_000, 7], block=block, lanes=2)
+
+
+@pytest.mark.parametrize("ctrl_loc", [1, 2])
+def test_control_words_either_side(ctrl_loc):
+    for proto in ("simple", "ll", "zc"):
+        for fifo_loc in ("device", "host"):
+            run_transfers(proto, 2, 2, 1024, [20_000, 3], fifo_loc=fifo_loc, ctrl_loc=ctrl_loc)
+
+
+@pytest.mark.parametrize("xcd_pairing", [-1, 1])
+def test_xcd_pairing_either_way(xcd_pairing):
+    # 8 channels x 1 lane -> 16 workgroups: the pairing remap is active when on
+    for proto in ("simple", "ll", "zc"):
+        run_transfers(proto, 8, 2, 4096, [1 << 20, 4097], xcd_pairing=xcd_pairing)
