@@ -68,7 +68,13 @@ class Timer:
 
     def time_launches(self, fn, warmup: int, steps: int) -> tuple[float, float]:
         """Returns (ms per step over the whole timed region, mean ms per launch
-        from per-launch event pairs)."""
+        from per-launch event pairs).  torch work inside fn is queued on the
+        same stream."""
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            return self._time(fn, warmup, steps)
+
+    def _time(self, fn, warmup: int, steps: int) -> tuple[float, float]:
         torch = self.torch
         for _ in range(warmup):
             fn()
@@ -252,8 +258,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["value", "all"], default="all",
-                    help="value: time only the headline workload (for profiling)")
+    ap.add_argument("--only", choices=["value", "all", "copy"], default="all",
+                    help="value: time only the headline workload; copy: only a plain 1 GiB "
+                         "device copy (the calibration kernel of the HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -270,6 +277,9 @@ def main() -> int:
         return 2
     stream = torch.cuda.Stream()
     T = Timer(torch, stream)
+    if args.only == "copy":
+        print(json.dumps({"plain_copy_1GiB_torch": plain_copy_ceiling(torch, T)}), flush=True)
+        return 0
     log("bench: W3 simple 32ch 1GiB, %d warmup + %d steps" % (args.warmup, args.steps))
     A, w3 = bench_w3(torch, T, W, synth, args.steps, args.warmup)
     payload = W.W3["nbytes"]

@@ -73,17 +73,33 @@ typedef enum {
   XFER_CTRL_HOST = 2     /* head/tail/ptrExchange words in pinned host memory */
 } xfer_ctrl_loc;
 
+/* How a hand-off orders the payload before the counter that publishes it.
+ * COHERENT: payload and control words are accessed with the cache policy of
+ * the connection's scope (performed at the coherence point, not in an XCD's
+ * private L2); each wave waits for its accesses to complete before the
+ * counter store, and the peer reads the payload only after its counter load
+ * returned.  FENCED: plain payload accesses with the scoped release/acquire
+ * fences of the compiler's memory model (an L2 writeback before the counter
+ * store, an L2 invalidate after the counter load), several times slower. */
+typedef enum {
+  XFER_ORDER_COHERENT = 0,
+  XFER_ORDER_FENCED = 1
+} xfer_ordering;
+
 /* Optional creation attributes; zero-filled fields take the defaults. */
 typedef struct {
   int wgs_per_channel;  /* workgroups per channel on each side (lanes), 1..16; default 1 */
   int block_threads;    /* threads per workgroup, a multiple of 64 in 64..1024; default 256 */
   int ctrl_loc;         /* xfer_ctrl_loc */
   uint32_t timeout_ms;  /* bound on every in-kernel wait; default 10000 */
-  int xcd_pairing;      /* 0 default (on), 1 on, -1 off: keep a channel's two sides on one XCD */
+  int xcd_pairing;      /* 1: place each producer/consumer pair on one XCD; 0 (default) or -1:
+                           dispatch order (a channel's sides spread over the XCDs, measured
+                           faster for bandwidth) */
   int roles;            /* fault injection: 0 = both sides (default), 1 = producer only,
                            2 = consumer/receiver only; a lone side ends its waits with
                            XFER_ERR_TIMEOUT (or XFER_ERR_ABORTED after xfer_conn_abort) */
-  int reserved[2];
+  int ordering;         /* xfer_ordering */
+  int reserved;
 } xfer_attr;
 
 /* State of one channel, read back after the stream has been synchronised. */
@@ -112,9 +128,9 @@ typedef struct xfer_conn xfer_conn;
  *   proto       xfer_proto.
  *   nchannels   1..64 (64-bit channel masks).
  *   nslots      >= 1 FIFO slots per channel (ignored by zero-copy).
- *   slot_bytes  bytes per slot: SIMPLE and zero-copy a multiple of 16 (a
- *               zero-copy step moves slot_bytes); LL a multiple of 8, of
- *               which half is payload.
+ *   slot_bytes  bytes per slot, at most 1 GiB: SIMPLE and zero-copy a
+ *               multiple of 16 (a zero-copy step moves slot_bytes); LL a
+ *               multiple of 8, of which half is payload.
  *   fifo_loc    xfer_fifo_loc.
  *   attr        NULL for defaults.
  *   out         receives the connection; owned by the caller until
@@ -151,7 +167,8 @@ int xfer_run(xfer_conn* c, const void* src, void* dst, size_t nbytes, void* stre
 
 /* xfer_run_batch: the transfers of n connections (n <= XFER_MAX_BATCH) in
  * ONE launch, e.g. the edges of a ring of logical endpoints.  All
- * connections must share protocol, FIFO location, block size and timeout.
+ * connections must share protocol, memory scope, ordering, block size and
+ * timeout.
  * Arrays are host arrays of length n. */
 #define XFER_MAX_BATCH 16
 int xfer_run_batch(xfer_conn* const* conns, const void* const* src, void* const* dst,

@@ -3,9 +3,14 @@
 // both endpoints.  Setup = allocate + zero + wire (the transport's
 // Setup/ProxySetup/Connect sequence, "transport建立" section 具体说明);
 // teardown = free.  After setup the host is silent: a run only launches.
+#include <stdlib.h>
 #include <string.h>
+#include <sys/syscall.h>
+#include <unistd.h>
 
 #include <algorithm>
+#include <array>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -15,7 +20,7 @@
 
 struct xfer_conn {
   int proto = 0, nch = 0, nslots = 0, fifo_loc = 0, ctrl_loc = 0;
-  int lanes = 1, block = 256, xcd_pairing = 1, roles = 3;
+  int lanes = 1, block = 256, xcd_pairing = 0, roles = 3, ordering = 0;
   size_t slot_bytes = 0, step_bytes = 0;
   uint32_t timeout_ms = 0;
   uint64_t timeout_ticks = 0;
@@ -65,6 +70,39 @@ struct DeviceGuard {
     int cur = -1;
     if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
   }
+};
+
+// Host allocations made while this is alive prefer the NUMA node closest to
+// the device, so host-FIFO traffic does not cross the socket interconnect; the
+// thread's previous memory policy is restored afterwards.  Disabled by
+// XFER_HOST_NUMA=0, and a no-op where the node is unknown.
+class NearNuma {
+ public:
+  explicit NearNuma(int device) {
+    const char* env = getenv("XFER_HOST_NUMA");
+    if (env && env[0] == '0') return;
+    int node = -1;
+    if (hipDeviceGetAttribute(&node, hipDeviceAttributeHostNumaId, device) != hipSuccess) {
+      (void)hipGetLastError();  // an unsupported query must not linger as the last error
+      return;
+    }
+    if (node < 0 || node >= kBits) return;
+    if (syscall(SYS_get_mempolicy, &old_mode_, old_mask_, kBits, nullptr, 0) != 0) return;
+    unsigned long mask[kWords] = {0};
+    mask[node / 64] = 1ul << (node % 64);
+    if (syscall(SYS_set_mempolicy, kPreferred, mask, kBits) != 0) return;
+    active_ = true;
+  }
+  ~NearNuma() {
+    if (active_) syscall(SYS_set_mempolicy, old_mode_, old_mask_, kBits);
+  }
+  unsigned flag() const { return active_ ? hipHostMallocNumaUser : 0u; }
+
+ private:
+  static constexpr int kBits = 4096, kWords = kBits / 64, kPreferred = 1;
+  bool active_ = false;
+  int old_mode_ = 0;
+  unsigned long old_mask_[kWords] = {0};
 };
 
 void release(xfer_conn* c) {
@@ -166,10 +204,34 @@ uint32_t remap_flag(int pairing, uint32_t total) {
   return pairing && total % 16u == 0 ? 1u : 0u;
 }
 
+// Resident-workgroup capacity per (device, kernel variant, block size),
+// queried once: the runtime query costs far more than a launch.
+int resident_capacity(const Variant& v, int kind, int block, int* cap) {
+  static std::mutex mu;
+  static std::map<std::array<int, 7>, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  const std::array<int, 7> key{dev, v.proto, v.scope, v.ordering, v.aligned, kind, block};
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      *cap = it->second;
+      return XFER_OK;
+    }
+  }
+  e = max_resident(v, kind, block, cap);
+  if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  std::lock_guard<std::mutex> lk(mu);
+  cache[key] = *cap;
+  return XFER_OK;
+}
+
 int check_resident(const Variant& v, int kind, int block, uint32_t total, const char* who) {
   int cap = 0;
-  hipError_t e = max_resident(v, kind, block, &cap);
-  if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  const int rc = resident_capacity(v, kind, block, &cap);
+  if (rc) return rc;
   if (int64_t(total) > int64_t(cap))
     return fail(XFER_ERR_INVALID_ARG,
                 std::string(who) + ": " + std::to_string(total) +
@@ -212,9 +274,9 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: nchannels must be in 1..64");
   if (nslots < 1) return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: nslots must be >= 1");
   const size_t gran = proto == XFER_PROTO_LL ? 8 : 16;
-  if (slot_bytes < gran || slot_bytes % gran || slot_bytes > (size_t(1) << 34))
+  if (slot_bytes < gran || slot_bytes % gran || slot_bytes > (size_t(1) << 30))
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: slot_bytes must be a positive multiple of " +
-                                          std::to_string(gran) + " up to 16 GiB");
+                                          std::to_string(gran) + " up to 1 GiB");
   if (fifo_loc != XFER_FIFO_DEVICE && fifo_loc != XFER_FIFO_HOST)
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: fifo_loc must be DEVICE or HOST");
   xfer_attr a;
@@ -233,6 +295,8 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: xcd_pairing must be -1, 0 or 1");
   if (a.roles < 0 || a.roles > 2)
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: roles must be 0, 1 or 2");
+  if (a.ordering != XFER_ORDER_COHERENT && a.ordering != XFER_ORDER_FENCED)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: ordering must be COHERENT or FENCED");
   const size_t fifo_bytes =
       proto == XFER_PROTO_ZEROCOPY ? 0 : size_t(nchannels) * size_t(nslots) * slot_bytes;
   if (proto != XFER_PROTO_ZEROCOPY && fifo_bytes / size_t(nchannels) / size_t(nslots) != slot_bytes)
@@ -249,8 +313,9 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
                     : a.ctrl_loc;
   c->lanes = lanes;
   c->block = block;
-  c->xcd_pairing = a.xcd_pairing >= 0 ? 1 : 0;
+  c->xcd_pairing = a.xcd_pairing == 1 ? 1 : 0;
   c->roles = a.roles == 0 ? 3 : a.roles;
+  c->ordering = a.ordering;
   c->slot_bytes = slot_bytes;
   c->step_bytes = proto == XFER_PROTO_LL ? slot_bytes / 2 : slot_bytes;
   c->timeout_ms = a.timeout_ms ? a.timeout_ms : kDefaultTimeoutMs;
@@ -274,9 +339,11 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
 
   // FIFO: HBM, or pinned host memory mapped into the device (fine-grained,
   // so device accesses reach host memory rather than a non-coherent cache).
+  NearNuma near(c->device);  // pinned host blocks below land next to the device
   if (fifo_bytes) {
     if (fifo_loc == XFER_FIFO_HOST) {
-      e = hipHostMalloc(&c->fifo_mem, fifo_bytes, hipHostMallocMapped | hipHostMallocCoherent);
+      e = hipHostMalloc(&c->fifo_mem, fifo_bytes,
+                        hipHostMallocMapped | hipHostMallocCoherent | near.flag());
       if (e != hipSuccess) {
         c->fifo_mem = nullptr;
         release(c);
@@ -308,7 +375,8 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
   // Control blocks: one per lane, head = tail = ptrExchange = 0.
   const size_t ctrl_bytes = sizeof(LaneCtrl) * size_t(nchannels) * size_t(lanes);
   if (c->ctrl_loc == XFER_CTRL_HOST) {
-    e = hipHostMalloc(&c->ctrl_mem, ctrl_bytes, hipHostMallocMapped | hipHostMallocCoherent);
+    e = hipHostMalloc(&c->ctrl_mem, ctrl_bytes,
+                      hipHostMallocMapped | hipHostMallocCoherent | near.flag());
     if (e != hipSuccess) {
       c->ctrl_mem = nullptr;
       release(c);
@@ -372,7 +440,7 @@ extern "C" int xfer_conn_destroy(xfer_conn* c) {
 }
 
 static Variant variant_of(const xfer_conn* c, bool aligned) {
-  return Variant{c->proto, c->scope, aligned ? 1 : 0};
+  return Variant{c->proto, c->scope, c->ordering, aligned ? 1 : 0};
 }
 
 extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nbytes, int iters,
@@ -428,11 +496,12 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
     for (int j = 0; j < i; ++j)
       if (conns[j] == c) return fail(XFER_ERR_INVALID_ARG, "xfer_run_batch: a connection appears twice");
     if (!first) first = c;
-    if (c->proto != first->proto || c->scope != first->scope || c->block != first->block ||
-        c->timeout_ticks != first->timeout_ticks || c->device != first->device)
+    if (c->proto != first->proto || c->scope != first->scope || c->ordering != first->ordering ||
+        c->block != first->block || c->timeout_ticks != first->timeout_ticks ||
+        c->device != first->device)
       return fail(XFER_ERR_INVALID_ARG,
-                  "xfer_run_batch: connections must share protocol, memory scope, block size, "
-                  "timeout and device");
+                  "xfer_run_batch: connections must share protocol, memory scope, ordering, "
+                  "block size, timeout and device");
     if (nbytes[i] == 0) continue;
     if (!src[i] || !dst[i])
       return fail(XFER_ERR_INVALID_ARG, "xfer_run_batch: NULL src or dst with nbytes > 0");
@@ -471,10 +540,10 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
   if (fwd == rev) return fail(XFER_ERR_INVALID_ARG, "xfer_run_pingpong: fwd and rev must differ");
   if (fwd->proto == XFER_PROTO_ZEROCOPY || fwd->proto != rev->proto || fwd->nch != rev->nch ||
       fwd->slot_bytes != rev->slot_bytes || fwd->lanes != rev->lanes || fwd->block != rev->block ||
-      fwd->device != rev->device)
+      fwd->ordering != rev->ordering || fwd->device != rev->device)
     return fail(XFER_ERR_INVALID_ARG,
                 "xfer_run_pingpong: fwd and rev must be SIMPLE or LL with equal channels, slot "
-                "size, lanes, block size and device");
+                "size, lanes, block size, ordering and device");
   if (iters < 1) return fail(XFER_ERR_INVALID_ARG, "xfer_run_pingpong: iters must be >= 1");
   if (nbytes == 0) return XFER_OK;
   if (!a || !b || !cbuf)
@@ -491,7 +560,8 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
   const uint32_t total = wgs_of(fwd);
   const int scope = (fwd->scope == kScopeSystem || rev->scope == kScopeSystem) ? kScopeSystem
                                                                                : kScopeAgent;
-  const Variant v{fwd->proto, scope, (aligned16(a) && aligned16(b) && aligned16(cbuf)) ? 1 : 0};
+  const Variant v{fwd->proto, scope, fwd->ordering,
+                  (aligned16(a) && aligned16(b) && aligned16(cbuf)) ? 1 : 0};
   rc = check_resident(v, 2, fwd->block, total, "xfer_run_pingpong");
   if (rc) return rc;
   PingArgs args;

@@ -10,16 +10,27 @@
 // section 4.  The LL line format carries the flag inside the data ("RDMA and
 // GPUDirect", section 四.1, option 2).
 //
-// Memory ordering on gfx950.  The eight XCDs each have their own L2; for
-// device memory an agent-scope release writes back dirty L2 lines and an
-// agent-scope acquire invalidates them.  A workgroup barrier does not wait
-// for the other waves' stores to reach L2, so a release by one thread after
-// the barrier would not cover them: every wave issues its own release fence
-// before the barrier that precedes the counter store, and every wave polls
-// the counter itself and issues its own acquire fence before it reads the
-// data.  Host FIFOs (or host control words) use system scope throughout.
-// Every wait is bounded by the connection's timeout and also watches the
-// host abort word, so every wave reaches the end of the kernel.
+// Memory ordering on gfx950.  The eight XCDs each have their own L2, not
+// kept coherent with each other for device memory by plain accesses.  Two
+// orderings are built; a connection picks one:
+//  * coherent (default): every access to shared protocol data -- FIFO
+//    payload, zero-copy destination, counters, ptrExchange -- carries the
+//    cache policy of the connection's scope (device: sc1; system: sc0 sc1),
+//    the policy the compiler itself uses for relaxed atomics at that scope,
+//    so each access is performed at the coherence point instead of in a
+//    private L2 line.  A wave's s_waitcnt on all its outstanding accesses
+//    completes them at that scope before the workgroup barrier that precedes
+//    the counter store (release side); the peer issues its data accesses
+//    only after its counter load has returned (acquire side).  No L2-wide
+//    writeback or invalidate is needed, which is what makes this path fast.
+//  * fenced: plain data accesses and the compiler's scoped release/acquire
+//    fences, per wave (an L2 writeback before the counter store, an L2
+//    invalidate after the counter load).  A workgroup barrier does not wait
+//    for the other waves' stores, so every wave fences itself.
+// Source payload and destination buffers that no peer reads during the
+// launch are streamed with non-temporal accesses.  Every wait is bounded by
+// the connection's timeout and also watches the host abort word, so every
+// wave reaches the end of the kernel.
 
 #include "xfer_internal.h"
 #include "xfer.h"
@@ -27,8 +38,8 @@
 namespace xfer {
 namespace {
 
-constexpr int kUnroll = 8;     // 16-byte vectors in flight per thread in the copy loop
-constexpr int kLLUnroll = 4;   // LL lines polled together per thread
+constexpr int kUnroll = 16;    // 16-byte vectors in flight per thread in the copy loop
+constexpr int kLLUnroll = 8;   // LL lines polled together per thread
 
 template <int SC>
 __device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) {
@@ -61,6 +72,38 @@ __device__ __forceinline__ void fence_acquire() {
   else
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
+
+enum : int { kOrdCoherent = 0, kOrdFenced = 1 };
+
+// Cache-policy immediates of gfx950 buffer instructions.
+constexpr int kPolSC0 = 1, kPolNT = 2, kPolSC1 = 16;
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Ordering of one connection: the cache policy of shared protocol data and
+// the two halves of a hand-off.
+template <int SC, int ORD>
+struct Order {
+  static constexpr int kShared =
+      ORD == kOrdFenced ? 0 : (SC == kScopeSystem ? (kPolSC0 | kPolSC1) : kPolSC1);
+  // This wave's earlier accesses are complete at the connection's scope.
+  static __device__ __forceinline__ void release() {
+    if constexpr (ORD == kOrdFenced) {
+      fence_release<SC>();
+    } else {
+      compiler_fence();
+      __builtin_amdgcn_s_waitcnt(0);
+      compiler_fence();
+    }
+  }
+  // Accesses after this point are issued after the counter load returned.
+  static __device__ __forceinline__ void acquire() {
+    if constexpr (ORD == kOrdFenced)
+      fence_acquire<SC>();
+    else
+      compiler_fence();
+  }
+};
 
 // Every lane loads the same word (one request per wave); the value is made
 // wave-uniform explicitly.
@@ -130,40 +173,47 @@ __device__ __forceinline__ void lane_share_lines(uint64_t L, uint64_t S, uint32_
   hi = min(nl, static_cast<uint64_t>(w + 1) * sub);
 }
 
-// Workgroup copy of n bytes, both ends 16-byte aligned: 16-byte vector
-// loads, kUnroll in flight per thread, then the stores; ragged tail bytewise.
-// The pointers are deliberately not __restrict__: with it the compiler sinks
-// each load next to its store and only one vector is in flight per thread.
-__device__ __forceinline__ void copy_aligned(const uint8_t* s, uint8_t* d, uint64_t n, uint32_t tid,
-                                             uint32_t nthr) {
-  const uint4* s4 = reinterpret_cast<const uint4*>(s);
-  uint4* d4 = reinterpret_cast<uint4*>(d);
-  const uint64_t nv = n >> 4;
-  const uint64_t stride = static_cast<uint64_t>(nthr) * kUnroll;
-  uint64_t i = tid;
-  for (; i + static_cast<uint64_t>(kUnroll - 1) * nthr < nv; i += stride) {
-    uint4 r[kUnroll];
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over n bytes: the buffer unit checks every access
+// against n (an access past it reads 0 and writes nothing).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), 0, static_cast<int>(n),
+                                           0x00020000);
+}
+
+// Workgroup copy of n (< 2^31) bytes with load policy LP and store policy SP.
+// Aligned (both ends 16-byte aligned): 16-byte vectors, kUnroll loads in
+// flight per thread before their stores, ragged tail bytewise.  Otherwise
+// bytewise.  The descriptors are opaque to alias analysis, so the batch of
+// loads stays ahead of the stores.
+template <int LP, int SP, bool AL>
+__device__ __forceinline__ void copy_pol(const uint8_t* s, uint8_t* d, uint64_t n64) {
+  const uint32_t n = static_cast<uint32_t>(n64);
+  if (n == 0) return;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, n), rd = make_rsrc(d, n);
+  const uint32_t tid = threadIdx.x, nthr = blockDim.x;
+  uint32_t done = 0;
+  if constexpr (AL) {
+    const uint32_t nv = n >> 4;
+    uint32_t i = tid;
+    for (; i + (kUnroll - 1) * nthr < nv; i += kUnroll * nthr) {
+      u32x4 r[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) r[u] = s4[i + static_cast<uint64_t>(u) * nthr];
+      for (int u = 0; u < kUnroll; ++u)
+        r[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (i + u * nthr) << 4, 0, LP);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) d4[i + static_cast<uint64_t>(u) * nthr] = r[u];
+      for (int u = 0; u < kUnroll; ++u)
+        __builtin_amdgcn_raw_buffer_store_b128(r[u], rd, (i + u * nthr) << 4, 0, SP);
+    }
+    for (; i < nv; i += nthr)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(rs, i << 4, 0, LP),
+                                             rd, i << 4, 0, SP);
+    done = nv << 4;
   }
-  for (; i < nv; i += nthr) d4[i] = s4[i];
-  const uint64_t done = nv << 4;
-  if (tid < n - done) d[done + tid] = s[done + tid];
-}
-
-__device__ __forceinline__ void copy_bytes(const uint8_t* __restrict__ s, uint8_t* __restrict__ d,
-                                           uint64_t n, uint32_t tid, uint32_t nthr) {
-  for (uint64_t i = tid; i < n; i += nthr) d[i] = s[i];
-}
-
-template <bool AL>
-__device__ __forceinline__ void wg_copy(const uint8_t* s, uint8_t* d, uint64_t n) {
-  if constexpr (AL)
-    copy_aligned(s, d, n, threadIdx.x, blockDim.x);
-  else
-    copy_bytes(s, d, n, threadIdx.x, blockDim.x);
+  for (uint32_t b = done + tid; b < n; b += nthr)
+    __builtin_amdgcn_raw_buffer_store_b8(__builtin_amdgcn_raw_buffer_load_b8(rs, b, 0, LP), rd, b, 0,
+                                         SP);
 }
 
 // Per-workgroup state of one side of a lane across the messages of a launch.
@@ -205,9 +255,10 @@ __device__ __forceinline__ bool wg_failed(Shared& sh, uint32_t local_err, Status
 // ------------------------------------------------------------------ SIMPLE
 // Producer of message m: for each step g, wait for credit g - head < nslots,
 // write the chunk into slot g mod nslots, release, tail = g+1.
-template <int SC, bool AL>
+template <int SC, int ORD, bool AL>
 __device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
                             const uint8_t* src, uint64_t ticks, Shared& sh) {
+  using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = sd.base + m * sd.r.k + j;
@@ -220,7 +271,7 @@ __device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
         __builtin_amdgcn_s_sleep(1);
       }
       if (!err) {
-        fence_acquire<SC>();  // the consumer's reads of the slot precede our writes
+        O::acquire();  // the consumer's reads of the slot precede our writes
         sd.seen = h;
       }
     }
@@ -229,8 +280,8 @@ __device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
       uint64_t lo, hi;
       lane_share16(L, S, A.lanes, w, lo, hi);
       uint8_t* slot = A.fifo + (static_cast<uint64_t>(c) * A.nslots + g % A.nslots) * A.slot_bytes;
-      wg_copy<AL>(src + sd.r.beg + j * S + lo, slot + lo, hi - lo);
-      fence_release<SC>();
+      copy_pol<kPolNT, O::kShared, AL>(src + sd.r.beg + j * S + lo, slot + lo, hi - lo);
+      O::release();
     }
     if (wg_failed(sh, err, A.status)) return false;
     if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
@@ -240,9 +291,10 @@ __device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
 
 // Consumer of message m: wait for tail > g, acquire, copy the slot out,
 // release, head = g+1.
-template <int SC, bool AL>
+template <int SC, int ORD, bool AL>
 __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
                             uint8_t* dst, uint64_t ticks, Shared& sh) {
+  using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = sd.base + m * sd.r.k + j;
@@ -255,7 +307,7 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
         __builtin_amdgcn_s_sleep(1);
       }
       if (!err) {
-        fence_acquire<SC>();
+        O::acquire();
         sd.seen = t;
       }
     }
@@ -265,8 +317,8 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
       lane_share16(L, S, A.lanes, w, lo, hi);
       const uint8_t* slot =
           A.fifo + (static_cast<uint64_t>(c) * A.nslots + g % A.nslots) * A.slot_bytes;
-      wg_copy<AL>(slot + lo, dst + sd.r.beg + j * S + lo, hi - lo);
-      fence_release<SC>();  // our slot reads complete before the slot is handed back
+      copy_pol<O::kShared, kPolNT, AL>(slot + lo, dst + sd.r.beg + j * S + lo, hi - lo);
+      O::release();  // our slot reads complete before the slot is handed back
     }
     if (wg_failed(sh, err, A.status)) return false;
     if (threadIdx.x == 0) st_u64<SC>(&sd.lc->head, g + 1);
@@ -276,7 +328,7 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
 
 // ---------------------------------------------------------------------- LL
 // Line = {4 payload bytes, flag = g+1}, stored and loaded as one 64-bit
-// access; the last word of a chunk is zero-padded.
+// access at the connection's scope; the last word of a chunk is zero-padded.
 template <bool AL>
 __device__ __forceinline__ uint32_t ll_src_word(const uint8_t* p, uint64_t L, uint64_t line) {
   const uint64_t off = line * 4;
@@ -296,9 +348,10 @@ __device__ __forceinline__ void ll_dst_word(uint8_t* p, uint64_t L, uint64_t lin
   for (uint64_t b = 0; b < 4 && off + b < L; ++b) p[off + b] = static_cast<uint8_t>(v >> (8 * b));
 }
 
-template <int SC, bool AL>
+template <int SC, int ORD, bool AL>
 __device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
                         const uint8_t* src, uint64_t ticks, Shared& sh) {
+  using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
   uint32_t err = 0;
   for (uint64_t j = 0; j < sd.r.k && !err; ++j) {
@@ -311,7 +364,7 @@ __device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
         __builtin_amdgcn_s_sleep(1);
       }
       if (err) break;
-      fence_acquire<SC>();
+      O::acquire();
       sd.seen = h;
     }
     const uint64_t L = min(S, sd.r.len - j * S);
@@ -327,9 +380,10 @@ __device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
   return !wg_failed(sh, err, A.status);
 }
 
-template <int SC, bool AL>
+template <int SC, int ORD, bool AL>
 __device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
                         uint8_t* dst, uint64_t ticks, Shared& sh) {
+  using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
   const uint32_t nthr = blockDim.x;
   for (uint64_t j = 0; j < sd.r.k; ++j) {
@@ -373,7 +427,11 @@ __device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
         }
       }
     }
-    fence_release<SC>();  // our line reads complete before the slot is handed back
+    // Our line reads are complete before the slot is handed back: every
+    // value has been consumed by its flag test.  Coherent ordering needs
+    // nothing more (the destination stores may still be in flight); fenced
+    // ordering keeps its release fence.
+    if constexpr (ORD == kOrdFenced) O::release();
     if (wg_failed(sh, err, A.status)) return false;
     if (threadIdx.x == 0) st_u64<SC>(&sd.lc->head, g + 1);
   }
@@ -389,9 +447,10 @@ __device__ __forceinline__ void ll_close(Side& sd, uint64_t iters) {
 // --------------------------------------------------------------- zero-copy
 // Producer: take the published destination, clear the word, write the chunk
 // straight there, release, tail = g+1.
-template <int SC, bool AL>
+template <int SC, int ORD, bool AL>
 __device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
                         const uint8_t* src, uint64_t ticks, Shared& sh) {
+  using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = sd.base + m * sd.r.k + j;
@@ -405,7 +464,7 @@ __device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
       }
       if (threadIdx.x == 0) {
         if (!err) {
-          fence_acquire<SC>();
+          O::acquire();
           st_u64<SC>(&sd.lc->ptrx, 0);
         }
         sh.ptr = p;
@@ -416,8 +475,8 @@ __device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
     const uint64_t L = min(S, sd.r.len - j * S);
     uint64_t lo, hi;
     lane_share16(L, S, A.lanes, w, lo, hi);
-    wg_copy<AL>(src + sd.r.beg + j * S + lo, p, hi - lo);
-    fence_release<SC>();
+    copy_pol<kPolNT, O::kShared, AL>(src + sd.r.beg + j * S + lo, p, hi - lo);
+    O::release();
     if (wg_failed(sh, 0, A.status)) return false;
     if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
   }
@@ -426,9 +485,10 @@ __device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
 
 // Receiver (one thread): publish the destination of the next step whenever
 // the word is clear; complete step g once tail > g by publishing head.
-template <int SC>
+template <int SC, int ORD>
 __device__ void zc_recv(const ConnArgs& A, uint32_t w, Side& sd, uint64_t iters, uint8_t* dst,
                         uint64_t ticks) {
+  using O = Order<SC, ORD>;
   if (threadIdx.x != 0) return;
   const uint64_t total = iters * sd.r.k, S = A.step_bytes;
   uint64_t npub = 0, ndone = 0;
@@ -441,14 +501,14 @@ __device__ void zc_recv(const ConnArgs& A, uint32_t w, Side& sd, uint64_t iters,
       uint64_t lo, hi;
       lane_share16(L, S, A.lanes, w, lo, hi);
       const uint64_t addr = reinterpret_cast<uint64_t>(dst + sd.r.beg + j * S + lo);
-      fence_release<SC>();
+      O::release();
       st_u64<SC>(&sd.lc->ptrx, addr);
       ++npub;
       moved = true;
     }
     const uint64_t t = ld_u64<SC>(&sd.lc->tail);
     if (t > sd.base + ndone) {
-      fence_acquire<SC>();
+      O::acquire();
       st_u64<SC>(&sd.lc->head, t);
       ndone = t - sd.base;
       moved = true;
@@ -472,7 +532,7 @@ __device__ __forceinline__ uint32_t logical_wg(uint32_t remap, uint32_t total) {
   return remap ? (b % 8u) * (total / 8u) + b / 8u : b;
 }
 
-template <int PROTO, int SC, bool AL, int MAXB>
+template <int PROTO, int SC, int ORD, bool AL, int MAXB>
 __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
   __shared__ Shared sh;
   if (threadIdx.x == 0) sh.err = 0;
@@ -493,20 +553,20 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
   const uint64_t ticks = args.timeout_ticks;
   if constexpr (PROTO == kProtoZC) {
     if (role == 1) {
-      zc_recv<SC>(A, w, sd, args.iters, A.dst, ticks);
+      zc_recv<SC, ORD>(A, w, sd, args.iters, A.dst, ticks);
       return;
     }
   }
   for (uint32_t m = 0; m < args.iters; ++m) {
     bool ok;
     if constexpr (PROTO == kProtoSimple)
-      ok = role == 0 ? simple_send<SC, AL>(A, c, w, sd, m, A.src, ticks, sh)
-                     : simple_recv<SC, AL>(A, c, w, sd, m, A.dst, ticks, sh);
+      ok = role == 0 ? simple_send<SC, ORD, AL>(A, c, w, sd, m, A.src, ticks, sh)
+                     : simple_recv<SC, ORD, AL>(A, c, w, sd, m, A.dst, ticks, sh);
     else if constexpr (PROTO == kProtoLL)
-      ok = role == 0 ? ll_send<SC, AL>(A, c, w, sd, m, A.src, ticks, sh)
-                     : ll_recv<SC, AL>(A, c, w, sd, m, A.dst, ticks, sh);
+      ok = role == 0 ? ll_send<SC, ORD, AL>(A, c, w, sd, m, A.src, ticks, sh)
+                     : ll_recv<SC, ORD, AL>(A, c, w, sd, m, A.dst, ticks, sh);
     else
-      ok = zc_send<SC, AL>(A, c, w, sd, m, A.src, ticks, sh);
+      ok = zc_send<SC, ORD, AL>(A, c, w, sd, m, A.src, ticks, sh);
     if (!ok) return;
   }
   if constexpr (PROTO == kProtoLL) {
@@ -516,7 +576,7 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
 
 // Ping-pong: pair side 0 is endpoint X (send on fwd, then receive on rev),
 // side 1 is endpoint Y (receive on fwd into b, then send b on rev).
-template <int PROTO, int SC, bool AL>
+template <int PROTO, int SC, int ORD, bool AL>
 __global__ void __launch_bounds__(1024) ping_kernel(PingArgs args) {
   __shared__ Shared sh;
   if (threadIdx.x == 0) sh.err = 0;
@@ -535,18 +595,18 @@ __global__ void __launch_bounds__(1024) ping_kernel(PingArgs args) {
     bool ok;
     if (side == 0) {
       if constexpr (PROTO == kProtoLL)
-        ok = ll_send<SC, AL>(F, c, w, fs, it, F.src, ticks, sh) &&
-             ll_recv<SC, AL>(R, c, w, rs, it, R.dst, ticks, sh);
+        ok = ll_send<SC, ORD, AL>(F, c, w, fs, it, F.src, ticks, sh) &&
+             ll_recv<SC, ORD, AL>(R, c, w, rs, it, R.dst, ticks, sh);
       else
-        ok = simple_send<SC, AL>(F, c, w, fs, it, F.src, ticks, sh) &&
-             simple_recv<SC, AL>(R, c, w, rs, it, R.dst, ticks, sh);
+        ok = simple_send<SC, ORD, AL>(F, c, w, fs, it, F.src, ticks, sh) &&
+             simple_recv<SC, ORD, AL>(R, c, w, rs, it, R.dst, ticks, sh);
     } else {
       if constexpr (PROTO == kProtoLL)
-        ok = ll_recv<SC, AL>(F, c, w, fs, it, F.dst, ticks, sh) &&
-             ll_send<SC, AL>(R, c, w, rs, it, R.src, ticks, sh);
+        ok = ll_recv<SC, ORD, AL>(F, c, w, fs, it, F.dst, ticks, sh) &&
+             ll_send<SC, ORD, AL>(R, c, w, rs, it, R.src, ticks, sh);
       else
-        ok = simple_recv<SC, AL>(F, c, w, fs, it, F.dst, ticks, sh) &&
-             simple_send<SC, AL>(R, c, w, rs, it, R.src, ticks, sh);
+        ok = simple_recv<SC, ORD, AL>(F, c, w, fs, it, F.dst, ticks, sh) &&
+             simple_send<SC, ORD, AL>(R, c, w, rs, it, R.src, ticks, sh);
     }
     if (!ok) return;
   }
@@ -563,56 +623,72 @@ template <int MAXB>
 using RunFn = void (*)(RunArgs<MAXB>);
 using PingFn = void (*)(PingArgs);
 
-template <int MAXB, int P, int SC>
+template <int MAXB, int P, int SC, int ORD>
 RunFn<MAXB> pick_run_al(bool al) {
-  return al ? run_kernel<P, SC, true, MAXB> : run_kernel<P, SC, false, MAXB>;
+  return al ? run_kernel<P, SC, ORD, true, MAXB> : run_kernel<P, SC, ORD, false, MAXB>;
+}
+
+template <int MAXB, int P, int SC>
+RunFn<MAXB> pick_run_ord(int ord, bool al) {
+  return ord == kOrdFenced ? pick_run_al<MAXB, P, SC, kOrdFenced>(al)
+                           : pick_run_al<MAXB, P, SC, kOrdCoherent>(al);
 }
 
 template <int MAXB, int P>
-RunFn<MAXB> pick_run_sc(int sc, bool al) {
-  return sc == kScopeSystem ? pick_run_al<MAXB, P, kScopeSystem>(al)
-                            : pick_run_al<MAXB, P, kScopeAgent>(al);
+RunFn<MAXB> pick_run_sc(const Variant& v) {
+  return v.scope == kScopeSystem ? pick_run_ord<MAXB, P, kScopeSystem>(v.ordering, v.aligned)
+                                 : pick_run_ord<MAXB, P, kScopeAgent>(v.ordering, v.aligned);
 }
 
 template <int MAXB>
 RunFn<MAXB> pick_run(const Variant& v) {
   switch (v.proto) {
-    case kProtoSimple: return pick_run_sc<MAXB, kProtoSimple>(v.scope, v.aligned);
-    case kProtoLL: return pick_run_sc<MAXB, kProtoLL>(v.scope, v.aligned);
-    default: return pick_run_sc<MAXB, kProtoZC>(v.scope, v.aligned);
+    case kProtoSimple: return pick_run_sc<MAXB, kProtoSimple>(v);
+    case kProtoLL: return pick_run_sc<MAXB, kProtoLL>(v);
+    default: return pick_run_sc<MAXB, kProtoZC>(v);
   }
 }
 
-template <int P, int SC>
+template <int P, int SC, int ORD>
 PingFn pick_ping_al(bool al) {
-  return al ? ping_kernel<P, SC, true> : ping_kernel<P, SC, false>;
+  return al ? ping_kernel<P, SC, ORD, true> : ping_kernel<P, SC, ORD, false>;
+}
+
+template <int P, int SC>
+PingFn pick_ping_ord(int ord, bool al) {
+  return ord == kOrdFenced ? pick_ping_al<P, SC, kOrdFenced>(al)
+                           : pick_ping_al<P, SC, kOrdCoherent>(al);
 }
 
 template <int P>
-PingFn pick_ping_sc(int sc, bool al) {
-  return sc == kScopeSystem ? pick_ping_al<P, kScopeSystem>(al) : pick_ping_al<P, kScopeAgent>(al);
+PingFn pick_ping_sc(const Variant& v) {
+  return v.scope == kScopeSystem ? pick_ping_ord<P, kScopeSystem>(v.ordering, v.aligned)
+                                 : pick_ping_ord<P, kScopeAgent>(v.ordering, v.aligned);
 }
 
 PingFn pick_ping(const Variant& v) {
-  return v.proto == kProtoLL ? pick_ping_sc<kProtoLL>(v.scope, v.aligned)
-                             : pick_ping_sc<kProtoSimple>(v.scope, v.aligned);
+  return v.proto == kProtoLL ? pick_ping_sc<kProtoLL>(v) : pick_ping_sc<kProtoSimple>(v);
 }
 
 }  // namespace
 
+// hipLaunchKernel reports this launch's own status (no sticky error state).
+template <typename Fn, typename Args>
+static hipError_t launch(Fn fn, const Args& a, uint32_t grid, int block, hipStream_t s) {
+  void* kargs[] = {const_cast<Args*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(block), kargs, 0, s);
+}
+
 hipError_t launch_run1(const Variant& v, const RunArgs<1>& a, int block, hipStream_t s) {
-  hipLaunchKernelGGL(pick_run<1>(v), dim3(a.total_wgs), dim3(block), 0, s, a);
-  return hipGetLastError();
+  return launch(pick_run<1>(v), a, a.total_wgs, block, s);
 }
 
 hipError_t launch_runB(const Variant& v, const RunArgs<16>& a, int block, hipStream_t s) {
-  hipLaunchKernelGGL(pick_run<16>(v), dim3(a.total_wgs), dim3(block), 0, s, a);
-  return hipGetLastError();
+  return launch(pick_run<16>(v), a, a.total_wgs, block, s);
 }
 
 hipError_t launch_ping(const Variant& v, const PingArgs& a, int block, hipStream_t s) {
-  hipLaunchKernelGGL(pick_ping(v), dim3(a.total_wgs), dim3(block), 0, s, a);
-  return hipGetLastError();
+  return launch(pick_ping(v), a, a.total_wgs, block, s);
 }
 
 hipError_t max_resident(const Variant& v, int kind, int block, int* wgs) {

@@ -71,9 +71,10 @@ struct PingArgs {
 
 // Kernel-variant selector and launchers (kernels.hip).
 struct Variant {
-  int proto;    // kProto*
-  int scope;    // kScope*
-  int aligned;  // all of src/dst 16-byte aligned
+  int proto;     // kProto*
+  int scope;     // kScope*
+  int ordering;  // 0: coherent accesses, 1: scoped fences
+  int aligned;   // all of src/dst 16-byte aligned
 };
 
 hipError_t launch_run1(const Variant& v, const RunArgs<1>& a, int block, hipStream_t s);

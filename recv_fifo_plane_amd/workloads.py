@@ -8,7 +8,8 @@ W4  zero-copy through ptrExchange: one pair on 128 MiB, and a ring of 8
     logical endpoints built by the host schedule, endpoint r sending its
     128 MiB slice to (r + 1) mod 8, all edges in one launch.
 W5  host FIFO: 16 channels x 8 x 256 KiB in pinned host memory, 2 GiB of
-    messages with log-uniform sizes 1 KiB .. 64 MiB at consecutive offsets.
+    messages with log-uniform sizes 1 KiB .. 64 MiB at consecutive offsets;
+    the head/tail words sit in HBM, next to the side that polls them.
 """
 from __future__ import annotations
 
@@ -22,20 +23,20 @@ W2 = dict(name="ll_pingpong", proto="ll", nchannels=1, nslots=8, slot_bytes=32 <
 W2_SIZES = [8 << i for i in range(14)]  # 8 B .. 64 KiB
 
 W3 = dict(name="simple_32ch_1GiB", proto="simple", nchannels=32, nslots=8, slot_bytes=512 << 10,
-          fifo_loc="device", wgs_per_channel=4, block_threads=256, nbytes=1 << 30)
+          fifo_loc="device", wgs_per_channel=4, block_threads=512, nbytes=1 << 30)
 
-W4_PAIR = dict(name="zc_pair_128MiB", proto="zc", nchannels=4, nslots=1, slot_bytes=512 << 10,
-               fifo_loc="device", wgs_per_channel=4, block_threads=256, nbytes=128 << 20)
+W4_PAIR = dict(name="zc_pair_128MiB", proto="zc", nchannels=8, nslots=1, slot_bytes=512 << 10,
+               fifo_loc="device", wgs_per_channel=16, block_threads=128, nbytes=128 << 20)
 
 W4_RING = dict(name="zc_ring_8x128MiB", proto="zc", endpoints=8, channels_per_edge=4,
-               nslots=1, slot_bytes=512 << 10, fifo_loc="device", wgs_per_channel=4,
-               block_threads=256, slice_bytes=128 << 20, max_peers=128)
+               nslots=1, slot_bytes=512 << 10, fifo_loc="device", wgs_per_channel=16,
+               block_threads=128, slice_bytes=128 << 20, max_peers=128)
 
 W5 = dict(name="host_fifo_16ch_2GiB", proto="simple", nchannels=16, nslots=8,
-          slot_bytes=256 << 10, fifo_loc="host", wgs_per_channel=2, block_threads=256,
-          total_bytes=2 << 30)
+          slot_bytes=256 << 10, fifo_loc="host", wgs_per_channel=16, block_threads=256,
+          ctrl_loc=1, total_bytes=2 << 30)
 
-_ATTRS = ("wgs_per_channel", "block_threads", "ctrl_loc", "timeout_ms", "xcd_pairing")
+_ATTRS = ("wgs_per_channel", "block_threads", "ctrl_loc", "timeout_ms", "xcd_pairing", "ordering")
 
 
 def make_conn(cfg: dict, **override) -> X.Conn:

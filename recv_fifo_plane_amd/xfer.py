@@ -31,6 +31,8 @@ XFER_FIFO_HOST = 1
 XFER_CTRL_DEFAULT = 0
 XFER_CTRL_DEVICE = 1
 XFER_CTRL_HOST = 2
+XFER_ORDER_COHERENT = 0
+XFER_ORDER_FENCED = 1
 XFER_OP_RECV_SETUP = 0
 XFER_OP_SEND_SETUP = 1
 XFER_OP_CONNECT_BATCH = 2
@@ -49,7 +51,8 @@ class xfer_attr(C.Structure):
         ("timeout_ms", C.c_uint32),
         ("xcd_pairing", C.c_int),
         ("roles", C.c_int),
-        ("reserved", C.c_int * 2),
+        ("ordering", C.c_int),
+        ("reserved", C.c_int),
     ]
 
 
@@ -165,7 +168,7 @@ class Conn:
 
     def __init__(self, proto="simple", nchannels=1, nslots=8, slot_bytes=128 << 10,
                  fifo_loc="device", wgs_per_channel=0, block_threads=0, ctrl_loc=0,
-                 timeout_ms=0, xcd_pairing=0, roles=0, _handle=None):
+                 timeout_ms=0, xcd_pairing=0, roles=0, ordering=0, _handle=None):
         self.proto = PROTOS[proto] if isinstance(proto, str) else int(proto)
         self.nchannels = int(nchannels)
         self.nslots = int(nslots)
@@ -176,7 +179,7 @@ class Conn:
             self._h = _handle
             return
         attr = xfer_attr(int(wgs_per_channel), int(block_threads), int(ctrl_loc), int(timeout_ms),
-                         int(xcd_pairing), int(roles))
+                         int(xcd_pairing), int(roles), int(ordering))
         h = _vp()
         check(lib().xfer_conn_create_ex(self.proto, self.nchannels, self.nslots, self.slot_bytes,
                                         self.fifo_loc, C.byref(attr), C.byref(h)))
@@ -291,7 +294,8 @@ def endpoints_connect(nranks: int, recv_masks, send_masks, max_peers: int = 128,
     fl = FIFO_LOCS[fifo_loc] if isinstance(fifo_loc, str) else int(fifo_loc)
     a = xfer_attr(int(attr.get("wgs_per_channel", 0)), int(attr.get("block_threads", 0)),
                   int(attr.get("ctrl_loc", 0)), int(attr.get("timeout_ms", 0)),
-                  int(attr.get("xcd_pairing", 0)), int(attr.get("roles", 0)))
+                  int(attr.get("xcd_pairing", 0)), int(attr.get("roles", 0)),
+                  int(attr.get("ordering", 0)))
     edges = (_vp * (nranks * nranks))()
     ne = C.c_int()
     check(lib().xfer_endpoints_connect(nranks, rm.ctypes.data_as(_u64p), sm.ctypes.data_as(_u64p),

@@ -54,3 +54,21 @@ def test_xcd_pairing_either_way(xcd_pairing):
     # 8 channels x 1 lane -> 16 workgroups: the pairing remap is active when on
     for proto in ("simple", "ll", "zc"):
         run_transfers(proto, 8, 2, 4096, [1 << 20, 4097], xcd_pairing=xcd_pairing)
+
+
+@pytest.mark.parametrize("fifo_loc", ["device", "host"])
+@pytest.mark.parametrize("proto", ["simple", "ll", "zc"])
+def test_fenced_ordering(proto, fifo_loc):
+    # the scoped-fence ordering must give the same bytes and counters
+    run_transfers(proto, 3, 2, 4096, SIZES, fifo_loc=fifo_loc, lanes=2, ordering=1,
+                  src_off=0, dst_off=0)
+    run_transfers(proto, 2, 3, 512, [5000, 33], fifo_loc=fifo_loc, lanes=2, ordering=1,
+                  src_off=3, dst_off=7)
+
+
+def test_many_steps_through_few_slots():
+    # long runs over 1-2 slots exercise slot reuse: every byte of every step
+    # must come from its own step
+    for proto in ("simple", "ll"):
+        run_transfers(proto, 4, 1, 1024, [4 << 20], lanes=4)
+        run_transfers(proto, 8, 2, 4096, [16 << 20], lanes=2, block=512)
