@@ -151,28 +151,14 @@ __device__ __forceinline__ Range chan_range(uint64_t n, uint32_t nch, uint32_t c
   return r;
 }
 
-// Lane w's part of a chunk of L <= S bytes.  Each lane owns a fixed slice of
-// the slot, cut from the full step size S (16-byte granular), so a slot byte
-// is always written and drained by the same lane pair and one lane's head
-// covers every byte its producer will overwrite; a short chunk just leaves
-// the upper slices empty.
-__device__ __forceinline__ void lane_share16(uint64_t L, uint64_t S, uint32_t P, uint32_t w,
-                                             uint64_t& lo, uint64_t& hi) {
-  const uint64_t sub = (((S + P - 1) / P) + 15) & ~uint64_t(15);
-  lo = min(L, static_cast<uint64_t>(w) * sub);
-  hi = min(L, static_cast<uint64_t>(w + 1) * sub);
-}
-
-// Lane w's lines of an LL chunk of L <= S payload bytes (one line per 4
-// bytes), again a fixed slice of the slot's S / 4 lines.
-__device__ __forceinline__ void lane_share_lines(uint64_t L, uint64_t S, uint32_t P, uint32_t w,
-                                                 uint64_t& lo, uint64_t& hi) {
-  const uint64_t nl = (L + 3) / 4;
-  const uint64_t sub = (S / 4 + P - 1) / P;
-  lo = min(nl, static_cast<uint64_t>(w) * sub);
-  hi = min(nl, static_cast<uint64_t>(w + 1) * sub);
-}
-
+// ------------------------------------------------------------ lane blocks
+// A slot is cut into blocks of blockDim.x 16-byte vectors (one per thread);
+// lane w of P owns blocks w, w + P, w + 2P, ...  Ownership depends only on
+// the position in the slot, never on the chunk length, so a slot byte is
+// always written and drained by the same lane pair and that lane's head
+// covers every byte its producer will overwrite.  A short chunk still
+// spreads over as many lanes as it has blocks.  LL uses the same map over
+// lines (a block is blockDim.x lines).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer descriptor over n bytes: the buffer unit checks every access
@@ -182,38 +168,139 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* p, ui
                                            0x00020000);
 }
 
-// Workgroup copy of n (< 2^31) bytes with load policy LP and store policy SP.
-// Aligned (both ends 16-byte aligned): 16-byte vectors, kUnroll loads in
-// flight per thread before their stores, ragged tail bytewise.  Otherwise
-// bytewise.  The descriptors are opaque to alias analysis, so the batch of
-// loads stays ahead of the stores.
-template <int LP, int SP, bool AL>
-__device__ __forceinline__ void copy_pol(const uint8_t* s, uint8_t* d, uint64_t n64) {
-  const uint32_t n = static_cast<uint32_t>(n64);
-  if (n == 0) return;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, n), rd = make_rsrc(d, n);
-  const uint32_t tid = threadIdx.x, nthr = blockDim.x;
-  uint32_t done = 0;
-  if constexpr (AL) {
-    const uint32_t nv = n >> 4;
-    uint32_t i = tid;
-    for (; i + (kUnroll - 1) * nthr < nv; i += kUnroll * nthr) {
-      u32x4 r[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        r[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (i + u * nthr) << 4, 0, LP);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        __builtin_amdgcn_raw_buffer_store_b128(r[u], rd, (i + u * nthr) << 4, 0, SP);
-    }
-    for (; i < nv; i += nthr)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(rs, i << 4, 0, LP),
-                                             rd, i << 4, 0, SP);
-    done = nv << 4;
+// Two fixed lane layouts (CYC template argument); both give every slot byte
+// one owning lane whatever the chunk length:
+//  * contiguous (SIMPLE): lane w owns the slice [w * sub, (w + 1) * sub) of
+//    the slot, sub = S / P rounded up to 16 bytes -- measured faster for the
+//    FIFO round trip;
+//  * block-cyclic (zero-copy): blocks of blockDim.x vectors dealt round-robin
+//    to the lanes -- measured faster for writes straight into B, and short
+//    chunks spread over more lanes.
+// A LaneSpan is the lane's addressable part of a chunk of L16 vector bytes:
+// base = first byte, lim = bytes addressable from base.
+struct LaneSpan {
+  uint32_t base, lim;
+};
+
+__device__ __forceinline__ uint32_t contiguous_slice(uint64_t S, uint32_t P) {
+  return static_cast<uint32_t>((((S + P - 1) / P) + 15) & ~uint64_t(15));
+}
+
+template <bool CYC>
+__device__ __forceinline__ LaneSpan lane_span(uint32_t L16, uint64_t S, uint32_t P, uint32_t w) {
+  if constexpr (CYC) {
+    return LaneSpan{0, L16};
+  } else {
+    const uint32_t sub = contiguous_slice(S, P);
+    const uint32_t lo = min(L16, w * sub), hi = min(L16, (w + 1) * sub);
+    return LaneSpan{lo, hi - lo};
   }
-  for (uint32_t b = done + tid; b < n; b += nthr)
-    __builtin_amdgcn_raw_buffer_store_b8(__builtin_amdgcn_raw_buffer_load_b8(rs, b, 0, LP), rd, b, 0,
-                                         SP);
+}
+
+// Byte offset (from the lane's base) of this thread's u-th vector.
+template <bool CYC>
+__device__ __forceinline__ uint32_t lane_vec(uint32_t w, uint32_t P, uint32_t u) {
+  if constexpr (CYC)
+    return ((w + u * P) * blockDim.x + threadIdx.x) << 4;
+  else
+    return (u * blockDim.x + threadIdx.x) << 4;
+}
+
+// Vector groups (of blockDim.x vectors) a lane covers in a full step of S bytes.
+template <bool CYC>
+__device__ __forceinline__ uint32_t lane_blocks(uint64_t S, uint32_t P) {
+  const uint32_t B = blockDim.x * 16u;
+  if constexpr (CYC) {
+    const uint64_t nb = (S + B - 1) / B;
+    return static_cast<uint32_t>((nb + P - 1) / P);
+  } else {
+    return (contiguous_slice(S, P) + B - 1) / B;
+  }
+}
+
+// Bytes of a chunk past its last whole vector (only the final chunk of a
+// transfer has them) are copied bytewise by the lane that owns offset L16.
+template <int LP, int SP, bool CYC>
+__device__ __forceinline__ void lane_tail(const uint8_t* s, uint8_t* d, uint32_t L, uint64_t S,
+                                          uint32_t P, uint32_t w) {
+  const uint32_t L16 = L & ~15u;
+  if (L == L16 || threadIdx.x >= L - L16) return;
+  uint32_t owner;
+  if constexpr (CYC)
+    owner = (L16 / (blockDim.x * 16u)) % P;
+  else
+    owner = min(P - 1, L16 / contiguous_slice(S, P));
+  if (owner != w) return;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, L), rd = make_rsrc(d, L);
+  __builtin_amdgcn_raw_buffer_store_b8(
+      __builtin_amdgcn_raw_buffer_load_b8(rs, L16 + threadIdx.x, 0, LP), rd, L16 + threadIdx.x, 0,
+      SP);
+}
+
+// Lane w's share of a chunk of L (< 2^31) bytes, from s to d (both chunk
+// bases), with load policy LP and store policy SP: kUnroll vectors in
+// flight per thread before their stores.  Either end may sit at any byte
+// address: compute queues run in unaligned-access mode (the FIFO side is
+// always 16-byte aligned).  The descriptors are opaque to alias analysis,
+// so a batch of loads stays ahead of its stores.
+template <int LP, int SP, bool CYC>
+__device__ __forceinline__ void lane_copy(const uint8_t* s, uint8_t* d, uint64_t L64, uint64_t S,
+                                          uint32_t P, uint32_t w) {
+  const uint32_t L = static_cast<uint32_t>(L64);
+  const LaneSpan sp = lane_span<CYC>(L & ~15u, S, P, w);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s + sp.base, sp.lim),
+                               rd = make_rsrc(d + sp.base, sp.lim);
+  const uint32_t B = blockDim.x * 16u;
+  const uint32_t groups = (sp.lim + B - 1) / B;  // vector groups spanned from base
+  for (uint32_t u0 = 0; (CYC ? w + u0 * P : u0) < groups; u0 += kUnroll) {
+    u32x4 r[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      r[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_vec<CYC>(w, P, u0 + u), 0, LP);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      __builtin_amdgcn_raw_buffer_store_b128(r[u], rd, lane_vec<CYC>(w, P, u0 + u), 0, SP);
+  }
+  lane_tail<LP, SP, CYC>(s, d, L, S, P, w);
+}
+
+// A lane's share of one step held in registers (software-pipelined
+// producers): kUnroll vectors per thread.  Every thread always issues
+// exactly kUnroll loads or stores; the buffer unit drops the ones past the
+// chunk (loads read 0), so the count of accesses in flight is a constant.
+struct Batch {
+  u32x4 r[kUnroll];
+};
+
+template <int LP, bool CYC>
+__device__ __forceinline__ void batch_load(Batch& b, const uint8_t* s, uint32_t L, uint64_t S,
+                                           uint32_t P, uint32_t w) {
+  const LaneSpan sp = lane_span<CYC>(L & ~15u, S, P, w);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s + sp.base, sp.lim);
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    b.r[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_vec<CYC>(w, P, u), 0, LP);
+}
+
+template <int SP, bool CYC>
+__device__ __forceinline__ void batch_store(const Batch& b, uint8_t* d, uint32_t L, uint64_t S,
+                                            uint32_t P, uint32_t w) {
+  const LaneSpan sp = lane_span<CYC>(L & ~15u, S, P, w);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(d + sp.base, sp.lim);
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    __builtin_amdgcn_raw_buffer_store_b128(b.r[u], rd, lane_vec<CYC>(w, P, u), 0, SP);
+}
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt in bits
+// [3:0] and [15:14]).  Vector memory operations complete in issue order, so
+// after "stores, then N loads" vmcnt(N) means the stores are complete.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  compiler_fence();
 }
 
 // Per-workgroup state of one side of a lane across the messages of a launch.
@@ -252,7 +339,67 @@ __device__ __forceinline__ bool wg_failed(Shared& sh, uint32_t local_err, Status
   return e != 0;
 }
 
+__device__ __forceinline__ uint8_t* slot_of(const ConnArgs& A, uint32_t c, uint64_t g) {
+  return A.fifo + (static_cast<uint64_t>(c) * A.nslots + g % A.nslots) * A.slot_bytes;
+}
+
+__device__ __forceinline__ uint32_t chunk_len(const Side& sd, uint64_t S, uint64_t j) {
+  return static_cast<uint32_t>(min(S, sd.r.len - j * S));
+}
+
 // ------------------------------------------------------------------ SIMPLE
+// Waits until step g has credit: g < head + nslots (wave-uniform poll of the
+// lane's head).  Written without a subtraction because head may run ahead
+// of g: an LL consumer whose lane owns no lines of a step has nothing to
+// wait for and frees that step at once.
+template <int SC, int ORD>
+__device__ __forceinline__ uint32_t wait_credit(const ConnArgs& A, Side& sd, uint64_t g,
+                                                uint64_t ticks) {
+  if (g < sd.seen + A.nslots) return 0;
+  Deadline dl(ticks, A.status);
+  uint64_t h;
+  while (g >= (h = wave_load<SC>(&sd.lc->head)) + A.nslots) {
+    const uint32_t err = dl.expired();
+    if (err) return err;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  Order<SC, ORD>::acquire();  // the consumer's reads of the slot precede our writes
+  sd.seen = h;
+  return 0;
+}
+
+// Coherent producer whose share of a step fits one register batch, software
+// pipelined: the source of step j+1 is loaded while the FIFO stores of
+// step j drain, and vmcnt(kUnroll) then covers exactly those stores.
+template <int SC, int ORD>
+__device__ bool simple_send_piped(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
+                                  const uint8_t* src, uint64_t ticks, Shared& sh) {
+  using O = Order<SC, ORD>;
+  const uint64_t S = A.step_bytes;
+  const uint32_t P = A.lanes;
+  Batch b;
+  batch_load<kPolNT, false>(b, src + sd.r.beg, chunk_len(sd, S, 0), S, P, w);
+  for (uint64_t j = 0; j < sd.r.k; ++j) {
+    const uint64_t g = sd.base + m * sd.r.k + j;
+    const uint32_t err = wait_credit<SC, ORD>(A, sd, g, ticks);
+    if (!err) {
+      const uint32_t L = chunk_len(sd, S, j);
+      uint8_t* slot = slot_of(A, c, g);
+      batch_store<O::kShared, false>(b, slot, L, S, P, w);
+      lane_tail<kPolNT, O::kShared, false>(src + sd.r.beg + j * S, slot, L, S, P, w);
+      if (j + 1 < sd.r.k) {
+        batch_load<kPolNT, false>(b, src + sd.r.beg + (j + 1) * S, chunk_len(sd, S, j + 1), S, P, w);
+        wait_vmcnt<kUnroll>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    }
+    if (wg_failed(sh, err, A.status)) return false;
+    if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
+  }
+  return true;
+}
+
 // Producer of message m: for each step g, wait for credit g - head < nslots,
 // write the chunk into slot g mod nslots, release, tail = g+1.
 template <int SC, int ORD, bool AL>
@@ -260,27 +407,16 @@ __device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
                             const uint8_t* src, uint64_t ticks, Shared& sh) {
   using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
+  if constexpr (ORD == kOrdCoherent) {
+    if (lane_blocks<false>(S, A.lanes) <= kUnroll)
+      return simple_send_piped<SC, ORD>(A, c, w, sd, m, src, ticks, sh);
+  }
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = sd.base + m * sd.r.k + j;
-    uint32_t err = 0;
-    if (g - sd.seen >= A.nslots) {
-      Deadline dl(ticks, A.status);
-      uint64_t h;
-      while (g - (h = wave_load<SC>(&sd.lc->head)) >= A.nslots) {
-        if ((err = dl.expired())) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      if (!err) {
-        O::acquire();  // the consumer's reads of the slot precede our writes
-        sd.seen = h;
-      }
-    }
+    const uint32_t err = wait_credit<SC, ORD>(A, sd, g, ticks);
     if (!err) {
-      const uint64_t L = min(S, sd.r.len - j * S);
-      uint64_t lo, hi;
-      lane_share16(L, S, A.lanes, w, lo, hi);
-      uint8_t* slot = A.fifo + (static_cast<uint64_t>(c) * A.nslots + g % A.nslots) * A.slot_bytes;
-      copy_pol<kPolNT, O::kShared, AL>(src + sd.r.beg + j * S + lo, slot + lo, hi - lo);
+      lane_copy<kPolNT, O::kShared, false>(src + sd.r.beg + j * S, slot_of(A, c, g), chunk_len(sd, S, j),
+                                    S, A.lanes, w);
       O::release();
     }
     if (wg_failed(sh, err, A.status)) return false;
@@ -290,7 +426,7 @@ __device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
 }
 
 // Consumer of message m: wait for tail > g, acquire, copy the slot out,
-// release, head = g+1.
+// head = g+1.
 template <int SC, int ORD, bool AL>
 __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
                             uint8_t* dst, uint64_t ticks, Shared& sh) {
@@ -312,13 +448,12 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
       }
     }
     if (!err) {
-      const uint64_t L = min(S, sd.r.len - j * S);
-      uint64_t lo, hi;
-      lane_share16(L, S, A.lanes, w, lo, hi);
-      const uint8_t* slot =
-          A.fifo + (static_cast<uint64_t>(c) * A.nslots + g % A.nslots) * A.slot_bytes;
-      copy_pol<O::kShared, kPolNT, AL>(slot + lo, dst + sd.r.beg + j * S + lo, hi - lo);
-      O::release();  // our slot reads complete before the slot is handed back
+      lane_copy<O::kShared, kPolNT, false>(slot_of(A, c, g), dst + sd.r.beg + j * S, chunk_len(sd, S, j),
+                                    S, A.lanes, w);
+      // Our slot reads are complete before the slot is handed back: each
+      // loaded value has already fed its store.  Coherent ordering needs no
+      // wait for the destination stores; fenced ordering keeps its fence.
+      if constexpr (ORD == kOrdFenced) O::release();
     }
     if (wg_failed(sh, err, A.status)) return false;
     if (threadIdx.x == 0) st_u64<SC>(&sd.lc->head, g + 1);
@@ -351,31 +486,21 @@ __device__ __forceinline__ void ll_dst_word(uint8_t* p, uint64_t L, uint64_t lin
 template <int SC, int ORD, bool AL>
 __device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
                         const uint8_t* src, uint64_t ticks, Shared& sh) {
-  using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
+  const uint32_t P = A.lanes, nthr = blockDim.x;
   uint32_t err = 0;
   for (uint64_t j = 0; j < sd.r.k && !err; ++j) {
     const uint64_t g = sd.base + m * sd.r.k + j;
-    if (g - sd.seen >= A.nslots) {
-      Deadline dl(ticks, A.status);
-      uint64_t h;
-      while (g - (h = wave_load<SC>(&sd.lc->head)) >= A.nslots) {
-        if ((err = dl.expired())) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      if (err) break;
-      O::acquire();
-      sd.seen = h;
-    }
-    const uint64_t L = min(S, sd.r.len - j * S);
-    uint64_t lo, hi;
-    lane_share_lines(L, S, A.lanes, w, lo, hi);
-    uint64_t* lines = reinterpret_cast<uint64_t*>(
-        A.fifo + (static_cast<uint64_t>(c) * A.nslots + g % A.nslots) * A.slot_bytes);
+    if ((err = wait_credit<SC, ORD>(A, sd, g, ticks))) break;
+    const uint32_t L = chunk_len(sd, S, j);
+    const uint64_t nl = (L + 3) / 4;
+    uint64_t* lines = reinterpret_cast<uint64_t*>(slot_of(A, c, g));
     const uint8_t* s = src + sd.r.beg + j * S;
     const uint64_t flag = static_cast<uint64_t>(static_cast<uint32_t>(g + 1)) << 32;
-    for (uint64_t i = lo + threadIdx.x; i < hi; i += blockDim.x)
-      st_u64<SC>(&lines[i], flag | ll_src_word<AL>(s, L, i));
+    for (uint64_t blk = w; blk * nthr < nl; blk += P) {
+      const uint64_t i = blk * nthr + threadIdx.x;
+      if (i < nl) st_u64<SC>(&lines[i], flag | ll_src_word<AL>(s, L, i));
+    }
   }
   return !wg_failed(sh, err, A.status);
 }
@@ -385,24 +510,22 @@ __device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
                         uint8_t* dst, uint64_t ticks, Shared& sh) {
   using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
-  const uint32_t nthr = blockDim.x;
+  const uint32_t P = A.lanes, nthr = blockDim.x;
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = sd.base + m * sd.r.k + j;
     const uint32_t want = static_cast<uint32_t>(g + 1);
-    const uint64_t L = min(S, sd.r.len - j * S);
-    uint64_t lo, hi;
-    lane_share_lines(L, S, A.lanes, w, lo, hi);
-    const uint64_t* lines = reinterpret_cast<const uint64_t*>(
-        A.fifo + (static_cast<uint64_t>(c) * A.nslots + g % A.nslots) * A.slot_bytes);
+    const uint32_t L = chunk_len(sd, S, j);
+    const uint64_t nl = (L + 3) / 4;
+    const uint64_t* lines = reinterpret_cast<const uint64_t*>(slot_of(A, c, g));
     uint8_t* d = dst + sd.r.beg + j * S;
     uint32_t err = 0;
-    for (uint64_t i0 = lo + threadIdx.x; i0 < hi && !err; i0 += static_cast<uint64_t>(kLLUnroll) * nthr) {
+    for (uint64_t b0 = w; b0 * nthr < nl && !err; b0 += static_cast<uint64_t>(kLLUnroll) * P) {
       uint64_t v[kLLUnroll];
       bool pend = false;
 #pragma unroll
       for (int u = 0; u < kLLUnroll; ++u) {
-        const uint64_t i = i0 + static_cast<uint64_t>(u) * nthr;
-        v[u] = i < hi ? ld_u64<SC>(&lines[i]) : (static_cast<uint64_t>(want) << 32);
+        const uint64_t i = (b0 + static_cast<uint64_t>(u) * P) * nthr + threadIdx.x;
+        v[u] = i < nl ? ld_u64<SC>(&lines[i]) : (static_cast<uint64_t>(want) << 32);
         pend |= static_cast<uint32_t>(v[u] >> 32) != want;
       }
       if (pend) {
@@ -412,7 +535,7 @@ __device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
 #pragma unroll
           for (int u = 0; u < kLLUnroll; ++u) {
             if (static_cast<uint32_t>(v[u] >> 32) != want) {
-              v[u] = ld_u64<SC>(&lines[i0 + static_cast<uint64_t>(u) * nthr]);
+              v[u] = ld_u64<SC>(&lines[(b0 + static_cast<uint64_t>(u) * P) * nthr + threadIdx.x]);
               pend |= static_cast<uint32_t>(v[u] >> 32) != want;
             }
           }
@@ -422,8 +545,8 @@ __device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
       if (!err) {
 #pragma unroll
         for (int u = 0; u < kLLUnroll; ++u) {
-          const uint64_t i = i0 + static_cast<uint64_t>(u) * nthr;
-          if (i < hi) ll_dst_word<AL>(d, L, i, static_cast<uint32_t>(v[u]));
+          const uint64_t i = (b0 + static_cast<uint64_t>(u) * P) * nthr + threadIdx.x;
+          if (i < nl) ll_dst_word<AL>(d, L, i, static_cast<uint32_t>(v[u]));
         }
       }
     }
@@ -445,6 +568,61 @@ __device__ __forceinline__ void ll_close(Side& sd, uint64_t iters) {
 }
 
 // --------------------------------------------------------------- zero-copy
+// Wave 0 waits for a published destination (the base of the step's chunk in
+// B), takes it and clears the word; the address reaches the other waves
+// through LDS after the caller's barrier.
+template <int SC, int ORD>
+__device__ __forceinline__ uint32_t take_address(const ConnArgs& A, Side& sd, uint64_t ticks,
+                                                 Shared& sh) {
+  uint32_t err = 0;
+  if (threadIdx.x < 64) {
+    Deadline dl(ticks, A.status);
+    uint64_t p;
+    while ((p = wave_load<SC>(&sd.lc->ptrx)) == 0) {
+      if ((err = dl.expired())) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (threadIdx.x == 0) {
+      if (!err) {
+        Order<SC, ORD>::acquire();
+        st_u64<SC>(&sd.lc->ptrx, 0);
+      }
+      sh.ptr = p;
+    }
+  }
+  return err;
+}
+
+// Coherent zero-copy producer whose share fits one register batch,
+// pipelined like simple_send_piped (the source does not depend on the
+// address).
+template <int SC, int ORD>
+__device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t m,
+                              const uint8_t* src, uint64_t ticks, Shared& sh) {
+  using O = Order<SC, ORD>;
+  const uint64_t S = A.step_bytes;
+  const uint32_t P = A.lanes;
+  Batch b;
+  batch_load<kPolNT, true>(b, src + sd.r.beg, chunk_len(sd, S, 0), S, P, w);
+  for (uint64_t j = 0; j < sd.r.k; ++j) {
+    const uint64_t g = sd.base + m * sd.r.k + j;
+    if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh), A.status)) return false;
+    uint8_t* p = reinterpret_cast<uint8_t*>(sh.ptr);
+    const uint32_t L = chunk_len(sd, S, j);
+    batch_store<O::kShared, true>(b, p, L, S, P, w);
+    lane_tail<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, p, L, S, P, w);
+    if (j + 1 < sd.r.k) {
+      batch_load<kPolNT, true>(b, src + sd.r.beg + (j + 1) * S, chunk_len(sd, S, j + 1), S, P, w);
+      wait_vmcnt<kUnroll>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    if (wg_failed(sh, 0, A.status)) return false;
+    if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
+  }
+  return true;
+}
+
 // Producer: take the published destination, clear the word, write the chunk
 // straight there, release, tail = g+1.
 template <int SC, int ORD, bool AL>
@@ -452,30 +630,15 @@ __device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
                         const uint8_t* src, uint64_t ticks, Shared& sh) {
   using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
+  if constexpr (ORD == kOrdCoherent) {
+    if (lane_blocks<true>(S, A.lanes) <= kUnroll)
+      return zc_send_piped<SC, ORD>(A, w, sd, m, src, ticks, sh);
+  }
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = sd.base + m * sd.r.k + j;
-    uint32_t err = 0;
-    if (threadIdx.x < 64) {  // wave 0 takes the address
-      Deadline dl(ticks, A.status);
-      uint64_t p;
-      while ((p = wave_load<SC>(&sd.lc->ptrx)) == 0) {
-        if ((err = dl.expired())) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      if (threadIdx.x == 0) {
-        if (!err) {
-          O::acquire();
-          st_u64<SC>(&sd.lc->ptrx, 0);
-        }
-        sh.ptr = p;
-      }
-    }
-    if (wg_failed(sh, err, A.status)) return false;
-    uint8_t* p = reinterpret_cast<uint8_t*>(sh.ptr);
-    const uint64_t L = min(S, sd.r.len - j * S);
-    uint64_t lo, hi;
-    lane_share16(L, S, A.lanes, w, lo, hi);
-    copy_pol<kPolNT, O::kShared, AL>(src + sd.r.beg + j * S + lo, p, hi - lo);
+    if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh), A.status)) return false;
+    lane_copy<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, reinterpret_cast<uint8_t*>(sh.ptr),
+                                  chunk_len(sd, S, j), S, A.lanes, w);
     O::release();
     if (wg_failed(sh, 0, A.status)) return false;
     if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
@@ -486,7 +649,7 @@ __device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
 // Receiver (one thread): publish the destination of the next step whenever
 // the word is clear; complete step g once tail > g by publishing head.
 template <int SC, int ORD>
-__device__ void zc_recv(const ConnArgs& A, uint32_t w, Side& sd, uint64_t iters, uint8_t* dst,
+__device__ void zc_recv(const ConnArgs& A, Side& sd, uint64_t iters, uint8_t* dst,
                         uint64_t ticks) {
   using O = Order<SC, ORD>;
   if (threadIdx.x != 0) return;
@@ -496,11 +659,7 @@ __device__ void zc_recv(const ConnArgs& A, uint32_t w, Side& sd, uint64_t iters,
   while (ndone < total) {
     bool moved = false;
     if (npub < total && ld_u64<SC>(&sd.lc->ptrx) == 0) {
-      const uint64_t j = npub % sd.r.k;
-      const uint64_t L = min(S, sd.r.len - j * S);
-      uint64_t lo, hi;
-      lane_share16(L, S, A.lanes, w, lo, hi);
-      const uint64_t addr = reinterpret_cast<uint64_t>(dst + sd.r.beg + j * S + lo);
+      const uint64_t addr = reinterpret_cast<uint64_t>(dst + sd.r.beg + (npub % sd.r.k) * S);
       O::release();
       st_u64<SC>(&sd.lc->ptrx, addr);
       ++npub;
@@ -553,7 +712,7 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
   const uint64_t ticks = args.timeout_ticks;
   if constexpr (PROTO == kProtoZC) {
     if (role == 1) {
-      zc_recv<SC, ORD>(A, w, sd, args.iters, A.dst, ticks);
+      zc_recv<SC, ORD>(A, sd, args.iters, A.dst, ticks);
       return;
     }
   }

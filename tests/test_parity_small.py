@@ -72,3 +72,31 @@ def test_many_steps_through_few_slots():
     for proto in ("simple", "ll"):
         run_transfers(proto, 4, 1, 1024, [4 << 20], lanes=4)
         run_transfers(proto, 8, 2, 4096, [16 << 20], lanes=2, block=512)
+
+
+@pytest.mark.parametrize("proto", ["simple", "zc"])
+@pytest.mark.parametrize("src_off,dst_off", [(3, 7), (1, 1), (0, 9), (12, 0)])
+def test_misaligned_large_pipelined(proto, src_off, dst_off):
+    # lane slices that fit one register batch take the pipelined producer
+    run_transfers(proto, 8, 4, 64 << 10, [(8 << 20) + 5, 4097], src_off=src_off,
+                  dst_off=dst_off, lanes=4, block=256)
+
+
+@pytest.mark.parametrize("fifo_loc", ["device", "host"])
+def test_messages_at_arbitrary_offsets(fifo_loc):
+    # consecutive messages of odd sizes on one connection, as the host-FIFO
+    # workload issues them: every message after the first starts misaligned
+    import synth
+    sizes = synth.log_uniform_message_sizes(24 << 20, 77, lo_exp=4, hi_exp=22)
+    run_transfers("simple", 16, 8, 256 << 10, sizes[:40], fifo_loc=fifo_loc, lanes=4,
+                  src_off=5, dst_off=11, ctrl_loc=1)
+
+
+@pytest.mark.parametrize("fifo_loc", ["device", "host"])
+@pytest.mark.parametrize("nslots", [1, 2])
+def test_ll_lanes_that_own_no_lines(fifo_loc, nslots):
+    # a 2 KiB LL slot holds 256 lines = one block of a 256-thread workgroup,
+    # so lanes 1..3 never own a line: their consumers free every step at once
+    # and run ahead of their producers, whose credit test must still hold
+    run_transfers("ll", 2, nslots, 2048, [100_000, 5, 40_000], fifo_loc=fifo_loc, lanes=4,
+                  kind="int32")
