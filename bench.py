@@ -207,11 +207,16 @@ def bench_w5(torch, T, W, synth):
     a = torch.from_numpy(synth.uint8_uniform(tot, synth.workload_seed(5))).to("cuda")
     b = torch.empty_like(a)
     conn = W.make_conn(cfg)
-    total, _ = T.time_launches(lambda: W.run_messages(conn, a, b, sizes, T.stream), 1, 3)
+    each, _ = T.time_launches(lambda: W.run_messages(conn, a, b, sizes, T.stream), 1, 3)
     check_no_error(conn, cfg["nchannels"], "W5")
-    ok = bool(torch.equal(a, b))
+    ok_each = bool(torch.equal(a, b))
+    b.zero_()
+    total, _ = T.time_launches(lambda: W.run_message_list(conn, a, b, sizes, T.stream), 1, 3)
+    check_no_error(conn, cfg["nchannels"], "W5")
+    ok = ok_each and bool(torch.equal(a, b))
     conn.close()
     gbs = tot / (total * 1e-3) / 1e9
+    gbs_each = tot / (each * 1e-3) / 1e9
     # pinned-memory copy ceilings of the same link, for context
     h = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
     d = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -219,6 +224,10 @@ def bench_w5(torch, T, W, synth):
     h2d, _ = T.time_launches(lambda: d.copy_(h, non_blocking=True), 2, 5)
     return {"payload_gbs": round(gbs, 2), "pcie_frac": round(gbs / PCIE_PEAK_GBS, 4),
             "messages": len(sizes), "ms": round(total, 3), "b_equals_a": ok,
+            "launches": (len(sizes) + 127) // 128,
+            "one_launch_per_message": {"payload_gbs": round(gbs_each, 2),
+                                       "pcie_frac": round(gbs_each / PCIE_PEAK_GBS, 4),
+                                       "ms": round(each, 3)},
             "pinned_copy_d2h_gbs": round((256 << 20) / (d2h * 1e-3) / 1e9, 2),
             "pinned_copy_h2d_gbs": round((256 << 20) / (h2d * 1e-3) / 1e9, 2)}
 

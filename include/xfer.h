@@ -174,6 +174,22 @@ int xfer_run(xfer_conn* c, const void* src, void* dst, size_t nbytes, void* stre
 int xfer_run_batch(xfer_conn* const* conns, const void* const* src, void* const* dst,
                    const size_t* nbytes, int n, void* stream);
 
+/* xfer_run_messages: n messages on one connection, in as few launches as
+ * possible (up to 128 messages per launch).  Message i moves sizes[i] bytes
+ * from src + offsets[i] to dst + offsets[i]; offsets and sizes are host
+ * arrays of n entries.  The result, the counters and the FIFO bytes are
+ * those of n xfer_run calls in order (each message is partitioned and
+ * numbered as its own transfer); the FIFO pipeline simply flows from one
+ * message into the next instead of draining at each launch boundary.
+ * Zero-size messages are skipped; n == 0 queues nothing.
+ * Messages must not overlap one another: channels reach different messages
+ * at different times, so overlapping writes would race.
+ * Errors: INVALID_ARG (NULL arrays, NULL buffers with bytes to move, two
+ * non-empty messages overlapping, the span of the messages overlapping
+ * between src and dst), RANGE, STATE, HIP. */
+int xfer_run_messages(xfer_conn* c, const void* src, void* dst, const size_t* offsets,
+                      const size_t* sizes, int n, void* stream);
+
 /* xfer_run_loop: iters messages of nbytes from src to dst back to back on
  * one connection in one launch (each message is a full transfer; dst holds
  * the last).  Measures per-message cost without launch overhead. */

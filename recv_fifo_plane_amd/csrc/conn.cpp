@@ -3,6 +3,7 @@
 // both endpoints.  Setup = allocate + zero + wire (the transport's
 // Setup/ProxySetup/Connect sequence, "transport建立" section 具体说明);
 // teardown = free.  After setup the host is silent: a run only launches.
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 #include <sys/syscall.h>
@@ -476,6 +477,76 @@ extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nb
 
 extern "C" int xfer_run(xfer_conn* c, const void* src, void* dst, size_t nbytes, void* stream) {
   return xfer_run_loop(c, src, dst, nbytes, 1, stream);
+}
+
+extern "C" int xfer_run_messages(xfer_conn* c, const void* src, void* dst, const size_t* offsets,
+                                 const size_t* sizes, int n, void* stream) {
+  int rc = check_runnable(c, "xfer_run_messages");
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && (!offsets || !sizes)))
+    return fail(XFER_ERR_INVALID_ARG, "xfer_run_messages: need n >= 0 and offset/size arrays");
+  // The span every message lies in, for the NULL and overlap checks.
+  size_t lo = SIZE_MAX, hi = 0;
+  std::vector<MsgDesc> msgs;
+  msgs.reserve(size_t(n));
+  for (int i = 0; i < n; ++i) {
+    if (sizes[i] == 0) continue;
+    if (offsets[i] > SIZE_MAX - sizes[i])
+      return fail(XFER_ERR_INVALID_ARG, "xfer_run_messages: offset + size overflows");
+    lo = std::min(lo, offsets[i]);
+    hi = std::max(hi, offsets[i] + sizes[i]);
+    msgs.push_back(MsgDesc{uint64_t(offsets[i]), uint64_t(sizes[i])});
+  }
+  if (msgs.empty()) return XFER_OK;
+  if (!src || !dst)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_run_messages: NULL src or dst with bytes to move");
+  {
+    // Channels reach different messages at different times, so two messages
+    // that write the same bytes would race; sequential runs would not.
+    std::vector<MsgDesc> by_off(msgs);
+    std::sort(by_off.begin(), by_off.end(),
+              [](const MsgDesc& a, const MsgDesc& b) { return a.off < b.off; });
+    for (size_t i = 1; i < by_off.size(); ++i)
+      if (by_off[i - 1].off + by_off[i - 1].len > by_off[i].off)
+        return fail(XFER_ERR_INVALID_ARG, "xfer_run_messages: two messages overlap");
+  }
+  if (overlap(static_cast<const uint8_t*>(src) + lo, hi - lo, static_cast<uint8_t*>(dst) + lo,
+              hi - lo))
+    return fail(XFER_ERR_INVALID_ARG, "xfer_run_messages: src and dst ranges overlap");
+  std::vector<uint64_t> add(size_t(c->nch), 0), one;
+  bool aligned = aligned16(src) && aligned16(dst);
+  for (const MsgDesc& m : msgs) {
+    rc = plan_steps(c, m.len, 1, one, "xfer_run_messages");
+    if (rc) return rc;
+    for (int ch = 0; ch < c->nch; ++ch) {
+      add[size_t(ch)] += one[size_t(ch)];
+      if (c->proto == XFER_PROTO_LL && c->steps[size_t(ch)] + add[size_t(ch)] > 0xFFFFFFFFull)
+        return fail(XFER_ERR_RANGE, "xfer_run_messages: LL connection would pass 2^32-1 steps");
+    }
+    aligned = aligned && (m.off & 15u) == 0;
+  }
+  DeviceGuard g(c->device);
+  const uint32_t total = wgs_of(c);
+  const Variant v = variant_of(c, aligned);
+  rc = check_resident(v, 0, c->block, total, "xfer_run_messages");
+  if (rc) return rc;
+  RunArgs<1> args;
+  for (size_t first = 0; first < msgs.size(); first += kMaxMsgs) {
+    const size_t cnt = std::min<size_t>(kMaxMsgs, msgs.size() - first);
+    memset(&args, 0, sizeof(args));
+    args.conn[0] = conn_args(c, src, dst, 0, 0);
+    args.nconn = 1;
+    args.iters = 1;
+    args.total_wgs = total;
+    args.xcd_remap = remap_flag(c->xcd_pairing, total);
+    args.timeout_ticks = c->timeout_ticks;
+    args.nmsgs = uint32_t(cnt);
+    for (size_t i = 0; i < cnt; ++i) args.msgs[i] = msgs[first + i];
+    hipError_t e = launch_run1(v, args, c->block, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "xfer_run_messages launch");
+  }
+  commit_steps(c, add);
+  return XFER_OK;
 }
 
 extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, void* const* dst,

@@ -308,14 +308,14 @@ struct Side {
   LaneCtrl* lc;
   uint64_t base;    // step counter at launch start (own counter: tail or head)
   uint64_t seen;    // last observed peer counter (wave-uniform)
-  Range r;
+  Range r;          // the channel's range and steps in the current message
 };
 
 __device__ __forceinline__ Side make_side(const ConnArgs& A, uint32_t c, uint32_t w, bool producer,
                                           int sc) {
   Side s;
   s.lc = A.ctrl + static_cast<uint64_t>(c) * A.lanes + w;
-  s.r = chan_range(A.nbytes, A.nch, c, A.step_bytes);
+  s.r = Range{0, 0, 0};  // set per message
   // A side is the only writer of its own counter, and the previous launch
   // that wrote it has completed, so a plain coherent load reads it.
   const uint64_t* own = producer ? &s.lc->tail : &s.lc->head;
@@ -372,7 +372,7 @@ __device__ __forceinline__ uint32_t wait_credit(const ConnArgs& A, Side& sd, uin
 // pipelined: the source of step j+1 is loaded while the FIFO stores of
 // step j drain, and vmcnt(kUnroll) then covers exactly those stores.
 template <int SC, int ORD>
-__device__ bool simple_send_piped(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
+__device__ bool simple_send_piped(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t g0,
                                   const uint8_t* src, uint64_t ticks, Shared& sh) {
   using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
@@ -380,7 +380,7 @@ __device__ bool simple_send_piped(const ConnArgs& A, uint32_t c, uint32_t w, Sid
   Batch b;
   batch_load<kPolNT, false>(b, src + sd.r.beg, chunk_len(sd, S, 0), S, P, w);
   for (uint64_t j = 0; j < sd.r.k; ++j) {
-    const uint64_t g = sd.base + m * sd.r.k + j;
+    const uint64_t g = g0 + j;
     const uint32_t err = wait_credit<SC, ORD>(A, sd, g, ticks);
     if (!err) {
       const uint32_t L = chunk_len(sd, S, j);
@@ -403,16 +403,16 @@ __device__ bool simple_send_piped(const ConnArgs& A, uint32_t c, uint32_t w, Sid
 // Producer of message m: for each step g, wait for credit g - head < nslots,
 // write the chunk into slot g mod nslots, release, tail = g+1.
 template <int SC, int ORD, bool AL>
-__device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
+__device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t g0,
                             const uint8_t* src, uint64_t ticks, Shared& sh) {
   using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
   if constexpr (ORD == kOrdCoherent) {
     if (lane_blocks<false>(S, A.lanes) <= kUnroll)
-      return simple_send_piped<SC, ORD>(A, c, w, sd, m, src, ticks, sh);
+      return simple_send_piped<SC, ORD>(A, c, w, sd, g0, src, ticks, sh);
   }
   for (uint64_t j = 0; j < sd.r.k; ++j) {
-    const uint64_t g = sd.base + m * sd.r.k + j;
+    const uint64_t g = g0 + j;
     const uint32_t err = wait_credit<SC, ORD>(A, sd, g, ticks);
     if (!err) {
       lane_copy<kPolNT, O::kShared, false>(src + sd.r.beg + j * S, slot_of(A, c, g), chunk_len(sd, S, j),
@@ -428,12 +428,12 @@ __device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
 // Consumer of message m: wait for tail > g, acquire, copy the slot out,
 // head = g+1.
 template <int SC, int ORD, bool AL>
-__device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
+__device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t g0,
                             uint8_t* dst, uint64_t ticks, Shared& sh) {
   using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
   for (uint64_t j = 0; j < sd.r.k; ++j) {
-    const uint64_t g = sd.base + m * sd.r.k + j;
+    const uint64_t g = g0 + j;
     uint32_t err = 0;
     if (sd.seen <= g) {
       Deadline dl(ticks, A.status);
@@ -484,13 +484,13 @@ __device__ __forceinline__ void ll_dst_word(uint8_t* p, uint64_t L, uint64_t lin
 }
 
 template <int SC, int ORD, bool AL>
-__device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
+__device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t g0,
                         const uint8_t* src, uint64_t ticks, Shared& sh) {
   const uint64_t S = A.step_bytes;
   const uint32_t P = A.lanes, nthr = blockDim.x;
   uint32_t err = 0;
   for (uint64_t j = 0; j < sd.r.k && !err; ++j) {
-    const uint64_t g = sd.base + m * sd.r.k + j;
+    const uint64_t g = g0 + j;
     if ((err = wait_credit<SC, ORD>(A, sd, g, ticks))) break;
     const uint32_t L = chunk_len(sd, S, j);
     const uint64_t nl = (L + 3) / 4;
@@ -506,13 +506,13 @@ __device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
 }
 
 template <int SC, int ORD, bool AL>
-__device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
+__device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t g0,
                         uint8_t* dst, uint64_t ticks, Shared& sh) {
   using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
   const uint32_t P = A.lanes, nthr = blockDim.x;
   for (uint64_t j = 0; j < sd.r.k; ++j) {
-    const uint64_t g = sd.base + m * sd.r.k + j;
+    const uint64_t g = g0 + j;
     const uint32_t want = static_cast<uint32_t>(g + 1);
     const uint32_t L = chunk_len(sd, S, j);
     const uint64_t nl = (L + 3) / 4;
@@ -563,8 +563,8 @@ __device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
 
 // LL has no polled tail: the producer records its final step count once.
 template <int SC>
-__device__ __forceinline__ void ll_close(Side& sd, uint64_t iters) {
-  if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, sd.base + iters * sd.r.k);
+__device__ __forceinline__ void ll_close(Side& sd, uint64_t end_step) {
+  if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, end_step);
 }
 
 // --------------------------------------------------------------- zero-copy
@@ -597,7 +597,7 @@ __device__ __forceinline__ uint32_t take_address(const ConnArgs& A, Side& sd, ui
 // pipelined like simple_send_piped (the source does not depend on the
 // address).
 template <int SC, int ORD>
-__device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t m,
+__device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
                               const uint8_t* src, uint64_t ticks, Shared& sh) {
   using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
@@ -605,7 +605,7 @@ __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t 
   Batch b;
   batch_load<kPolNT, true>(b, src + sd.r.beg, chunk_len(sd, S, 0), S, P, w);
   for (uint64_t j = 0; j < sd.r.k; ++j) {
-    const uint64_t g = sd.base + m * sd.r.k + j;
+    const uint64_t g = g0 + j;
     if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh), A.status)) return false;
     uint8_t* p = reinterpret_cast<uint8_t*>(sh.ptr);
     const uint32_t L = chunk_len(sd, S, j);
@@ -626,16 +626,16 @@ __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t 
 // Producer: take the published destination, clear the word, write the chunk
 // straight there, release, tail = g+1.
 template <int SC, int ORD, bool AL>
-__device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t m,
+__device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t g0,
                         const uint8_t* src, uint64_t ticks, Shared& sh) {
   using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
   if constexpr (ORD == kOrdCoherent) {
     if (lane_blocks<true>(S, A.lanes) <= kUnroll)
-      return zc_send_piped<SC, ORD>(A, w, sd, m, src, ticks, sh);
+      return zc_send_piped<SC, ORD>(A, w, sd, g0, src, ticks, sh);
   }
   for (uint64_t j = 0; j < sd.r.k; ++j) {
-    const uint64_t g = sd.base + m * sd.r.k + j;
+    const uint64_t g = g0 + j;
     if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh), A.status)) return false;
     lane_copy<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, reinterpret_cast<uint8_t*>(sh.ptr),
                                   chunk_len(sd, S, j), S, A.lanes, w);
@@ -646,23 +646,72 @@ __device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
   return true;
 }
 
-// Receiver (one thread): publish the destination of the next step whenever
-// the word is clear; complete step g once tail > g by publishing head.
-template <int SC, int ORD>
-__device__ void zc_recv(const ConnArgs& A, Side& sd, uint64_t iters, uint8_t* dst,
+// The launch's messages of one connection, repeated `iters` times.
+template <int MAXB>
+struct MsgList {
+  const MsgDesc* msgs;
+  uint32_t n;
+  uint64_t nbytes;
+  __device__ uint32_t count() const { return n ? n : 1u; }
+  __device__ MsgDesc at(uint32_t i) const { return n ? msgs[i] : MsgDesc{0, nbytes}; }
+};
+
+// Walks the steps of a channel over every message of the launch, in order.
+template <int MAXB>
+struct StepCursor {
+  uint32_t rep, mi;
+  uint64_t j, off;
+  Range r;
+  bool done;
+  __device__ void load(const MsgList<MAXB>& L, const ConnArgs& A, uint32_t c) {
+    const MsgDesc md = L.at(mi);
+    off = md.off;
+    r = chan_range(md.len, A.nch, c, A.step_bytes);
+  }
+  // Positions on the first step at or after (rep, mi, j).
+  __device__ void settle(const MsgList<MAXB>& L, const ConnArgs& A, uint32_t c, uint32_t iters) {
+    while (!done && j >= r.k) {
+      j = 0;
+      if (++mi == L.count()) {
+        mi = 0;
+        if (++rep == iters) {
+          done = true;
+          return;
+        }
+      }
+      load(L, A, c);
+    }
+  }
+};
+
+// Receiver (one thread): publish the destination of the next step (the base
+// of its chunk in B) whenever the word is clear; complete steps once tail
+// passes them by publishing head.
+template <int SC, int ORD, int MAXB>
+__device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<MAXB>& args,
                         uint64_t ticks) {
   using O = Order<SC, ORD>;
   if (threadIdx.x != 0) return;
-  const uint64_t total = iters * sd.r.k, S = A.step_bytes;
-  uint64_t npub = 0, ndone = 0;
+  const MsgList<MAXB> L{args.msgs, args.nmsgs, A.nbytes};
+  const uint64_t S = A.step_bytes;
+  uint64_t per_rep = 0;
+  for (uint32_t i = 0; i < L.count(); ++i) per_rep += chan_range(L.at(i).len, A.nch, c, S).k;
+  const uint64_t total = per_rep * args.iters;
+  StepCursor<MAXB> cur{0, 0, 0, 0, Range{0, 0, 0}, total == 0};
+  if (!cur.done) {
+    cur.load(L, A, c);
+    cur.settle(L, A, c, args.iters);
+  }
+  uint64_t ndone = 0;
   Deadline dl(ticks, A.status);
   while (ndone < total) {
     bool moved = false;
-    if (npub < total && ld_u64<SC>(&sd.lc->ptrx) == 0) {
-      const uint64_t addr = reinterpret_cast<uint64_t>(dst + sd.r.beg + (npub % sd.r.k) * S);
+    if (!cur.done && ld_u64<SC>(&sd.lc->ptrx) == 0) {
+      const uint64_t addr = reinterpret_cast<uint64_t>(A.dst + cur.off + cur.r.beg + cur.j * S);
       O::release();
       st_u64<SC>(&sd.lc->ptrx, addr);
-      ++npub;
+      ++cur.j;
+      cur.settle(L, A, c, args.iters);
       moved = true;
     }
     const uint64_t t = ld_u64<SC>(&sd.lc->tail);
@@ -708,28 +757,35 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
   if (c >= A.nch) return;  // never taken: the host sizes the grid exactly
   if (!((A.roles >> role) & 1u)) return;  // side switched off for fault injection
   Side sd = make_side(A, c, w, role == 0, SC);
-  if (sd.r.k == 0) return;
   const uint64_t ticks = args.timeout_ticks;
   if constexpr (PROTO == kProtoZC) {
     if (role == 1) {
-      zc_recv<SC, ORD>(A, sd, args.iters, A.dst, ticks);
+      zc_recv<SC, ORD, MAXB>(A, c, sd, args, ticks);
       return;
     }
   }
-  for (uint32_t m = 0; m < args.iters; ++m) {
-    bool ok;
-    if constexpr (PROTO == kProtoSimple)
-      ok = role == 0 ? simple_send<SC, ORD, AL>(A, c, w, sd, m, A.src, ticks, sh)
-                     : simple_recv<SC, ORD, AL>(A, c, w, sd, m, A.dst, ticks, sh);
-    else if constexpr (PROTO == kProtoLL)
-      ok = role == 0 ? ll_send<SC, ORD, AL>(A, c, w, sd, m, A.src, ticks, sh)
-                     : ll_recv<SC, ORD, AL>(A, c, w, sd, m, A.dst, ticks, sh);
-    else
-      ok = zc_send<SC, ORD, AL>(A, c, w, sd, m, A.src, ticks, sh);
-    if (!ok) return;
+  const MsgList<MAXB> L{args.msgs, args.nmsgs, A.nbytes};
+  uint64_t g0 = sd.base;
+  for (uint32_t rep = 0; rep < args.iters; ++rep) {
+    for (uint32_t mi = 0; mi < L.count(); ++mi) {
+      const MsgDesc md = L.at(mi);
+      sd.r = chan_range(md.len, A.nch, c, A.step_bytes);
+      if (sd.r.k == 0) continue;
+      bool ok;
+      if constexpr (PROTO == kProtoSimple)
+        ok = role == 0 ? simple_send<SC, ORD, AL>(A, c, w, sd, g0, A.src + md.off, ticks, sh)
+                       : simple_recv<SC, ORD, AL>(A, c, w, sd, g0, A.dst + md.off, ticks, sh);
+      else if constexpr (PROTO == kProtoLL)
+        ok = role == 0 ? ll_send<SC, ORD, AL>(A, c, w, sd, g0, A.src + md.off, ticks, sh)
+                       : ll_recv<SC, ORD, AL>(A, c, w, sd, g0, A.dst + md.off, ticks, sh);
+      else
+        ok = zc_send<SC, ORD, AL>(A, c, w, sd, g0, A.src + md.off, ticks, sh);
+      if (!ok) return;
+      g0 += sd.r.k;
+    }
   }
   if constexpr (PROTO == kProtoLL) {
-    if (role == 0) ll_close<SC>(sd, args.iters);
+    if (role == 0 && g0 != sd.base) ll_close<SC>(sd, g0);
   }
 }
 
@@ -748,32 +804,36 @@ __global__ void __launch_bounds__(1024) ping_kernel(PingArgs args) {
   if (c >= F.nch) return;
   Side fs = make_side(F, c, w, side == 0, SC);
   Side rs = make_side(R, c, w, side == 1, SC);
-  if (fs.r.k == 0) return;
+  fs.r = chan_range(F.nbytes, F.nch, c, F.step_bytes);
+  rs.r = chan_range(R.nbytes, R.nch, c, R.step_bytes);
+  const uint64_t k = fs.r.k;
+  if (k == 0) return;
   const uint64_t ticks = args.timeout_ticks;
   for (uint32_t it = 0; it < args.iters; ++it) {
+    const uint64_t gf = fs.base + it * k, gr = rs.base + it * k;
     bool ok;
     if (side == 0) {
       if constexpr (PROTO == kProtoLL)
-        ok = ll_send<SC, ORD, AL>(F, c, w, fs, it, F.src, ticks, sh) &&
-             ll_recv<SC, ORD, AL>(R, c, w, rs, it, R.dst, ticks, sh);
+        ok = ll_send<SC, ORD, AL>(F, c, w, fs, gf, F.src, ticks, sh) &&
+             ll_recv<SC, ORD, AL>(R, c, w, rs, gr, R.dst, ticks, sh);
       else
-        ok = simple_send<SC, ORD, AL>(F, c, w, fs, it, F.src, ticks, sh) &&
-             simple_recv<SC, ORD, AL>(R, c, w, rs, it, R.dst, ticks, sh);
+        ok = simple_send<SC, ORD, AL>(F, c, w, fs, gf, F.src, ticks, sh) &&
+             simple_recv<SC, ORD, AL>(R, c, w, rs, gr, R.dst, ticks, sh);
     } else {
       if constexpr (PROTO == kProtoLL)
-        ok = ll_recv<SC, ORD, AL>(F, c, w, fs, it, F.dst, ticks, sh) &&
-             ll_send<SC, ORD, AL>(R, c, w, rs, it, R.src, ticks, sh);
+        ok = ll_recv<SC, ORD, AL>(F, c, w, fs, gf, F.dst, ticks, sh) &&
+             ll_send<SC, ORD, AL>(R, c, w, rs, gr, R.src, ticks, sh);
       else
-        ok = simple_recv<SC, ORD, AL>(F, c, w, fs, it, F.dst, ticks, sh) &&
-             simple_send<SC, ORD, AL>(R, c, w, rs, it, R.src, ticks, sh);
+        ok = simple_recv<SC, ORD, AL>(F, c, w, fs, gf, F.dst, ticks, sh) &&
+             simple_send<SC, ORD, AL>(R, c, w, rs, gr, R.src, ticks, sh);
     }
     if (!ok) return;
   }
   if constexpr (PROTO == kProtoLL) {
     if (side == 0)
-      ll_close<SC>(fs, args.iters);
+      ll_close<SC>(fs, fs.base + args.iters * k);
     else
-      ll_close<SC>(rs, args.iters);
+      ll_close<SC>(rs, rs.base + args.iters * k);
   }
 }
 

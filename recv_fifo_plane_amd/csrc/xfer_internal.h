@@ -50,15 +50,30 @@ struct ConnArgs {
   uint32_t pad;
 };
 
+// One message of a launch: bytes [off, off + len) of the connection's src
+// move to the same range of its dst.
+struct MsgDesc {
+  uint64_t off, len;
+};
+constexpr int kMaxMsgs = 128;  // messages carried by one launch's arguments
+
+// A launch runs, for each connection, its message list `iters` times in
+// order (nmsgs == 0: the single message {0, conn.nbytes}).  Every message is
+// partitioned and numbered exactly as a separate run would be; the FIFO
+// pipeline just flows from one message into the next.
 template <int MAXB>
 struct RunArgs {
   ConnArgs conn[MAXB];
   uint32_t nconn;
-  uint32_t iters;        // messages per run (xfer_run_loop), 1 otherwise
+  uint32_t iters;
   uint32_t total_wgs;
   uint32_t xcd_remap;    // 1: logical workgroup = (b % 8) * (G / 8) + b / 8
   uint64_t timeout_ticks;
+  uint32_t nmsgs;        // single-connection launches only
+  uint32_t pad;
+  MsgDesc msgs[kMaxMsgs];
 };
+static_assert(sizeof(RunArgs<16>) <= 4096, "kernel arguments are limited to 4 KiB");
 
 struct PingArgs {
   ConnArgs fwd, rev;     // fwd: a -> b (X sends), rev: b -> c (Y sends)

@@ -88,10 +88,23 @@ def run_pingpong(fwd: X.Conn, rev: X.Conn, a, b, c, nbytes: int, iters: int, str
     X.run_pingpong(fwd, rev, a, b, c, nbytes, iters, stream)
 
 
+def message_offsets(sizes) -> list[int]:
+    offs, off = [], 0
+    for s in sizes:
+        offs.append(off)
+        off += s
+    return offs
+
+
 def run_messages(conn: X.Conn, a, b, sizes, stream=None) -> None:
-    """One transfer per message, at consecutive offsets of a and b."""
+    """One transfer (one launch) per message, at consecutive offsets of a and b."""
     off = 0
     pa, pb = _addr(a), _addr(b)
     for s in sizes:
         conn.run(pa + off, pb + off, s, stream)
         off += s
+
+
+def run_message_list(conn: X.Conn, a, b, sizes, stream=None) -> None:
+    """The same messages through xfer_run_messages (up to 128 per launch)."""
+    conn.run_messages(a, b, message_offsets(sizes), sizes, stream)

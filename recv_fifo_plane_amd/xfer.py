@@ -86,6 +86,8 @@ SIGNATURES = {
     "xfer_run_batch": (C.c_int, [C.POINTER(_vp), C.POINTER(_vp), C.POINTER(_vp),
                                  C.POINTER(C.c_size_t), C.c_int, _vp]),
     "xfer_run_loop": (C.c_int, [_vp, _vp, _vp, C.c_size_t, C.c_int, _vp]),
+    "xfer_run_messages": (C.c_int, [_vp, _vp, _vp, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t),
+                                    C.c_int, _vp]),
     "xfer_run_pingpong": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_size_t, C.c_int, _vp]),
     "xfer_conn_query": (C.c_int, [_vp, C.c_int, C.POINTER(xfer_chan_state)]),
     "xfer_conn_fifo": (C.c_int, [_vp, C.c_int, C.POINTER(_vp), C.POINTER(C.c_size_t)]),
@@ -206,6 +208,13 @@ class Conn:
     def run_loop(self, src, dst, nbytes: int, iters: int, stream=None) -> None:
         check(lib().xfer_run_loop(self._h, _addr(src), _addr(dst), int(nbytes), int(iters),
                                   _stream_handle(stream)))
+
+    def run_messages(self, src, dst, offsets, sizes, stream=None) -> None:
+        n = len(sizes)
+        offs = (C.c_size_t * max(n, 1))(*[int(x) for x in offsets])
+        szs = (C.c_size_t * max(n, 1))(*[int(x) for x in sizes])
+        check(lib().xfer_run_messages(self._h, _addr(src), _addr(dst), offs, szs, n,
+                                      _stream_handle(stream)))
 
     def query(self, channel: int) -> dict:
         st = xfer_chan_state()

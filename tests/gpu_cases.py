@@ -115,3 +115,43 @@ def run_transfers(proto: str, nch: int, nslots: int, slot_bytes: int, sizes, *,
         torch.cuda.synchronize()
         conn.close()
         ocn.close()
+
+
+def run_message_list(proto: str, nch: int, nslots: int, slot_bytes: int, sizes, *,
+                     fifo_loc="device", lanes=1, block=0, base_off=0, kind="uint8", seed=5,
+                     ctrl_loc=0, repeat=1) -> None:
+    """The messages go through xfer_run_messages (consecutive offsets from
+    base_off); the oracle runs them as separate transfers in order.  The
+    whole destination buffer, the counters and the FIFO bytes must match."""
+    import recv_fifo_plane_amd as xf
+    torch = torch_mod()
+    total = int(sum(sizes))
+    what = "messages %s n=%d total=%d nch=%d nslots=%d slot=%d lanes=%d %s" % (
+        proto, len(sizes), total, nch, nslots, slot_bytes, lanes, fifo_loc)
+    log("case: " + what)
+    offs, off = [], base_off
+    for s_ in sizes:
+        offs.append(off)
+        off += s_
+    conn = xf.Conn(proto, nch, nslots, slot_bytes, fifo_loc, wgs_per_channel=lanes,
+                   block_threads=block, ctrl_loc=ctrl_loc)
+    ocn = oracle.Conn(proto, nch, nslots, slot_bytes)
+    try:
+        for r in range(repeat):
+            A = payload(kind, base_off + total + 16, seed + r)
+            dstb = synth.guard_pattern(base_off + total + 2 * GUARD, seed=r)
+            ob = dstb.copy()
+            da = to_dev(A)
+            dd = to_dev(dstb)
+            conn.run_messages(da, dd.data_ptr() + GUARD, offs, sizes)
+            torch.cuda.synchronize()
+            for o, s_ in zip(offs, sizes):
+                ocn.run(np.ascontiguousarray(A[o:o + s_]), ob[GUARD + o:GUARD + o + s_], s_)
+            got = to_host(dd)
+            bad = np.flatnonzero(got != ob)
+            assert bad.size == 0, (what, "repeat", r, describe_mismatch(got, ob, dstb, bad, GUARD))
+        compare_state(conn, ocn, nch, what)
+    finally:
+        torch.cuda.synchronize()
+        conn.close()
+        ocn.close()

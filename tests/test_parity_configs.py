@@ -124,17 +124,21 @@ def test_w4_eight_endpoint_ring():
     ring.close()
 
 
-def test_w5_host_fifo_mixed_messages():
+@pytest.mark.parametrize("one_launch_per_message", [True, False])
+def test_w5_host_fifo_mixed_messages(one_launch_per_message):
     torch = _torch()
     cfg = W.W5
-    log("case: W5 " + str({k: v for k, v in cfg.items()}))
+    log("case: W5 launch per message=%s %s" % (one_launch_per_message, cfg))
     sizes = synth.log_uniform_message_sizes(cfg["total_bytes"], synth.workload_seed(5))
     A = synth.uint8_uniform(cfg["total_bytes"], synth.workload_seed(5))
     conn = W.make_conn(cfg)
     ocn = oracle.Conn("simple", 16, 8, 256 << 10)
     a = to_dev(A)
     b = torch.zeros_like(a)
-    W.run_messages(conn, a, b, sizes)
+    if one_launch_per_message:
+        W.run_messages(conn, a, b, sizes)
+    else:
+        W.run_message_list(conn, a, b, sizes)
     torch.cuda.synchronize()
     B = np.zeros_like(A)
     off = 0
