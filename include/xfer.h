@@ -92,9 +92,11 @@ typedef struct {
   int block_threads;    /* threads per workgroup, a multiple of 64 in 64..1024; default 256 */
   int ctrl_loc;         /* xfer_ctrl_loc */
   uint32_t timeout_ms;  /* bound on every in-kernel wait; default 10000 */
-  int xcd_pairing;      /* 1: place each producer/consumer pair on one XCD; 0 (default) or -1:
-                           dispatch order (a channel's sides spread over the XCDs, measured
-                           faster for bandwidth) */
+  int xcd_pairing;      /* 0 (default) or 1: place each producer/consumer pair on one XCD,
+                           an XCD's producers dispatched before its consumers (applied when
+                           the grid is a multiple of 16 workgroups); -1: dispatch order
+                           (producers on even block ids, which the hardware deals to XCDs
+                           0, 2, 4 and 6 only) */
   int roles;            /* fault injection: 0 = both sides (default), 1 = producer only,
                            2 = consumer/receiver only; a lone side ends its waits with
                            XFER_ERR_TIMEOUT (or XFER_ERR_ABORTED after xfer_conn_abort) */

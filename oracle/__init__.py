@@ -24,6 +24,12 @@ PROTO_NAMES = {"simple": SIMPLE, "ll": LL, "zc": ZC, "zerocopy": ZC}
 
 OP_RECV_SETUP, OP_SEND_SETUP, OP_CONNECT_BATCH = 0, 1, 2
 
+# Producer program orders: the pages' order, and the kernels' where it differs.
+ORDER = {
+    "pages": 0,
+    "zc_take_ahead": 1,  # ZC: take step g+1's address after writing step g, before tail = g+1
+}
+
 MUT = {
     "none": 0,
     "weak_credit": 1,
@@ -33,6 +39,7 @@ MUT = {
     "zc_no_wait": 5,
     "zc_no_reset": 6,
     "early_head": 7,
+    "zc_ahead_past_end": 8,
 }
 VIOLATIONS = {
     0: "ok",
@@ -94,13 +101,15 @@ def lib():
             L.orc_conn_new.restype = vp
             L.orc_conn_free.argtypes = [vp]
             L.orc_conn_set_mutation.argtypes = [vp, C.c_int]
+            L.orc_conn_set_order.argtypes = [vp, C.c_int]
             L.orc_run.argtypes = [vp, vp, vp, C.c_uint64]
             L.orc_run_pingpong.argtypes = [vp, vp, vp, vp, vp, C.c_uint64, C.c_int]
             L.orc_conn_state.argtypes = [vp, C.c_int, u64p]
             L.orc_conn_fifo.argtypes = [vp, C.c_int, u64p]
             L.orc_conn_fifo.restype = vp
             L.orc_enumerate.argtypes = [C.c_int, C.c_int, C.c_int, C.c_uint64, vp, C.c_uint64,
-                                        C.c_int, C.c_int, C.c_uint64, C.POINTER(_EnumResult)]
+                                        C.c_int, C.c_int, C.c_int, C.c_uint64,
+                                        C.POINTER(_EnumResult)]
             _lib = L
     return _lib
 
@@ -195,6 +204,9 @@ class Conn:
     def set_mutation(self, name: str) -> None:
         lib().orc_conn_set_mutation(self._h, MUT[name])
 
+    def set_order(self, name: str) -> None:
+        lib().orc_conn_set_order(self._h, ORDER[name])
+
     def run(self, A: np.ndarray, B: np.ndarray, nbytes: int | None = None) -> None:
         """Transfer A[:n] into B[:n] (both uint8 arrays, modified in place)."""
         n = A.size if nbytes is None else int(nbytes)
@@ -223,12 +235,12 @@ def run_pingpong(fwd: Conn, rev: Conn, a: np.ndarray, b: np.ndarray, c: np.ndarr
 
 def enumerate_interleavings(proto, nchannels: int, nslots: int, slot_bytes: int, A: np.ndarray,
                             mutation: str = "none", prior_runs: int = 0,
-                            max_states: int = 2_000_000) -> dict:
+                            max_states: int = 2_000_000, order: str = "pages") -> dict:
     """Every interleaving of one transfer of A; returns counts and the first violation."""
     A = np.ascontiguousarray(A, dtype=np.uint8)
     res = _EnumResult()
     rc = lib().orc_enumerate(_proto(proto), nchannels, nslots, slot_bytes, _ptr(A), A.size,
-                             MUT[mutation], prior_runs, max_states, C.byref(res))
+                             MUT[mutation], ORDER[order], prior_runs, max_states, C.byref(res))
     if rc != 0:
         raise OracleError("orc_enumerate error %d" % rc)
     return {

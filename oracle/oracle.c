@@ -148,7 +148,7 @@ typedef struct {
 } orc_ctrl;
 
 struct orc_conn {
-  int proto, nch, nslots, mutation;
+  int proto, nch, nslots, mutation, order;
   uint64_t slot_bytes, step_bytes;
   uint8_t* fifo; /* nch * nslots * slot_bytes, zero at creation; none for zero-copy */
   orc_ctrl* ctrl;
@@ -181,6 +181,10 @@ void orc_conn_free(orc_conn* c) {
   free(c);
 }
 
+void orc_conn_set_order(orc_conn* c, int order) {
+  if (c) c->order = order;
+}
+
 void orc_conn_set_mutation(orc_conn* c, int mutation) {
   if (c) c->mutation = mutation;
 }
@@ -210,6 +214,7 @@ const uint8_t* orc_conn_fifo(const orc_conn* c, int ch, uint64_t* bytes) {
 typedef struct {
   uint64_t beg, len, k; /* channel range and its number of steps */
   uint64_t pj, pline, pptr;
+  uint64_t pnext; /* ZC take-ahead: address taken for step pj+1, 0 if none */
   uint32_t pphase, pfinal;
   uint64_t cj, cline, cnpub;
   uint32_t cphase, pad;
@@ -325,6 +330,13 @@ static uint32_t get32(const uint8_t* p) {
 /* ------------------------------------------------------------------ actors */
 enum { ACT_PROD = 0, ACT_CONS = 1, ACT_PUB = 2, N_ACT = 3 };
 
+/* Whether the ZC producer, having written step pj, takes step pj+1's
+ * address before it publishes tail (the kernels' pipelined order). */
+static int zc_takes_ahead(const orc_conn* c, const orc_cur* u) {
+  if (c->order != ORC_ORDER_ZC_TAKE_AHEAD) return 0;
+  return u->pj + 1 < u->k || c->mutation == ORC_MUT_ZC_AHEAD_PAST_END;
+}
+
 static int prod_enabled(const world* w, int ch) {
   const orc_conn* c = w->cfg;
   const orc_ctrl* q = &W_ctrl(w)[ch];
@@ -336,8 +348,11 @@ static int prod_enabled(const world* w, int ch) {
     case ORC_LL:
       if (u->pj == u->k) return !u->pfinal;
       return u->pline > 0 || u->pphase != 0 || credit_ok(w, q, g);
-    default: /* ORC_ZC: the first action of a step needs a published address */
-      return u->pj < u->k && (u->pphase != 0 || q->ptrx != 0);
+    default: /* ORC_ZC: taking an address needs a published one */
+      if (u->pj >= u->k) return 0;
+      if (u->pphase == 0) return u->pnext != 0 || q->ptrx != 0;
+      if (u->pphase == 2 && zc_takes_ahead(c, u)) return q->ptrx != 0;
+      return 1;
   }
 }
 
@@ -533,21 +548,35 @@ static int ll_cons(world* w, int ch, uint64_t budget) {
 }
 
 /* Zero-copy producer (Reading R7): take the published address, clear the
- * word, write the chunk straight into B there, publish tail = g+1. */
+ * word, write the chunk straight into B there, publish tail = g+1.  In the
+ * take-ahead order the producer takes step g+1's address between writing
+ * step g and publishing its tail (phase 2), and step g+1 then starts from
+ * that address instead of the word. */
+static uint64_t zc_take(const orc_conn* c, orc_ctrl* q) {
+  uint64_t p = q->ptrx;
+  if (c->mutation != ORC_MUT_ZC_NO_RESET) q->ptrx = 0;
+  return p;
+}
+
 static int zc_prod(world* w, int ch) {
   const orc_conn* c = w->cfg;
   orc_ctrl* q = &W_ctrl(w)[ch];
   orc_cur* u = &W_cur(w)[ch];
   uint64_t g = q->base + u->pj, off = u->beg + u->pj * c->step_bytes;
   if (u->pphase == 0) {
-    uint64_t p = q->ptrx;
-    if (c->mutation != ORC_MUT_ZC_NO_RESET) q->ptrx = 0;
+    uint64_t p = u->pnext ? u->pnext : zc_take(c, q);
+    u->pnext = 0;
     if (p != off + 1) return ORC_V_WRONG_PTR;
     u->pptr = p;
     u->pphase = 1;
   } else if (u->pphase == 1) {
     memcpy(w->B + (u->pptr - 1), w->A + off, (size_t)chunk_len(w, u, u->pj));
     u->pphase = 2;
+  } else if (u->pphase == 2 && zc_takes_ahead(c, u)) {
+    uint64_t p = zc_take(c, q);
+    if (p != off + c->step_bytes + 1) return ORC_V_WRONG_PTR;
+    u->pnext = p;
+    u->pphase = 3;
   } else {
     q->tail = g + 1;
     u->pphase = 0;
@@ -790,8 +819,10 @@ static int bs_push(blobstack* s, uint8_t* b) {
 static uint8_t guard_byte(uint64_t i) { return (uint8_t)(i * 151u + 89u); }
 
 int orc_enumerate(int proto, int nch, int nslots, uint64_t slot_bytes, const uint8_t* A, uint64_t n,
-                  int mutation, int prior_runs, uint64_t max_states, orc_enum_result* out) {
+                  int mutation, int order, int prior_runs, uint64_t max_states,
+                  orc_enum_result* out) {
   if (!out || (n && !A) || prior_runs < 0) return ORC_E_ARG;
+  if (order != ORC_ORDER_PAGES && order != ORC_ORDER_ZC_TAKE_AHEAD) return ORC_E_ARG;
   memset(out, 0, sizeof(*out));
   out->channel = -1;
   orc_conn* c = orc_conn_new(proto, nch, nslots, slot_bytes);
@@ -811,6 +842,7 @@ int orc_enumerate(int proto, int nch, int nslots, uint64_t slot_bytes, const uin
     }
   }
   c->mutation = mutation;
+  c->order = order;
 
   uint64_t mb = meta_size(c), fb = fifo_size(c), bb = n + 2 * GUARD, blob = mb + fb + bb;
   world w;

@@ -62,6 +62,15 @@ extern "C" {
 #define ORC_MUT_ZC_NO_WAIT 5  /* ZC: receiver publishes without waiting for ptrExchange == 0 */
 #define ORC_MUT_ZC_NO_RESET 6 /* ZC: producer does not clear ptrExchange after reading it */
 #define ORC_MUT_EARLY_HEAD 7  /* SIMPLE/LL: consumer frees the slot (head) before reading it */
+#define ORC_MUT_ZC_AHEAD_PAST_END 8 /* ZC take-ahead order: also waits for an address after the
+                                       transfer's last step */
+
+/* producer program orders: the pages' order, and the orders the GPU kernels
+ * use where they differ from it (each must stay safe and confluent) */
+#define ORC_ORDER_PAGES 0
+#define ORC_ORDER_ZC_TAKE_AHEAD 1 /* ZC: the producer takes step g+1's address, when g+1 is a step
+                                     of the same transfer, after writing step g and before it
+                                     publishes tail = g+1 */
 
 /* setup-plan op kinds */
 #define ORC_OP_RECV_SETUP 0
@@ -84,6 +93,7 @@ typedef struct orc_conn orc_conn;
 orc_conn* orc_conn_new(int proto, int nchannels, int nslots, uint64_t slot_bytes);
 void orc_conn_free(orc_conn* c);
 void orc_conn_set_mutation(orc_conn* c, int mutation);
+void orc_conn_set_order(orc_conn* c, int order);
 /* one transfer A[0:n] -> B[0:n] through the FIFO; 0, a violation code, or an error */
 int orc_run(orc_conn* c, const uint8_t* A, uint8_t* B, uint64_t n);
 /* iters round trips: a -> b on fwd, then b -> c on rev, each as one transfer */
@@ -105,9 +115,10 @@ typedef struct {
 
 /* Enumerates every interleaving of the producer and consumer actions of one
  * transfer of A[0:n] on a fresh connection, after prior_runs deterministic
- * transfers of the same bytes (so a nonzero step base is covered). */
+ * transfers of the same bytes (so a nonzero step base is covered), with the
+ * producer in program order `order`. */
 int orc_enumerate(int proto, int nchannels, int nslots, uint64_t slot_bytes, const uint8_t* A,
-                  uint64_t n, int mutation, int prior_runs, uint64_t max_states,
+                  uint64_t n, int mutation, int order, int prior_runs, uint64_t max_states,
                   orc_enum_result* out);
 
 #ifdef __cplusplus

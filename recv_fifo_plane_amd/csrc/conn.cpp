@@ -198,9 +198,9 @@ ConnArgs conn_args(const xfer_conn* c, const void* src, void* dst, uint64_t nbyt
 
 uint32_t wgs_of(const xfer_conn* c) { return uint32_t(c->nch) * uint32_t(c->lanes) * 2u; }
 
-// Keep a pair (producer 2q, consumer 2q+1) on one XCD: workgroups are
-// dispatched round-robin over the 8 XCDs, so logical id (b % 8) * (G/8) + b/8
-// puts G/8 consecutive logical ids on XCD b % 8.
+// Keep a pair (producer 2q, consumer 2q+1) on one XCD, producers first in
+// each XCD's dispatch order (the kernel's logical_wg); needs a grid of a
+// multiple of 16 workgroups, otherwise dispatch order is kept.
 uint32_t remap_flag(int pairing, uint32_t total) {
   return pairing && total % 16u == 0 ? 1u : 0u;
 }
@@ -314,7 +314,10 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
                     : a.ctrl_loc;
   c->lanes = lanes;
   c->block = block;
-  c->xcd_pairing = a.xcd_pairing == 1 ? 1 : 0;
+  // Pairing by default: in dispatch order producers sit at even block ids,
+  // which the hardware deals to XCDs 0, 2, 4 and 6 only; for zero-copy,
+  // whose receivers are nearly idle, half the XCDs would do all the copying.
+  c->xcd_pairing = a.xcd_pairing == -1 ? 0 : 1;
   c->roles = a.roles == 0 ? 3 : a.roles;
   c->ordering = a.ordering;
   c->slot_bytes = slot_bytes;

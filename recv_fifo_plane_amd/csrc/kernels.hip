@@ -328,7 +328,7 @@ __device__ __forceinline__ Side make_side(const ConnArgs& A, uint32_t c, uint32_
 struct Shared {
   uint32_t err;
   uint32_t pad;
-  uint64_t ptr;
+  uint64_t ptr[2];  // zero-copy destinations, indexed by step parity
 };
 
 __device__ __forceinline__ bool wg_failed(Shared& sh, uint32_t local_err, Status* st) {
@@ -570,10 +570,10 @@ __device__ __forceinline__ void ll_close(Side& sd, uint64_t end_step) {
 // --------------------------------------------------------------- zero-copy
 // Wave 0 waits for a published destination (the base of the step's chunk in
 // B), takes it and clears the word; the address reaches the other waves
-// through LDS after the caller's barrier.
+// through LDS (`out`) after the caller's barrier.
 template <int SC, int ORD>
 __device__ __forceinline__ uint32_t take_address(const ConnArgs& A, Side& sd, uint64_t ticks,
-                                                 Shared& sh) {
+                                                 uint64_t& out) {
   uint32_t err = 0;
   if (threadIdx.x < 64) {
     Deadline dl(ticks, A.status);
@@ -587,7 +587,7 @@ __device__ __forceinline__ uint32_t take_address(const ConnArgs& A, Side& sd, ui
         Order<SC, ORD>::acquire();
         st_u64<SC>(&sd.lc->ptrx, 0);
       }
-      sh.ptr = p;
+      out = p;
     }
   }
   return err;
@@ -595,7 +595,11 @@ __device__ __forceinline__ uint32_t take_address(const ConnArgs& A, Side& sd, ui
 
 // Coherent zero-copy producer whose share fits one register batch,
 // pipelined like simple_send_piped (the source does not depend on the
-// address).
+// address).  The receiver publishes step j+1's destination as soon as it
+// sees step j's taken, so wave 0 takes it while step j's stores drain
+// instead of after step j's tail: two LDS words, by step parity, keep the
+// other waves' read of step j's address clear of that write (the barrier
+// of step j separates the read of a word from its next write).
 template <int SC, int ORD>
 __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
                               const uint8_t* src, uint64_t ticks, Shared& sh) {
@@ -604,20 +608,22 @@ __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t 
   const uint32_t P = A.lanes;
   Batch b;
   batch_load<kPolNT, true>(b, src + sd.r.beg, chunk_len(sd, S, 0), S, P, w);
+  if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh.ptr[0]), A.status)) return false;
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
-    if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh), A.status)) return false;
-    uint8_t* p = reinterpret_cast<uint8_t*>(sh.ptr);
+    uint8_t* p = reinterpret_cast<uint8_t*>(sh.ptr[j & 1]);
     const uint32_t L = chunk_len(sd, S, j);
     batch_store<O::kShared, true>(b, p, L, S, P, w);
     lane_tail<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, p, L, S, P, w);
+    uint32_t err = 0;
     if (j + 1 < sd.r.k) {
       batch_load<kPolNT, true>(b, src + sd.r.beg + (j + 1) * S, chunk_len(sd, S, j + 1), S, P, w);
+      err = take_address<SC, ORD>(A, sd, ticks, sh.ptr[(j + 1) & 1]);
       wait_vmcnt<kUnroll>();
     } else {
       wait_vmcnt<0>();
     }
-    if (wg_failed(sh, 0, A.status)) return false;
+    if (wg_failed(sh, err, A.status)) return false;
     if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
   }
   return true;
@@ -636,8 +642,8 @@ __device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
   }
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
-    if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh), A.status)) return false;
-    lane_copy<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, reinterpret_cast<uint8_t*>(sh.ptr),
+    if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh.ptr[0]), A.status)) return false;
+    lane_copy<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, reinterpret_cast<uint8_t*>(sh.ptr[0]),
                                   chunk_len(sd, S, j), S, A.lanes, w);
     O::release();
     if (wg_failed(sh, 0, A.status)) return false;
@@ -735,9 +741,17 @@ __device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<M
 }
 
 // ------------------------------------------------------------------ kernels
+// Logical workgroup of this block.  Blocks are dealt round-robin to the 8
+// XCDs, so block b runs on XCD b % 8 as that XCD's (b / 8)-th block.  With
+// the remap (total a multiple of 16) XCD x serves the total/16 consecutive
+// pairs starting at x * total/16: its first total/16 blocks are their
+// producers, the rest their consumers.  A pair then shares one XCD, and
+// producers spread evenly over the XCDs and over each XCD's dispatch order.
 __device__ __forceinline__ uint32_t logical_wg(uint32_t remap, uint32_t total) {
   const uint32_t b = blockIdx.x;
-  return remap ? (b % 8u) * (total / 8u) + b / 8u : b;
+  if (!remap) return b;
+  const uint32_t half = total / 16u, s = b / 8u;
+  return 2u * ((b % 8u) * half + s % half) + s / half;
 }
 
 template <int PROTO, int SC, int ORD, bool AL, int MAXB>

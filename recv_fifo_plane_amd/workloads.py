@@ -25,15 +25,15 @@ W2_SIZES = [8 << i for i in range(14)]  # 8 B .. 64 KiB
 W3 = dict(name="simple_32ch_1GiB", proto="simple", nchannels=32, nslots=8, slot_bytes=512 << 10,
           fifo_loc="device", wgs_per_channel=4, block_threads=512, nbytes=1 << 30)
 
-W4_PAIR = dict(name="zc_pair_128MiB", proto="zc", nchannels=8, nslots=1, slot_bytes=512 << 10,
+W4_PAIR = dict(name="zc_pair_128MiB", proto="zc", nchannels=32, nslots=1, slot_bytes=512 << 10,
                fifo_loc="device", wgs_per_channel=16, block_threads=128, nbytes=128 << 20)
 
 W4_RING = dict(name="zc_ring_8x128MiB", proto="zc", endpoints=8, channels_per_edge=4,
-               nslots=1, slot_bytes=512 << 10, fifo_loc="device", wgs_per_channel=16,
-               block_threads=128, slice_bytes=128 << 20, max_peers=128)
+               nslots=1, slot_bytes=512 << 10, fifo_loc="device", wgs_per_channel=4,
+               block_threads=512, slice_bytes=128 << 20, max_peers=128)
 
 W5 = dict(name="host_fifo_16ch_2GiB", proto="simple", nchannels=16, nslots=8,
-          slot_bytes=256 << 10, fifo_loc="host", wgs_per_channel=16, block_threads=256,
+          slot_bytes=256 << 10, fifo_loc="host", wgs_per_channel=8, block_threads=512,
           ctrl_loc=1, total_bytes=2 << 30)
 
 _ATTRS = ("wgs_per_channel", "block_threads", "ctrl_loc", "timeout_ms", "xcd_pairing", "ordering")

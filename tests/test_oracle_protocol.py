@@ -271,6 +271,50 @@ def test_correct_protocol_is_clean_under_the_same_inputs_as_the_mutations():
             assert r["violation"] == "ok" and r["terminals"] == 1
 
 
+# The zero-copy kernels take step g+1's address while step g's stores drain,
+# before tail = g+1: a producer program order the pages do not print.  It
+# must be as safe and confluent as theirs, end in the same state, and the
+# enumerator must still catch the broken rules under it.
+@pytest.mark.parametrize("nch,nslots", [(1, 1), (1, 2), (2, 1), (2, 3)])
+def test_zc_take_ahead_order_is_safe_and_confluent(nch, nslots):
+    S = 16
+    max_steps = 6 if nch == 1 else 3
+    for n in sorted({1, S - 1, S, S + 1, 2 * S, max_steps * S * nch - 3, max_steps * S * nch}):
+        A = synth.uint8_uniform(n, 3000 + n)
+        for prior in (0, 1):
+            pages = oracle.enumerate_interleavings("zc", nch, nslots, S, A, prior_runs=prior)
+            ahead = oracle.enumerate_interleavings("zc", nch, nslots, S, A, prior_runs=prior,
+                                                   order="zc_take_ahead")
+            assert ahead["violation"] == "ok" and ahead["terminals"] == 1, (n, prior, ahead)
+            assert pages["violation"] == "ok"
+
+
+def test_zc_take_ahead_ends_in_the_pages_state():
+    for n in (0, 5, 16, 100, 1000):
+        A = synth.uint8_uniform(n, 4000 + n)
+        ends = []
+        for order in ("pages", "zc_take_ahead"):
+            c = oracle.Conn("zc", 3, 1, 32)
+            c.set_order(order)
+            B = np.zeros(n, dtype=np.uint8)
+            for _ in range(2):
+                c.run(A, B)
+            ends.append((B.tobytes(), [sorted(c.state(ch).items()) for ch in range(3)]))
+            c.close()
+        assert ends[0] == ends[1]
+        assert ends[1][0] == A.tobytes()
+
+
+@pytest.mark.parametrize("mutation,expected", [("zc_no_wait", {"wrong_ptr"}),
+                                               ("zc_no_reset", {"wrong_ptr", "counters"}),
+                                               ("zc_ahead_past_end", {"deadlock"})])
+def test_enumerator_catches_broken_rules_under_take_ahead(mutation, expected):
+    A = synth.uint8_uniform(4 * 16 + 3, 77)
+    r = oracle.enumerate_interleavings("zc", 1, 1, 16, A, mutation=mutation,
+                                       order="zc_take_ahead")
+    assert r["violation"] in expected, r
+
+
 def test_conn_rejects_bad_shapes():
     for args in [("simple", 0, 8, 16), ("simple", 65, 8, 16), ("simple", 1, 0, 16),
                  ("simple", 1, 8, 24), ("ll", 1, 8, 12), ("zc", 1, 8, 8)]:
