@@ -133,9 +133,23 @@ def bench_w1(torch, T, W, synth):
     ok = bool(torch.equal(a, b))
     conn.close()
     gbs = n / (per * 1e-3) / 1e9
+    # Ceiling of one workgroup copying A -> B straight (zero-copy, one channel,
+    # one 4 MiB step: a single address hand-off, then a plain copy).
+    zc = W.make_conn(dict(cfg, proto="zc", nslots=1, slot_bytes=n))
+    b.zero_()
+    _, per_zc = T.time_launches(lambda: zc.run(a, b, n, T.stream), 5, 100)
+    check_no_error(zc, 1, "W1 single-workgroup copy")
+    ok = ok and bool(torch.equal(a, b))
+    zc.close()
+    wg = n / (per_zc * 1e-3) / 1e9
     return {"payload_gbs": round(gbs, 2), "real_gbs": round(4 * gbs, 2),
             "hbm_frac": round(4 * gbs / HBM_PEAK_GBS, 4), "kernel_us": round(per * 1e3, 2),
-            "b_equals_a": ok, "note": "one producer/consumer workgroup pair"}
+            "b_equals_a": ok, "note": "one producer/consumer workgroup pair",
+            "single_wg_copy_ceiling": {
+                "payload_gbs": round(wg, 2), "kernel_us": round(per_zc * 1e3, 2),
+                "vs_ceiling": round(gbs / wg, 3),
+                "note": "one %d-thread workgroup copying the 4 MiB straight into B; each side of "
+                        "the FIFO pair is one such copy" % cfg["block_threads"]}}
 
 
 def bench_w2(torch, T, W, synth):
@@ -162,6 +176,26 @@ def bench_w2(torch, T, W, synth):
     big = out[str(W.W2_SIZES[-1])]
     big["real_gbs_6x"] = round(6 * big["payload_gbs"], 2)
     big["hbm_frac_6x"] = round(6 * big["payload_gbs"] / HBM_PEAK_GBS, 4)
+    # Secondary: messages back to back on one connection in one launch (the
+    # pipeline never drains), and one host-issued launch per message.
+    sec = {}
+    for size in (8, 1024, 65536):
+        A = synth.int32_uniform_bytes(size, synth.workload_seed(2) + size)
+        a = torch.from_numpy(A).to("cuda")
+        b = torch.zeros_like(a)
+        conn = W.make_conn(cfg)
+        _, per_loop = T.time_launches(lambda: conn.run_loop(a, b, size, iters, T.stream), 1, 3)
+        ok = bool(torch.equal(a, b))
+        b.zero_()
+        nrun = 1000
+        _, per_runs = T.time_launches(
+            lambda: [conn.run(a, b, size, T.stream) for _ in range(nrun)], 1, 3)
+        check_no_error(conn, 1, "W2 secondary")
+        ok = ok and bool(torch.equal(a, b))
+        conn.close()
+        sec[str(size)] = {"in_launch_us_per_msg": round(per_loop * 1e3 / iters, 3),
+                          "host_issued_us_per_msg": round(per_runs * 1e3 / nrun, 3), "ok": ok}
+    out["serialized_one_connection"] = sec
     return out
 
 
@@ -241,25 +275,60 @@ def plain_copy_ceiling(torch, T) -> dict:
     return {"bytes": n, "ms": round(per, 4), "real_gbs": round(2 * n / (per * 1e-3) / 1e9, 1)}
 
 
-def cpu_baseline(A, budget_s: float = 10.0) -> dict:
-    """The oracle as it is (single-threaded C), on the same 1 GiB input."""
+def _cpu_threads() -> int:
+    """Host threads the threaded oracle may use: the CPUs this process may run
+    on, capped at 16 (the host share of one GPU) and at 2 x 32 channels."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n, 64))
+
+
+def cpu_baseline(A, budget_s: float = 8.0) -> dict:
+    """The oracle as it is, on the same 1 GiB input: its threaded mode (one
+    producer and one consumer actor per channel on the host's cores) is the
+    value; the single-threaded sequential simulation and a two-thread LL
+    ping-pong latency are reported beside it."""
     import numpy as np
 
     import oracle
     B = np.empty_like(A)
-    runs, t0 = 0, time.perf_counter()
-    while True:
-        conn = oracle.Conn("simple", 32, 8, 512 << 10)
-        conn.run(A, B)
-        conn.close()
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or runs >= 20:
-            break
-    gbs = runs * A.size / el / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+
+    def timed(run):
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            conn = oracle.Conn("simple", 32, 8, 512 << 10)
+            run(conn)
+            conn.close()
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or runs >= 20:
+                return runs, el
+
+    threads = _cpu_threads()
+    runs_t, el_t = timed(lambda c: c.run_threaded(A, B, threads))
+    runs_s, el_s = timed(lambda c: c.run(A, B))
+    lat = {}
+    for size in (8, 1024, 65536):
+        a = np.ascontiguousarray(A[:size])
+        b, c = np.zeros(size, np.uint8), np.zeros(size, np.uint8)
+        f, r = oracle.Conn("ll", 1, 8, 32 << 10), oracle.Conn("ll", 1, 8, 32 << 10)
+        iters = 10000 if size <= 1024 else 2000
+        sec = oracle.pingpong_threaded(f, r, a, b, c, size, iters)
+        f.close()
+        r.close()
+        lat[str(size)] = round(sec * 1e6 / (2 * iters), 3)
+    return {"value": round(runs_t * A.size / el_t / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
             "sample": "%d full transfers of the 1 GiB bf16 input through 32 channels x 8 x 512 KiB "
-                      "(deterministic single-threaded simulation, %.1f s)" % (runs, el)}
+                      "in the oracle's threaded mode (64 actors on %d threads, %.1f s)"
+                      % (runs_t, threads, el_t),
+            "single_thread": {"value": round(runs_s * A.size / el_s / 1e9, 3), "unit": "GB/s",
+                              "cores": 1, "sample": "%d transfers, sequential simulation, %.1f s"
+                                                    % (runs_s, el_s)},
+            "ll_pingpong_one_way_us": lat,
+            "ll_pingpong_note": "two host threads on two cores, LL 1 channel x 8 x 32 KiB"}
 
 
 def main() -> int:

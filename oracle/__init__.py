@@ -1,9 +1,9 @@
 """CPU oracle of the FIFO send/recv data plane (test infrastructure only).
 
 Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
-leg may import this package.  It wraps ``oracle.c`` (plain C, built with gcc
-into ``liboracle.so`` next to it) through ctypes and shares no code with the
-GPU library.  See the header comment of ``oracle.c`` for what is modelled and
+leg may import this package.  It wraps ``oracle.c`` and ``threaded.c`` (plain
+C, built with gcc into ``liboracle.so`` next to them) through ctypes and shares
+no code with the GPU library.  See the header comment of ``oracle.c`` for what is modelled and
 for every reading taken where the pages are silent.
 """
 from __future__ import annotations
@@ -16,7 +16,8 @@ import threading
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "oracle.c")
+SRCS = [os.path.join(HERE, f) for f in ("oracle.c", "threaded.c", "oracle.h",
+                                        "oracle_internal.h")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 SIMPLE, LL, ZC = 0, 1, 2
@@ -59,12 +60,17 @@ _lock = threading.Lock()
 _lib = None
 
 
+def _stale() -> bool:
+    return not os.path.exists(LIB) or os.path.getmtime(LIB) < max(map(os.path.getmtime, SRCS))
+
+
 def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc."""
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+    """Compile the oracle's C sources into liboracle.so with gcc."""
+    if not force and not _stale():
         return LIB
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-o", tmp, SRC]
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-o", tmp,
+           *[f for f in SRCS if f.endswith(".c")], "-lpthread"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB
@@ -85,7 +91,7 @@ def lib():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            if _stale():
                 build()
             L = C.CDLL(LIB)
             u64p = C.POINTER(C.c_uint64)
@@ -104,6 +110,9 @@ def lib():
             L.orc_conn_set_order.argtypes = [vp, C.c_int]
             L.orc_run.argtypes = [vp, vp, vp, C.c_uint64]
             L.orc_run_pingpong.argtypes = [vp, vp, vp, vp, vp, C.c_uint64, C.c_int]
+            L.orc_run_threaded.argtypes = [vp, vp, vp, C.c_uint64, C.c_int]
+            L.orc_pingpong_threaded.argtypes = [vp, vp, vp, vp, vp, C.c_uint64, C.c_int,
+                                                C.POINTER(C.c_double)]
             L.orc_conn_state.argtypes = [vp, C.c_int, u64p]
             L.orc_conn_fifo.argtypes = [vp, C.c_int, u64p]
             L.orc_conn_fifo.restype = vp
@@ -214,6 +223,16 @@ class Conn:
         assert A.flags.c_contiguous and B.flags.c_contiguous
         _check(lib().orc_run(self._h, _ptr(A), _ptr(B), n), "orc_run")
 
+    def run_threaded(self, A: np.ndarray, B: np.ndarray, nthreads: int,
+                     nbytes: int | None = None) -> None:
+        """The same transfer in the threaded mode: every channel's producer and
+        consumer as actors on `nthreads` threads (clamped to 2 x channels)."""
+        n = A.size if nbytes is None else int(nbytes)
+        assert A.dtype == np.uint8 and B.dtype == np.uint8 and A.size >= n and B.size >= n
+        assert A.flags.c_contiguous and B.flags.c_contiguous
+        _check(lib().orc_run_threaded(self._h, _ptr(A), _ptr(B), n, int(nthreads)),
+               "orc_run_threaded")
+
     def state(self, channel: int) -> dict:
         out = (C.c_uint64 * 4)()
         _check(lib().orc_conn_state(self._h, channel, out), "orc_conn_state")
@@ -232,6 +251,18 @@ def run_pingpong(fwd: Conn, rev: Conn, a: np.ndarray, b: np.ndarray, c: np.ndarr
     _check(lib().orc_run_pingpong(fwd._h, rev._h, _ptr(a), _ptr(b), _ptr(c), nbytes, iters),
            "orc_run_pingpong")
 
+
+
+def pingpong_threaded(fwd: Conn, rev: Conn, a: np.ndarray, b: np.ndarray, c: np.ndarray,
+                      nbytes: int, iters: int) -> float:
+    """iters round trips a -> b (fwd), b -> c (rev) with the two endpoints on two
+    threads (on two distinct cores when possible); returns the wall seconds."""
+    for x in (a, b, c):
+        assert x.dtype == np.uint8 and x.flags.c_contiguous and x.size >= nbytes
+    sec = C.c_double()
+    _check(lib().orc_pingpong_threaded(fwd._h, rev._h, _ptr(a), _ptr(b), _ptr(c), int(nbytes),
+                                       int(iters), C.byref(sec)), "orc_pingpong_threaded")
+    return sec.value
 
 def enumerate_interleavings(proto, nchannels: int, nslots: int, slot_bytes: int, A: np.ndarray,
                             mutation: str = "none", prior_runs: int = 0,

@@ -48,6 +48,7 @@
  *      never spans two transfers.
  */
 #include "oracle.h"
+#include "oracle_internal.h"
 
 #include <stdio.h>
 #include <stdlib.h>
@@ -143,16 +144,6 @@ int orc_partition(uint64_t n, int nch, uint64_t* beg, uint64_t* len) {
 }
 
 /* ------------------------------------------------------------ connection */
-typedef struct {
-  uint64_t head, tail, ptrx, base;
-} orc_ctrl;
-
-struct orc_conn {
-  int proto, nch, nslots, mutation, order;
-  uint64_t slot_bytes, step_bytes;
-  uint8_t* fifo; /* nch * nslots * slot_bytes, zero at creation; none for zero-copy */
-  orc_ctrl* ctrl;
-};
 
 orc_conn* orc_conn_new(int proto, int nch, int nslots, uint64_t slot_bytes) {
   if (proto < ORC_SIMPLE || proto > ORC_ZC || nch < 1 || nch > 64 || nslots < 1) return NULL;

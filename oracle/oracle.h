@@ -99,6 +99,16 @@ int orc_run(orc_conn* c, const uint8_t* A, uint8_t* B, uint64_t n);
 /* iters round trips: a -> b on fwd, then b -> c on rev, each as one transfer */
 int orc_run_pingpong(orc_conn* fwd, orc_conn* rev, const uint8_t* a, uint8_t* b, uint8_t* c,
                      uint64_t n, int iters);
+/* Threaded mode: the same transfer with the producer and consumer of every
+ * channel as actors on nthreads real threads (1 .. 2 x channels; more are
+ * clamped), handing off through C11 atomics.  Its end state must equal
+ * orc_run's. */
+int orc_run_threaded(orc_conn* c, const uint8_t* A, uint8_t* B, uint64_t n, int nthreads);
+/* Threaded ping-pong (SIMPLE or LL): endpoint X and endpoint Y on two
+ * threads, pinned to two distinct cores when the process may use two;
+ * *seconds = wall time of the iters round trips. */
+int orc_pingpong_threaded(orc_conn* fwd, orc_conn* rev, const uint8_t* a, uint8_t* b,
+                          uint8_t* c, uint64_t n, int iters, double* seconds);
 /* out = {head, tail, ptrExchange, steps (the persistent step base)} */
 int orc_conn_state(const orc_conn* c, int channel, uint64_t* out4);
 const uint8_t* orc_conn_fifo(const orc_conn* c, int channel, uint64_t* bytes);

@@ -119,18 +119,27 @@ __device__ __forceinline__ void raise_err(Status* st, uint32_t code) {
   __hip_atomic_store(&st->err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Bound of one wait: wall-clock ticks (s_memrealtime) plus the host abort word.
+// Bound of one wait: wall-clock ticks (s_memrealtime) plus the host abort
+// word.  Reading the clock is a scalar-memory round trip that would sit
+// between two polls, so it is read only every 64th poll (the first read
+// starts the clock) and the abort word every 1024th: a wait ends at most
+// about 64 polls after its bound.
 struct Deadline {
   uint64_t start, ticks;
   Status* st;
   uint32_t n;
-  __device__ Deadline(uint64_t t, Status* s) : start(wall_clock64()), ticks(t), st(s), n(0) {}
+  __device__ Deadline(uint64_t t, Status* s) : start(0), ticks(t), st(s), n(0) {}
   __device__ __forceinline__ uint32_t expired() {
-    if (((++n) & 255u) == 0u &&
+    if (((++n) & 63u) != 0u) return 0;
+    if ((n & 1023u) == 0u &&
         __hip_atomic_load(&st->abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM))
       return XFER_ERR_ABORTED;
-    if (wall_clock64() - start > ticks) return XFER_ERR_TIMEOUT;
-    return 0;
+    const uint64_t now = wall_clock64();
+    if (start == 0) {
+      start = now;
+      return 0;
+    }
+    return now - start > ticks ? XFER_ERR_TIMEOUT : 0;
   }
 };
 

@@ -19,7 +19,7 @@ W1 = dict(name="simple_1ch_4MiB", proto="simple", nchannels=1, nslots=8, slot_by
           fifo_loc="device", wgs_per_channel=1, block_threads=256, nbytes=4 << 20)
 
 W2 = dict(name="ll_pingpong", proto="ll", nchannels=1, nslots=8, slot_bytes=32 << 10,
-          fifo_loc="device", wgs_per_channel=1, block_threads=256, iters=10000)
+          fifo_loc="device", wgs_per_channel=1, block_threads=1024, iters=10000)
 W2_SIZES = [8 << i for i in range(14)]  # 8 B .. 64 KiB
 
 W3 = dict(name="simple_32ch_1GiB", proto="simple", nchannels=32, nslots=8, slot_bytes=512 << 10,
