@@ -93,10 +93,10 @@ typedef struct {
   int ctrl_loc;         /* xfer_ctrl_loc */
   uint32_t timeout_ms;  /* bound on every in-kernel wait; default 10000 */
   int xcd_pairing;      /* 0 (default) or 1: place each producer/consumer pair on one XCD,
-                           an XCD's producers dispatched before its consumers (applied when
-                           the grid is a multiple of 16 workgroups); -1: dispatch order
-                           (producers on even block ids, which the hardware deals to XCDs
-                           0, 2, 4 and 6 only) */
+                           an XCD's producers dispatched before its consumers (the grid is
+                           padded to a multiple of 16 workgroups; padding exits at once);
+                           -1: dispatch order (producers on even block ids, which the
+                           hardware deals to XCDs 0, 2, 4 and 6 only) */
   int roles;            /* fault injection: 0 = both sides (default), 1 = producer only,
                            2 = consumer/receiver only; a lone side ends its waits with
                            XFER_ERR_TIMEOUT (or XFER_ERR_ABORTED after xfer_conn_abort) */
@@ -225,7 +225,8 @@ int xfer_conn_read_fifo(const xfer_conn* c, int channel, void* host_dst, size_t 
  * running or later launch on it ends with XFER_ERR_ABORTED. */
 int xfer_conn_abort(xfer_conn* c);
 
-/* Grid (workgroups) and block size one run of this connection launches. */
+/* Grid (workgroups, padding included) and block size one run of this
+ * connection launches. */
 int xfer_conn_launch_shape(const xfer_conn* c, int* workgroups, int* block_threads);
 
 /* Thread-local message of the last failure in this thread ("" if none). */

@@ -198,12 +198,11 @@ ConnArgs conn_args(const xfer_conn* c, const void* src, void* dst, uint64_t nbyt
 
 uint32_t wgs_of(const xfer_conn* c) { return uint32_t(c->nch) * uint32_t(c->lanes) * 2u; }
 
-// Keep a pair (producer 2q, consumer 2q+1) on one XCD, producers first in
-// each XCD's dispatch order (the kernel's logical_wg); needs a grid of a
-// multiple of 16 workgroups, otherwise dispatch order is kept.
-uint32_t remap_flag(int pairing, uint32_t total) {
-  return pairing && total % 16u == 0 ? 1u : 0u;
-}
+// Launched grid.  Pairing keeps a pair (producer 2q, consumer 2q+1) on one
+// XCD, producers first in each XCD's dispatch order (the kernel's
+// logical_wg); its remap needs a grid of a multiple of 16, so the grid is
+// padded with workgroups that exit at once.
+uint32_t grid_of(int pairing, uint32_t total) { return pairing ? (total + 15u) & ~15u : total; }
 
 // Resident-workgroup capacity per (device, kernel variant, block size),
 // queried once: the runtime query costs far more than a launch.
@@ -460,7 +459,7 @@ extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nb
   rc = plan_steps(c, nbytes, uint64_t(iters), add, "xfer_run");
   if (rc) return rc;
   DeviceGuard g(c->device);
-  const uint32_t total = wgs_of(c);
+  const uint32_t total = grid_of(c->xcd_pairing, wgs_of(c));
   const Variant v = variant_of(c, aligned16(src) && aligned16(dst));
   rc = check_resident(v, 0, c->block, total, "xfer_run");
   if (rc) return rc;
@@ -470,7 +469,7 @@ extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nb
   args.nconn = 1;
   args.iters = uint32_t(iters);
   args.total_wgs = total;
-  args.xcd_remap = remap_flag(c->xcd_pairing, total);
+  args.xcd_remap = c->xcd_pairing ? 1u : 0u;
   args.timeout_ticks = c->timeout_ticks;
   hipError_t e = launch_run1(v, args, c->block, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "xfer_run launch");
@@ -529,7 +528,7 @@ extern "C" int xfer_run_messages(xfer_conn* c, const void* src, void* dst, const
     aligned = aligned && (m.off & 15u) == 0;
   }
   DeviceGuard g(c->device);
-  const uint32_t total = wgs_of(c);
+  const uint32_t total = grid_of(c->xcd_pairing, wgs_of(c));
   const Variant v = variant_of(c, aligned);
   rc = check_resident(v, 0, c->block, total, "xfer_run_messages");
   if (rc) return rc;
@@ -541,7 +540,7 @@ extern "C" int xfer_run_messages(xfer_conn* c, const void* src, void* dst, const
     args.nconn = 1;
     args.iters = 1;
     args.total_wgs = total;
-    args.xcd_remap = remap_flag(c->xcd_pairing, total);
+    args.xcd_remap = c->xcd_pairing ? 1u : 0u;
     args.timeout_ticks = c->timeout_ticks;
     args.nmsgs = uint32_t(cnt);
     for (size_t i = 0; i < cnt; ++i) args.msgs[i] = msgs[first + i];
@@ -591,12 +590,13 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
   if (!live) return XFER_OK;
   DeviceGuard g(first->device);
   const Variant v = variant_of(first, aligned);
-  int rc = check_resident(v, 1, first->block, total, "xfer_run_batch");
+  const uint32_t grid = grid_of(first->xcd_pairing, total);
+  int rc = check_resident(v, 1, first->block, grid, "xfer_run_batch");
   if (rc) return rc;
   args.nconn = uint32_t(live);
   args.iters = 1;
-  args.total_wgs = total;
-  args.xcd_remap = remap_flag(first->xcd_pairing, total);
+  args.total_wgs = grid;
+  args.xcd_remap = first->xcd_pairing ? 1u : 0u;
   args.timeout_ticks = first->timeout_ticks;
   hipError_t e = launch_runB(v, args, first->block, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "xfer_run_batch launch");
@@ -631,7 +631,7 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
   rc = plan_steps(rev, nbytes, uint64_t(iters), addr, "xfer_run_pingpong");
   if (rc) return rc;
   DeviceGuard g(fwd->device);
-  const uint32_t total = wgs_of(fwd);
+  const uint32_t total = grid_of(fwd->xcd_pairing, wgs_of(fwd));
   const int scope = (fwd->scope == kScopeSystem || rev->scope == kScopeSystem) ? kScopeSystem
                                                                                : kScopeAgent;
   const Variant v{fwd->proto, scope, fwd->ordering,
@@ -644,7 +644,7 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
   args.rev = conn_args(rev, b, cbuf, nbytes, 0);
   args.iters = uint32_t(iters);
   args.total_wgs = total;
-  args.xcd_remap = remap_flag(fwd->xcd_pairing, total);
+  args.xcd_remap = fwd->xcd_pairing ? 1u : 0u;
   args.timeout_ticks = std::max(fwd->timeout_ticks, rev->timeout_ticks);
   hipError_t e = launch_ping(v, args, fwd->block, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "xfer_run_pingpong launch");
@@ -722,7 +722,7 @@ extern "C" int xfer_conn_abort(xfer_conn* c) {
 extern "C" int xfer_conn_launch_shape(const xfer_conn* c, int* workgroups, int* block_threads) {
   if (!c || !workgroups || !block_threads)
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_launch_shape: NULL argument");
-  *workgroups = int(wgs_of(c));
+  *workgroups = int(grid_of(c->xcd_pairing, wgs_of(c)));
   *block_threads = c->block;
   return XFER_OK;
 }

@@ -348,8 +348,13 @@ __device__ __forceinline__ bool wg_failed(Shared& sh, uint32_t local_err, Status
   return e != 0;
 }
 
+// Slot of step g: g mod nslots.  A 64-bit remainder is a long chain of
+// scalar instructions that sits on the latency path of every small message,
+// so a power-of-two slot count takes a mask instead.
 __device__ __forceinline__ uint8_t* slot_of(const ConnArgs& A, uint32_t c, uint64_t g) {
-  return A.fifo + (static_cast<uint64_t>(c) * A.nslots + g % A.nslots) * A.slot_bytes;
+  const uint32_t ns = A.nslots;
+  const uint64_t s = (ns & (ns - 1u)) == 0u ? (g & (ns - 1u)) : g % ns;
+  return A.fifo + (static_cast<uint64_t>(c) * ns + s) * A.slot_bytes;
 }
 
 __device__ __forceinline__ uint32_t chunk_len(const Side& sd, uint64_t S, uint64_t j) {
@@ -473,23 +478,25 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
 // ---------------------------------------------------------------------- LL
 // Line = {4 payload bytes, flag = g+1}, stored and loaded as one 64-bit
 // access at the connection's scope; the last word of a chunk is zero-padded.
+// Chunks are under 2^31 bytes (half a slot of at most 1 GiB), so line
+// indices and byte offsets within a chunk fit 32 bits.
 template <bool AL>
-__device__ __forceinline__ uint32_t ll_src_word(const uint8_t* p, uint64_t L, uint64_t line) {
-  const uint64_t off = line * 4;
-  if (AL && off + 4 <= L) return *reinterpret_cast<const uint32_t*>(p + off);
+__device__ __forceinline__ uint32_t ll_src_word(const uint8_t* p, uint32_t L, uint32_t line) {
+  const uint32_t off = line * 4u;
+  if (AL && off + 4u <= L) return *reinterpret_cast<const uint32_t*>(p + off);
   uint32_t v = 0;
-  for (uint64_t b = 0; b < 4 && off + b < L; ++b) v |= static_cast<uint32_t>(p[off + b]) << (8 * b);
+  for (uint32_t b = 0; b < 4u && off + b < L; ++b) v |= static_cast<uint32_t>(p[off + b]) << (8u * b);
   return v;
 }
 
 template <bool AL>
-__device__ __forceinline__ void ll_dst_word(uint8_t* p, uint64_t L, uint64_t line, uint32_t v) {
-  const uint64_t off = line * 4;
-  if (AL && off + 4 <= L) {
+__device__ __forceinline__ void ll_dst_word(uint8_t* p, uint32_t L, uint32_t line, uint32_t v) {
+  const uint32_t off = line * 4u;
+  if (AL && off + 4u <= L) {
     *reinterpret_cast<uint32_t*>(p + off) = v;
     return;
   }
-  for (uint64_t b = 0; b < 4 && off + b < L; ++b) p[off + b] = static_cast<uint8_t>(v >> (8 * b));
+  for (uint32_t b = 0; b < 4u && off + b < L; ++b) p[off + b] = static_cast<uint8_t>(v >> (8u * b));
 }
 
 template <int SC, int ORD, bool AL>
@@ -502,12 +509,17 @@ __device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
     const uint64_t g = g0 + j;
     if ((err = wait_credit<SC, ORD>(A, sd, g, ticks))) break;
     const uint32_t L = chunk_len(sd, S, j);
-    const uint64_t nl = (L + 3) / 4;
+    const uint32_t nl = (L + 3u) / 4u;
     uint64_t* lines = reinterpret_cast<uint64_t*>(slot_of(A, c, g));
     const uint8_t* s = src + sd.r.beg + j * S;
     const uint64_t flag = static_cast<uint64_t>(static_cast<uint32_t>(g + 1)) << 32;
-    for (uint64_t blk = w; blk * nthr < nl; blk += P) {
-      const uint64_t i = blk * nthr + threadIdx.x;
+    if (nl <= nthr * P) {  // one pass: at most one line per thread
+      const uint32_t i = w * nthr + threadIdx.x;
+      if (i < nl) st_u64<SC>(&lines[i], flag | ll_src_word<AL>(s, L, i));
+      continue;
+    }
+    for (uint32_t blk = w; blk * nthr < nl; blk += P) {
+      const uint32_t i = blk * nthr + threadIdx.x;
       if (i < nl) st_u64<SC>(&lines[i], flag | ll_src_word<AL>(s, L, i));
     }
   }
@@ -524,38 +536,52 @@ __device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
     const uint64_t g = g0 + j;
     const uint32_t want = static_cast<uint32_t>(g + 1);
     const uint32_t L = chunk_len(sd, S, j);
-    const uint64_t nl = (L + 3) / 4;
+    const uint32_t nl = (L + 3u) / 4u;
     const uint64_t* lines = reinterpret_cast<const uint64_t*>(slot_of(A, c, g));
     uint8_t* d = dst + sd.r.beg + j * S;
     uint32_t err = 0;
-    for (uint64_t b0 = w; b0 * nthr < nl && !err; b0 += static_cast<uint64_t>(kLLUnroll) * P) {
-      uint64_t v[kLLUnroll];
-      bool pend = false;
-#pragma unroll
-      for (int u = 0; u < kLLUnroll; ++u) {
-        const uint64_t i = (b0 + static_cast<uint64_t>(u) * P) * nthr + threadIdx.x;
-        v[u] = i < nl ? ld_u64<SC>(&lines[i]) : (static_cast<uint64_t>(want) << 32);
-        pend |= static_cast<uint32_t>(v[u] >> 32) != want;
-      }
-      if (pend) {
-        Deadline dl(ticks, A.status);
-        while (pend) {
-          pend = false;
-#pragma unroll
-          for (int u = 0; u < kLLUnroll; ++u) {
-            if (static_cast<uint32_t>(v[u] >> 32) != want) {
-              v[u] = ld_u64<SC>(&lines[(b0 + static_cast<uint64_t>(u) * P) * nthr + threadIdx.x]);
-              pend |= static_cast<uint32_t>(v[u] >> 32) != want;
-            }
-          }
-          if (pend && (err = dl.expired())) break;
+    if (nl <= nthr * P) {  // one pass: at most one line per thread
+      const uint32_t i = w * nthr + threadIdx.x;
+      if (i < nl) {
+        uint64_t v = ld_u64<SC>(&lines[i]);
+        if (static_cast<uint32_t>(v >> 32) != want) {
+          Deadline dl(ticks, A.status);
+          do {
+            v = ld_u64<SC>(&lines[i]);
+          } while (static_cast<uint32_t>(v >> 32) != want && !(err = dl.expired()));
         }
+        if (!err) ll_dst_word<AL>(d, L, i, static_cast<uint32_t>(v));
       }
-      if (!err) {
+    } else {
+      for (uint32_t b0 = w; b0 * nthr < nl && !err; b0 += static_cast<uint32_t>(kLLUnroll) * P) {
+        uint64_t v[kLLUnroll];
+        bool pend = false;
 #pragma unroll
         for (int u = 0; u < kLLUnroll; ++u) {
-          const uint64_t i = (b0 + static_cast<uint64_t>(u) * P) * nthr + threadIdx.x;
-          if (i < nl) ll_dst_word<AL>(d, L, i, static_cast<uint32_t>(v[u]));
+          const uint32_t i = (b0 + static_cast<uint32_t>(u) * P) * nthr + threadIdx.x;
+          v[u] = i < nl ? ld_u64<SC>(&lines[i]) : (static_cast<uint64_t>(want) << 32);
+          pend |= static_cast<uint32_t>(v[u] >> 32) != want;
+        }
+        if (pend) {
+          Deadline dl(ticks, A.status);
+          while (pend) {
+            pend = false;
+#pragma unroll
+            for (int u = 0; u < kLLUnroll; ++u) {
+              if (static_cast<uint32_t>(v[u] >> 32) != want) {
+                v[u] = ld_u64<SC>(&lines[(b0 + static_cast<uint32_t>(u) * P) * nthr + threadIdx.x]);
+                pend |= static_cast<uint32_t>(v[u] >> 32) != want;
+              }
+            }
+            if (pend && (err = dl.expired())) break;
+          }
+        }
+        if (!err) {
+#pragma unroll
+          for (int u = 0; u < kLLUnroll; ++u) {
+            const uint32_t i = (b0 + static_cast<uint32_t>(u) * P) * nthr + threadIdx.x;
+            if (i < nl) ll_dst_word<AL>(d, L, i, static_cast<uint32_t>(v[u]));
+          }
         }
       }
     }
@@ -752,7 +778,8 @@ __device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<M
 // ------------------------------------------------------------------ kernels
 // Logical workgroup of this block.  Blocks are dealt round-robin to the 8
 // XCDs, so block b runs on XCD b % 8 as that XCD's (b / 8)-th block.  With
-// the remap (total a multiple of 16) XCD x serves the total/16 consecutive
+// the remap (the host pads the grid to a multiple of 16; logical ids past
+// the real workgroups exit at once) XCD x serves the total/16 consecutive
 // pairs starting at x * total/16: its first total/16 blocks are their
 // producers, the rest their consumers.  A pair then shares one XCD, and
 // producers spread evenly over the XCDs and over each XCD's dispatch order.
@@ -777,7 +804,7 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
   const uint32_t local = lw - A.wg_begin;
   const uint32_t pair = local >> 1, role = local & 1u;
   const uint32_t c = pair / A.lanes, w = pair % A.lanes;
-  if (c >= A.nch) return;  // never taken: the host sizes the grid exactly
+  if (c >= A.nch) return;  // padding of a paired launch (its grid is a multiple of 16)
   if (!((A.roles >> role) & 1u)) return;  // side switched off for fault injection
   Side sd = make_side(A, c, w, role == 0, SC);
   const uint64_t ticks = args.timeout_ticks;
