@@ -200,37 +200,42 @@ def bench_w2(torch, T, W, synth):
 
 
 def bench_w4(torch, T, W, synth):
+    """Zero-copy through ptrExchange (pair and ring), and the same shapes with
+    the destination known before the launch ("direct": no pointer hand-off)."""
     res = {}
-    cfg = W.W4_PAIR
-    n = cfg["nbytes"]
-    a = torch.from_numpy(synth.fp32_uniform_bytes(n, synth.workload_seed(4))).to("cuda")
-    b = torch.empty_like(a)
-    conn = W.make_conn(cfg)
-    total, per = T.time_launches(lambda: conn.run(a, b, n, T.stream), 3, 20)
-    check_no_error(conn, cfg["nchannels"], "W4 pair")
-    ok = bool(torch.equal(a, b))
-    conn.close()
-    gbs = n / (per * 1e-3) / 1e9
-    res["pair"] = {"payload_gbs": round(gbs, 2), "real_gbs": round(2 * gbs, 2),
-                   "hbm_frac": round(2 * gbs / HBM_PEAK_GBS, 4), "kernel_ms": round(per, 4),
-                   "b_equals_a": ok}
-    del a, b
-    cfg = W.W4_RING
-    ring = W.make_ring(cfg)
-    tot = cfg["endpoints"] * cfg["slice_bytes"]
-    a = torch.from_numpy(synth.fp32_uniform_bytes(tot, synth.workload_seed(4) + 100)).to("cuda")
-    b = torch.empty_like(a)
-    total, per = T.time_launches(lambda: ring.run(a, b, T.stream), 3, 20)
-    for e in ring.edges.values():
-        check_no_error(e, cfg["channels_per_edge"], "W4 ring")
-    S = cfg["slice_bytes"]
-    ok = all(bool(torch.equal(a[r * S:(r + 1) * S], b[((r + 1) % 8) * S:((r + 1) % 8 + 1) * S]))
-             for r in range(8))
-    ring.close()
-    gbs = tot / (per * 1e-3) / 1e9
-    res["ring"] = {"payload_gbs": round(gbs, 2), "real_gbs": round(2 * gbs, 2),
-                   "hbm_frac": round(2 * gbs / HBM_PEAK_GBS, 4), "kernel_ms": round(per, 4),
-                   "edges_ok": ok}
+    for pair_cfg, ring_cfg, key in ((W.W4_PAIR, W.W4_RING, ""), (W.W4D_PAIR, W.W4D_RING, "direct_")):
+        proto = pair_cfg["proto"]
+        cfg = pair_cfg
+        n = cfg["nbytes"]
+        a = torch.from_numpy(synth.fp32_uniform_bytes(n, synth.workload_seed(4))).to("cuda")
+        b = torch.empty_like(a)
+        conn = W.make_conn(cfg)
+        total, per = T.time_launches(lambda: conn.run(a, b, n, T.stream), 3, 20)
+        check_no_error(conn, cfg["nchannels"], "W4 pair " + proto)
+        ok = bool(torch.equal(a, b))
+        conn.close()
+        gbs = n / (per * 1e-3) / 1e9
+        res[key + "pair"] = {"payload_gbs": round(gbs, 2), "real_gbs": round(2 * gbs, 2),
+                             "hbm_frac": round(2 * gbs / HBM_PEAK_GBS, 4),
+                             "kernel_ms": round(per, 4), "b_equals_a": ok}
+        del a, b
+        cfg = ring_cfg
+        ring = W.make_ring(cfg)
+        tot = cfg["endpoints"] * cfg["slice_bytes"]
+        a = torch.from_numpy(synth.fp32_uniform_bytes(tot, synth.workload_seed(4) + 100)).to("cuda")
+        b = torch.empty_like(a)
+        total, per = T.time_launches(lambda: ring.run(a, b, T.stream), 3, 20)
+        for e in ring.edges.values():
+            check_no_error(e, cfg["channels_per_edge"], "W4 ring " + proto)
+        S = cfg["slice_bytes"]
+        ok = all(bool(torch.equal(a[r * S:(r + 1) * S], b[((r + 1) % 8) * S:((r + 1) % 8 + 1) * S]))
+                 for r in range(8))
+        ring.close()
+        del a, b
+        gbs = tot / (per * 1e-3) / 1e9
+        res[key + "ring"] = {"payload_gbs": round(gbs, 2), "real_gbs": round(2 * gbs, 2),
+                             "hbm_frac": round(2 * gbs / HBM_PEAK_GBS, 4),
+                             "kernel_ms": round(per, 4), "edges_ok": ok}
     return res
 
 
@@ -251,19 +256,41 @@ def bench_w5(torch, T, W, synth):
     conn.close()
     gbs = tot / (total * 1e-3) / 1e9
     gbs_each = tot / (each * 1e-3) / 1e9
-    # pinned-memory copy ceilings of the same link, for context
-    h = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
-    d = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    # pinned-memory copy ceilings of the same link, for context: one
+    # direction at a time, and both at once (the FIFO's traffic pattern)
+    m = 256 << 20
+    h = torch.empty(m, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(m, dtype=torch.uint8, device="cuda")
     d2h, _ = T.time_launches(lambda: h.copy_(d, non_blocking=True), 2, 5)
     h2d, _ = T.time_launches(lambda: d.copy_(h, non_blocking=True), 2, 5)
+    h2 = torch.empty(m, dtype=torch.uint8, pin_memory=True)
+    d2 = torch.empty(m, dtype=torch.uint8, device="cuda")
+    s_up, s_down = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def duplex():
+        with torch.cuda.stream(s_up):
+            h.copy_(d, non_blocking=True)
+        with torch.cuda.stream(s_down):
+            d2.copy_(h2, non_blocking=True)
+        s_up.synchronize()
+        s_down.synchronize()
+
+    for _ in range(2):
+        duplex()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        duplex()
+    dup_gbs = m / ((time.perf_counter() - t0) / 5) / 1e9
     return {"payload_gbs": round(gbs, 2), "pcie_frac": round(gbs / PCIE_PEAK_GBS, 4),
             "messages": len(sizes), "ms": round(total, 3), "b_equals_a": ok,
             "launches": (len(sizes) + 127) // 128,
             "one_launch_per_message": {"payload_gbs": round(gbs_each, 2),
                                        "pcie_frac": round(gbs_each / PCIE_PEAK_GBS, 4),
                                        "ms": round(each, 3)},
-            "pinned_copy_d2h_gbs": round((256 << 20) / (d2h * 1e-3) / 1e9, 2),
-            "pinned_copy_h2d_gbs": round((256 << 20) / (h2d * 1e-3) / 1e9, 2)}
+            "pinned_copy_d2h_gbs": round(m / (d2h * 1e-3) / 1e9, 2),
+            "pinned_copy_h2d_gbs": round(m / (h2d * 1e-3) / 1e9, 2),
+            "pinned_copy_duplex_gbs_each_way": round(dup_gbs, 2),
+            "vs_duplex_copy": round(gbs / dup_gbs, 3)}
 
 
 def plain_copy_ceiling(torch, T) -> dict:

@@ -59,7 +59,12 @@ typedef enum {
 typedef enum {
   XFER_PROTO_SIMPLE = 0,   /* copy through FIFO slots, tail/head per step */
   XFER_PROTO_LL = 1,       /* 8-byte lines {4 data bytes, 4-byte flag = step+1}, no polled tail */
-  XFER_PROTO_ZEROCOPY = 2  /* receiver publishes the destination per step in ptrExchange */
+  XFER_PROTO_ZEROCOPY = 2, /* receiver publishes the destination per step in ptrExchange */
+  XFER_PROTO_ZEROCOPY_DIRECT = 3 /* destination known before the launch: the producer writes
+                                    each step at its own offset of dst and publishes tail, the
+                                    receiver answers with head; ptrExchange unused
+                                    ("【NCCL】transport数据传输（二）", p2pTransport, zero copy,
+                                    second kind) */
 } xfer_proto;
 
 typedef enum {

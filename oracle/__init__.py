@@ -20,8 +20,9 @@ SRCS = [os.path.join(HERE, f) for f in ("oracle.c", "threaded.c", "oracle.h",
                                         "oracle_internal.h")]
 LIB = os.path.join(HERE, "liboracle.so")
 
-SIMPLE, LL, ZC = 0, 1, 2
-PROTO_NAMES = {"simple": SIMPLE, "ll": LL, "zc": ZC, "zerocopy": ZC}
+SIMPLE, LL, ZC, ZCD = 0, 1, 2, 3
+PROTO_NAMES = {"simple": SIMPLE, "ll": LL, "zc": ZC, "zerocopy": ZC, "zcd": ZCD,
+               "zerocopy_direct": ZCD}
 
 OP_RECV_SETUP, OP_SEND_SETUP, OP_CONNECT_BATCH = 0, 1, 2
 

@@ -44,6 +44,10 @@
  *      so the producer never waits on head.  (Order of the five actions:
  *      transfer page, p2pTransport, "zero copy方式传递数据", first kind.)
  *      The oracle's address token is (offset of the chunk in B) + 1.
+ *      Zero-copy direct (ORC_ZCD, the page's second kind): the destination is
+ *      known before the launch, so ptrExchange is not used; per step the
+ *      producer writes the chunk into B and publishes tail = g+1, and the
+ *      receiver, seeing tail > g, publishes head = g+1.
  *  R8  The step base persists across transfers on one connection; a step
  *      never spans two transfers.
  */
@@ -145,8 +149,11 @@ int orc_partition(uint64_t n, int nch, uint64_t* beg, uint64_t* len) {
 
 /* ------------------------------------------------------------ connection */
 
+/* Zero-copy modes write straight into B: no FIFO. */
+static int has_fifo(int proto) { return proto == ORC_SIMPLE || proto == ORC_LL; }
+
 orc_conn* orc_conn_new(int proto, int nch, int nslots, uint64_t slot_bytes) {
-  if (proto < ORC_SIMPLE || proto > ORC_ZC || nch < 1 || nch > 64 || nslots < 1) return NULL;
+  if (proto < ORC_SIMPLE || proto > ORC_ZCD || nch < 1 || nch > 64 || nslots < 1) return NULL;
   if (proto == ORC_LL ? (slot_bytes < 8 || slot_bytes % 8) : (slot_bytes < 16 || slot_bytes % 16))
     return NULL;
   orc_conn* c = (orc_conn*)calloc(1, sizeof(*c));
@@ -157,8 +164,8 @@ orc_conn* orc_conn_new(int proto, int nch, int nslots, uint64_t slot_bytes) {
   c->slot_bytes = slot_bytes;
   c->step_bytes = orc_step_bytes(proto, slot_bytes);
   c->ctrl = (orc_ctrl*)calloc((size_t)nch, sizeof(orc_ctrl)); /* Reading R1: all zero */
-  if (proto != ORC_ZC) c->fifo = (uint8_t*)calloc((size_t)nch * nslots, slot_bytes);
-  if (!c->ctrl || (proto != ORC_ZC && !c->fifo)) {
+  if (has_fifo(proto)) c->fifo = (uint8_t*)calloc((size_t)nch * nslots, slot_bytes);
+  if (!c->ctrl || (has_fifo(proto) && !c->fifo)) {
     orc_conn_free(c);
     return NULL;
   }
@@ -244,7 +251,7 @@ static uint64_t meta_size(const orc_conn* c) {
 }
 
 static uint64_t fifo_size(const orc_conn* c) {
-  return c->proto == ORC_ZC ? 0 : (uint64_t)c->nch * c->nslots * c->slot_bytes;
+  return has_fifo(c->proto) ? (uint64_t)c->nch * c->nslots * c->slot_bytes : 0;
 }
 
 /* Fills meta for a new transfer of n bytes; FIFO and B are set by the caller. */
@@ -339,6 +346,8 @@ static int prod_enabled(const world* w, int ch) {
     case ORC_LL:
       if (u->pj == u->k) return !u->pfinal;
       return u->pline > 0 || u->pphase != 0 || credit_ok(w, q, g);
+    case ORC_ZCD: /* the destination is known: nothing to wait for */
+      return u->pj < u->k;
     default: /* ORC_ZC: taking an address needs a published one */
       if (u->pj >= u->k) return 0;
       if (u->pphase == 0) return u->pnext != 0 || q->ptrx != 0;
@@ -363,7 +372,7 @@ static int cons_enabled(const world* w, int ch) {
       const uint8_t* line = slot_ptr(w, ch, g) + 8 * u->cline;
       return get32(line + 4) == (uint32_t)(g + 1);
     }
-    default: /* ORC_ZC receiver, completion cursor */
+    default: /* ORC_ZC and ORC_ZCD receiver, completion cursor */
       return q->tail > g;
   }
 }
@@ -587,12 +596,39 @@ static int zc_pub(world* w, int ch) {
   return 0;
 }
 
-/* Zero-copy receiver, completion cursor: tail > g means step g landed. */
+/* Zero-copy receiver, completion cursor: tail > g means step g landed, so
+ * its bytes must be in B when the receiver takes it. */
 static int zc_done(world* w, int ch) {
+  const orc_conn* c = w->cfg;
   orc_ctrl* q = &W_ctrl(w)[ch];
   orc_cur* u = &W_cur(w)[ch];
+  uint64_t off = u->beg + u->cj * c->step_bytes;
+  if (memcmp(w->B + off, w->A + off, (size_t)chunk_len(w, u, u->cj)) != 0)
+    return ORC_V_READ_UNFILLED;
   q->head = q->base + u->cj + 1;
   u->cj++;
+  return 0;
+}
+
+/* Zero-copy direct producer (the page's second kind): write the chunk into
+ * B at its own offset, then publish tail = g+1. */
+static int zcd_prod(world* w, int ch) {
+  const orc_conn* c = w->cfg;
+  orc_ctrl* q = &W_ctrl(w)[ch];
+  orc_cur* u = &W_cur(w)[ch];
+  uint64_t g = q->base + u->pj, off = u->beg + u->pj * c->step_bytes;
+  int early = c->mutation == ORC_MUT_EARLY_TAIL;
+  if ((u->pphase == 0) != early) {
+    memcpy(w->B + off, w->A + off, (size_t)chunk_len(w, u, u->pj));
+  } else {
+    q->tail = g + 1;
+  }
+  if (u->pphase == 0) {
+    u->pphase = 1;
+  } else {
+    u->pphase = 0;
+    u->pj++;
+  }
   return 0;
 }
 
@@ -602,6 +638,8 @@ static int fire(world* w, int ch, int act, uint64_t budget) {
       return act == ACT_PROD ? simple_prod(w, ch) : simple_cons(w, ch);
     case ORC_LL:
       return act == ACT_PROD ? ll_prod(w, ch, budget) : ll_cons(w, ch, budget);
+    case ORC_ZCD:
+      return act == ACT_PROD ? zcd_prod(w, ch) : zc_done(w, ch);
     default:
       return act == ACT_PROD ? zc_prod(w, ch) : act == ACT_PUB ? zc_pub(w, ch) : zc_done(w, ch);
   }
@@ -610,7 +648,7 @@ static int fire(world* w, int ch, int act, uint64_t budget) {
 /* Steps the producer of a channel has begun, for the in-flight bound. */
 static int window_ok(const world* w, int ch) {
   const orc_conn* c = w->cfg;
-  if (c->proto == ORC_ZC) return 1;
+  if (!has_fifo(c->proto)) return 1;
   const orc_ctrl* q = &W_ctrl(w)[ch];
   const orc_cur* u = &W_cur(w)[ch];
   uint64_t begun = u->pj;

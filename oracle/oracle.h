@@ -11,7 +11,9 @@
  *  - the producer/consumer data transfer through a ring of FIFO slots with
  *    head/tail step counters: the copy mode and the zero-copy mode with the
  *    ptrExchange word ("【NCCL】transport数据传输（二）", p2pTransport:
- *    "zero copy方式传递数据" and "copy方式传递数据"; the same hand-off over
+ *    "zero copy方式传递数据" (both kinds: the destination exchanged through
+ *    ptrExchange during the kernel, or known before it) and "copy方式传递数据";
+ *    the same hand-off over
  *    host memory in its shmTransport "正常方式" section);
  *  - the LL idea of a completion flag carried inside the data
  *    ("RDMA and GPUDirect" series article, section 四.1, signalling option 2);
@@ -34,6 +36,7 @@ extern "C" {
 #define ORC_SIMPLE 0
 #define ORC_LL 1
 #define ORC_ZC 2
+#define ORC_ZCD 3 /* zero-copy with the destination known before the launch (no ptrExchange) */
 
 /* error returns (negative) */
 #define ORC_E_ARG (-1)
@@ -43,7 +46,9 @@ extern "C" {
 
 /* protocol violations (positive), found by the simulator or the enumerator */
 #define ORC_V_OVERWRITE 1     /* producer wrote a slot whose previous step was not drained */
-#define ORC_V_READ_UNFILLED 2 /* consumer read a slot/line that does not hold its step's payload */
+#define ORC_V_READ_UNFILLED 2 /* consumer read a slot/line that does not hold its step's payload,
+                                 or a zero-copy receiver completed a step whose bytes had not
+                                 landed in the destination */
 #define ORC_V_READ_EARLY 3    /* consumer read a slot before observing tail > step */
 #define ORC_V_WINDOW 4        /* more than nslots steps in flight */
 #define ORC_V_WRONG_PTR 5     /* zero-copy producer took an address not published for its step */
@@ -56,7 +61,7 @@ extern "C" {
 /* deliberate protocol mistakes, for the tests that prove the enumerator catches them */
 #define ORC_MUT_NONE 0
 #define ORC_MUT_WEAK_CREDIT 1 /* credit test admits nslots+1 steps in flight */
-#define ORC_MUT_EARLY_TAIL 2  /* SIMPLE: tail published before the slot is written */
+#define ORC_MUT_EARLY_TAIL 2  /* SIMPLE, ZCD: tail published before the chunk is written */
 #define ORC_MUT_NO_ACQUIRE 3  /* SIMPLE: consumer loads the slot before it checks tail */
 #define ORC_MUT_TORN_LINE 4   /* LL: flag and data halves of a line stored separately, flag first */
 #define ORC_MUT_ZC_NO_WAIT 5  /* ZC: receiver publishes without waiting for ptrExchange == 0 */

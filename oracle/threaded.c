@@ -22,7 +22,9 @@
  *  - Zero-copy: the receiver publishes the next destination whenever the
  *    word is 0 and publishes head once tail passes a step; the producer
  *    takes the address, clears the word, writes the chunk into B there and
- *    publishes tail.
+ *    publishes tail.  Zero-copy direct: the destination is known, so the
+ *    producer writes the chunk at its own offset of B and publishes tail,
+ *    and the receiver only answers tail with head.
  *
  * Each channel has two actors (producer; consumer or receiver).  Actors are
  * dealt round-robin to the threads; a thread sweeps its actors, each taking
@@ -172,14 +174,37 @@ static int try_zc_prod(const tconn* t, int ch, tside* s, const uint8_t* A, uint8
   return 1;
 }
 
+/* Zero-copy direct producer: the destination is known, so it writes the
+ * chunk at its own offset of B and publishes tail. */
+static int try_zcd_prod(const tconn* t, int ch, tside* s, const uint8_t* A, uint8_t* B) {
+  const orc_conn* c = t->c;
+  if (s->j == s->k) {
+    s->done = 1;
+    return 1;
+  }
+  const uint64_t off = s->beg + s->j * c->step_bytes;
+  memcpy(B + off, A + off, (size_t)chunk(c, s, s->j));
+  atomic_store_explicit(&t->tail[ch], s->base + s->j + 1, memory_order_release);
+  s->j++;
+  return 1;
+}
+
 static int prod_action(const tconn* t, int ch, tside* s, const uint8_t* A, uint8_t* B) {
-  return t->c->proto == ORC_ZC ? try_zc_prod(t, ch, s, A, B) : try_prod(t, ch, s, A);
+  switch (t->c->proto) {
+    case ORC_ZC:
+      return try_zc_prod(t, ch, s, A, B);
+    case ORC_ZCD:
+      return try_zcd_prod(t, ch, s, A, B);
+    default:
+      return try_prod(t, ch, s, A);
+  }
 }
 
 static int cons_action(const tconn* t, int ch, tside* s, uint8_t* B) {
   const orc_conn* c = t->c;
-  if (c->proto == ORC_ZC) {
+  if (c->proto == ORC_ZC || c->proto == ORC_ZCD) {
     int moved = 0;
+    if (c->proto == ORC_ZCD) s->npub = s->k; /* nothing to publish */
     if (s->npub < s->k && atomic_load_explicit(&t->ptrx[ch], memory_order_acquire) == 0) {
       atomic_store_explicit(&t->ptrx[ch], s->beg + s->npub * c->step_bytes + 1,
                             memory_order_release);
@@ -442,7 +467,7 @@ int orc_pingpong_threaded(orc_conn* fwd, orc_conn* rev, const uint8_t* a, uint8_
                           uint8_t* cbuf, uint64_t n, int iters, double* seconds) {
   if (!fwd || !rev || iters < 0 || fwd->nch != rev->nch || (n && (!a || !b || !cbuf)))
     return ORC_E_ARG;
-  if (fwd->proto == ORC_ZC || rev->proto == ORC_ZC) return ORC_E_ARG;
+  if (fwd->proto >= ORC_ZC || rev->proto >= ORC_ZC) return ORC_E_ARG;
   tconn tf, tr;
   int rc = tconn_init(&tf, fwd);
   if (!rc) rc = tconn_init(&tr, rev);

@@ -196,6 +196,11 @@ ConnArgs conn_args(const xfer_conn* c, const void* src, void* dst, uint64_t nbyt
   return a;
 }
 
+// Both zero-copy modes write straight into the destination: no FIFO.
+bool zero_copy(int proto) {
+  return proto == XFER_PROTO_ZEROCOPY || proto == XFER_PROTO_ZEROCOPY_DIRECT;
+}
+
 uint32_t wgs_of(const xfer_conn* c) { return uint32_t(c->nch) * uint32_t(c->lanes) * 2u; }
 
 // Launched grid.  Pairing keeps a pair (producer 2q, consumer 2q+1) on one
@@ -268,7 +273,7 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
                                    int fifo_loc, const xfer_attr* attr, xfer_conn** out) {
   if (!out) return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: out is NULL");
   *out = nullptr;
-  if (proto < XFER_PROTO_SIMPLE || proto > XFER_PROTO_ZEROCOPY)
+  if (proto < XFER_PROTO_SIMPLE || proto > XFER_PROTO_ZEROCOPY_DIRECT)
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: unknown protocol " + std::to_string(proto));
   if (nchannels < 1 || nchannels > 64)
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: nchannels must be in 1..64");
@@ -298,8 +303,8 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
   if (a.ordering != XFER_ORDER_COHERENT && a.ordering != XFER_ORDER_FENCED)
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: ordering must be COHERENT or FENCED");
   const size_t fifo_bytes =
-      proto == XFER_PROTO_ZEROCOPY ? 0 : size_t(nchannels) * size_t(nslots) * slot_bytes;
-  if (proto != XFER_PROTO_ZEROCOPY && fifo_bytes / size_t(nchannels) / size_t(nslots) != slot_bytes)
+      zero_copy(proto) ? 0 : size_t(nchannels) * size_t(nslots) * slot_bytes;
+  if (!zero_copy(proto) && fifo_bytes / size_t(nchannels) / size_t(nslots) != slot_bytes)
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: FIFO size overflows");
 
   xfer_conn* c = new (std::nothrow) xfer_conn();
@@ -612,7 +617,7 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
   rc = check_runnable(rev, "xfer_run_pingpong");
   if (rc) return rc;
   if (fwd == rev) return fail(XFER_ERR_INVALID_ARG, "xfer_run_pingpong: fwd and rev must differ");
-  if (fwd->proto == XFER_PROTO_ZEROCOPY || fwd->proto != rev->proto || fwd->nch != rev->nch ||
+  if (zero_copy(fwd->proto) || fwd->proto != rev->proto || fwd->nch != rev->nch ||
       fwd->slot_bytes != rev->slot_bytes || fwd->lanes != rev->lanes || fwd->block != rev->block ||
       fwd->ordering != rev->ordering || fwd->device != rev->device)
     return fail(XFER_ERR_INVALID_ARG,

@@ -687,6 +687,75 @@ __device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
   return true;
 }
 
+// ------------------------------------------------------- zero-copy direct
+// The destination is known before the launch ("zero copy" second kind on the
+// transfer page): no ptrExchange.  The producer writes step j's chunk at its
+// own offset of B, releases and publishes tail = g+1; pipelined like the
+// other producers when its share of a step fits one register batch.
+template <int SC, int ORD, bool AL>
+__device__ bool zcd_send(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
+                         const uint8_t* src, uint8_t* dst, uint64_t ticks, Shared& sh) {
+  using O = Order<SC, ORD>;
+  const uint64_t S = A.step_bytes;
+  const uint32_t P = A.lanes;
+  if (ORD == kOrdCoherent && lane_blocks<true>(S, P) <= kUnroll) {
+    Batch b;
+    batch_load<kPolNT, true>(b, src + sd.r.beg, chunk_len(sd, S, 0), S, P, w);
+    for (uint64_t j = 0; j < sd.r.k; ++j) {
+      const uint64_t g = g0 + j;
+      uint8_t* p = dst + sd.r.beg + j * S;
+      const uint32_t L = chunk_len(sd, S, j);
+      batch_store<O::kShared, true>(b, p, L, S, P, w);
+      lane_tail<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, p, L, S, P, w);
+      if (j + 1 < sd.r.k) {
+        batch_load<kPolNT, true>(b, src + sd.r.beg + (j + 1) * S, chunk_len(sd, S, j + 1), S, P, w);
+        wait_vmcnt<kUnroll>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      if (wg_failed(sh, 0, A.status)) return false;
+      if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
+    }
+    return true;
+  }
+  for (uint64_t j = 0; j < sd.r.k; ++j) {
+    const uint64_t g = g0 + j;
+    lane_copy<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, dst + sd.r.beg + j * S,
+                                        chunk_len(sd, S, j), S, P, w);
+    O::release();
+    if (wg_failed(sh, 0, A.status)) return false;
+    if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
+  }
+  return true;
+}
+
+// Receiver of zero-copy direct (one thread): answer tail with head until the
+// message's last step has landed.
+template <int SC, int ORD>
+__device__ bool zcd_recv(const ConnArgs& A, Side& sd, uint64_t g0, uint64_t ticks) {
+  if (threadIdx.x != 0) return true;
+  const uint64_t end = g0 + sd.r.k;
+  uint64_t done = g0;
+  Deadline dl(ticks, A.status);
+  while (done < end) {
+    const uint64_t t = ld_u64<SC>(&sd.lc->tail);
+    if (t > done) {
+      Order<SC, ORD>::acquire();
+      done = t;
+      st_u64<SC>(&sd.lc->head, t);
+      dl = Deadline(ticks, A.status);
+      continue;
+    }
+    const uint32_t e = dl.expired();
+    if (e) {
+      raise_err(A.status, e);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
 // The launch's messages of one connection, repeated `iters` times.
 template <int MAXB>
 struct MsgList {
@@ -825,6 +894,10 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
       if constexpr (PROTO == kProtoSimple)
         ok = role == 0 ? simple_send<SC, ORD, AL>(A, c, w, sd, g0, A.src + md.off, ticks, sh)
                        : simple_recv<SC, ORD, AL>(A, c, w, sd, g0, A.dst + md.off, ticks, sh);
+      else if constexpr (PROTO == kProtoZCD)
+        ok = role == 0
+                 ? zcd_send<SC, ORD, AL>(A, w, sd, g0, A.src + md.off, A.dst + md.off, ticks, sh)
+                 : zcd_recv<SC, ORD>(A, sd, g0, ticks);
       else if constexpr (PROTO == kProtoLL)
         ok = role == 0 ? ll_send<SC, ORD, AL>(A, c, w, sd, g0, A.src + md.off, ticks, sh)
                        : ll_recv<SC, ORD, AL>(A, c, w, sd, g0, A.dst + md.off, ticks, sh);
@@ -914,6 +987,7 @@ RunFn<MAXB> pick_run(const Variant& v) {
   switch (v.proto) {
     case kProtoSimple: return pick_run_sc<MAXB, kProtoSimple>(v);
     case kProtoLL: return pick_run_sc<MAXB, kProtoLL>(v);
+    case kProtoZCD: return pick_run_sc<MAXB, kProtoZCD>(v);
     default: return pick_run_sc<MAXB, kProtoZC>(v);
   }
 }

@@ -32,7 +32,7 @@ struct alignas(128) Status {
   uint32_t pad1[31];
 };
 
-enum : uint32_t { kProtoSimple = 0, kProtoLL = 1, kProtoZC = 2 };
+enum : uint32_t { kProtoSimple = 0, kProtoLL = 1, kProtoZC = 2, kProtoZCD = 3 };
 enum : int { kScopeAgent = 0, kScopeSystem = 1 };
 
 // Device view of one connection for one run.

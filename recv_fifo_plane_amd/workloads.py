@@ -6,7 +6,8 @@ W2  LL, 1 channel, 8 x 32 KiB, messages 8 B .. 64 KiB, in-kernel ping-pong.
 W3  SIMPLE, 32 channels x 8 x 512 KiB HBM, 1 GiB, 4 workgroups per channel side.
 W4  zero-copy through ptrExchange: one pair on 128 MiB, and a ring of 8
     logical endpoints built by the host schedule, endpoint r sending its
-    128 MiB slice to (r + 1) mod 8, all edges in one launch.
+    128 MiB slice to (r + 1) mod 8, all edges in one launch.  W4D: the same
+    with the destination known before the launch (zero-copy direct).
 W5  host FIFO: 16 channels x 8 x 256 KiB in pinned host memory, 2 GiB of
     messages with log-uniform sizes 1 KiB .. 64 MiB at consecutive offsets;
     the head/tail words sit in HBM, next to the side that polls them.
@@ -32,8 +33,14 @@ W4_RING = dict(name="zc_ring_8x128MiB", proto="zc", endpoints=8, channels_per_ed
                nslots=1, slot_bytes=512 << 10, fifo_loc="device", wgs_per_channel=4,
                block_threads=512, slice_bytes=128 << 20, max_peers=128)
 
+# The same two zero-copy workloads with the destination known before the
+# launch (no ptrExchange hand-off); the ring's launch shape was swept apart.
+W4D_PAIR = dict(W4_PAIR, name="zcd_pair_128MiB", proto="zcd")
+W4D_RING = dict(W4_RING, name="zcd_ring_8x128MiB", proto="zcd", wgs_per_channel=16,
+                block_threads=128)
+
 W5 = dict(name="host_fifo_16ch_2GiB", proto="simple", nchannels=16, nslots=8,
-          slot_bytes=256 << 10, fifo_loc="host", wgs_per_channel=8, block_threads=512,
+          slot_bytes=256 << 10, fifo_loc="host", wgs_per_channel=8, block_threads=1024,
           ctrl_loc=1, total_bytes=2 << 30)
 
 _ATTRS = ("wgs_per_channel", "block_threads", "ctrl_loc", "timeout_ms", "xcd_pairing", "ordering")

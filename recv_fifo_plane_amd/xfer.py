@@ -26,6 +26,7 @@ XFER_ERR_STATE = 8
 XFER_PROTO_SIMPLE = 0
 XFER_PROTO_LL = 1
 XFER_PROTO_ZEROCOPY = 2
+XFER_PROTO_ZEROCOPY_DIRECT = 3
 XFER_FIFO_DEVICE = 0
 XFER_FIFO_HOST = 1
 XFER_CTRL_DEFAULT = 0
@@ -39,7 +40,8 @@ XFER_OP_CONNECT_BATCH = 2
 XFER_MAX_BATCH = 16
 
 PROTOS = {"simple": XFER_PROTO_SIMPLE, "ll": XFER_PROTO_LL, "zc": XFER_PROTO_ZEROCOPY,
-          "zerocopy": XFER_PROTO_ZEROCOPY}
+          "zerocopy": XFER_PROTO_ZEROCOPY, "zcd": XFER_PROTO_ZEROCOPY_DIRECT,
+          "zerocopy_direct": XFER_PROTO_ZEROCOPY_DIRECT}
 FIFO_LOCS = {"device": XFER_FIFO_DEVICE, "host": XFER_FIFO_HOST}
 
 

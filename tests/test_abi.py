@@ -37,13 +37,15 @@ def test_library_exports_every_declared_symbol():
 
 
 @pytest.mark.parametrize("args", [
-    (3, 1, 8, 128, 0),          # unknown protocol
+    (4, 1, 8, 128, 0),          # unknown protocol
+    (-1, 1, 8, 128, 0),         # unknown protocol
     (0, 0, 8, 128, 0),          # no channels
     (0, 65, 8, 128, 0),         # too many channels (64-bit masks)
     (0, 1, 0, 128, 0),          # no slots
     (0, 1, 8, 24, 0),           # SIMPLE slot not a multiple of 16
     (1, 1, 8, 12, 0),           # LL slot not a multiple of 8
     (2, 1, 8, 8, 0),            # zero-copy step not a multiple of 16
+    (3, 1, 8, 8, 0),            # zero-copy direct step not a multiple of 16
     (0, 1, 8, 128, 2),          # unknown FIFO location
 ])
 def test_create_rejects_bad_arguments(args):

@@ -19,8 +19,8 @@ def _bufs(n):
                                                                           device="cuda")
 
 
-@pytest.mark.parametrize("proto", ["simple", "ll", "zc"])
-@pytest.mark.parametrize("roles", [1, 2])
+@pytest.mark.parametrize("proto,roles", [("simple", 1), ("simple", 2), ("ll", 1), ("ll", 2),
+                                         ("zc", 1), ("zc", 2), ("zcd", 2)])
 def test_lone_side_times_out(proto, roles):
     import torch
     log("case: lone side %s roles=%d" % (proto, roles))
@@ -39,7 +39,23 @@ def test_lone_side_times_out(proto, roles):
     c.close()
 
 
-@pytest.mark.parametrize("proto", ["simple", "ll", "zc"])
+def test_lone_direct_zero_copy_producer_needs_no_receiver():
+    # the destination is known before the launch: the producer writes every
+    # step and publishes tail without waiting for its receiver
+    import torch
+    c = xf.Conn("zcd", 2, 1, 4096, timeout_ms=20, roles=1)
+    a, b = _bufs(1 << 16)
+    a.copy_(torch.arange(1 << 16, device="cuda").to(torch.uint8))
+    c.run(a, b, 1 << 16)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    for ch in range(2):
+        st = c.query(ch)
+        assert st["error"] == 0 and st["tail"] == 8 and st["head"] == 0
+    c.close()
+
+
+@pytest.mark.parametrize("proto", ["simple", "ll", "zc", "zcd"])
 def test_abort_word_ends_waits(proto):
     import torch
     log("case: abort %s" % proto)

@@ -119,6 +119,8 @@ CASES = [
     ("ll", 5, 1, 8, [100, 3]),
     ("zc", 1, 8, 64, [1000, 1]),
     ("zc", 3, 1, 16, [555, 16, 0]),
+    ("zcd", 1, 8, 64, [1000, 1]),
+    ("zcd", 3, 1, 16, [555, 16, 0]),
 ]
 
 
@@ -142,7 +144,7 @@ def test_counters_result_and_fifo_by_replay(proto, nch, nslots, slot_bytes, size
         st = conn.state(c)
         assert st["head"] == st["tail"] == st["steps"] == base[c]
         assert st["ptr_exchange"] == 0
-        if pid == oracle.ZC:
+        if pid in (oracle.ZC, oracle.ZCD):
             assert conn.fifo(c).size == 0
         else:
             assert bytes(conn.fifo(c)) == bytes(fifo[c])
@@ -174,7 +176,7 @@ def test_ll_lines_interleave_payload_and_step_flags():
 
 
 @pytest.mark.parametrize("proto,slot_sizes", [("simple", [16, 32, 48]), ("ll", [8, 24]),
-                                              ("zc", [16, 48])])
+                                              ("zc", [16, 48]), ("zcd", [16, 48])])
 def test_edge_sizes_brute_force(proto, slot_sizes):
     pid = oracle.PROTO_NAMES[proto]
     for slot_bytes in slot_sizes:
@@ -210,7 +212,7 @@ def test_pingpong_composes_two_connections():
 
 # ------------------------------------------------------------ interleavings
 ENUM_CASES = []
-for _p, _slots in (("simple", (16, 32)), ("ll", (8, 16)), ("zc", (16,))):
+for _p, _slots in (("simple", (16, 32)), ("ll", (8, 16)), ("zc", (16,)), ("zcd", (16,))):
     for _ns in (1, 2, 3):
         for _sb in _slots:
             for _nch in (1, 2):
@@ -246,6 +248,7 @@ MUTATION_CASES = [
     ("ll", "early_head", {"overwrite", "deadlock"}),
     ("zc", "zc_no_wait", {"wrong_ptr"}),
     ("zc", "zc_no_reset", {"wrong_ptr", "counters"}),
+    ("zcd", "early_tail", {"read_unfilled"}),
 ]
 
 
@@ -261,7 +264,7 @@ def test_enumerator_catches_each_broken_rule(proto, mutation, expected, nslots):
 
 
 def test_correct_protocol_is_clean_under_the_same_inputs_as_the_mutations():
-    for proto in ("simple", "ll", "zc"):
+    for proto in ("simple", "ll", "zc", "zcd"):
         pid = oracle.PROTO_NAMES[proto]
         slot_bytes = 16 if pid != oracle.LL else 8
         S = oracle.step_bytes(pid, slot_bytes)
@@ -317,6 +320,6 @@ def test_enumerator_catches_broken_rules_under_take_ahead(mutation, expected):
 
 def test_conn_rejects_bad_shapes():
     for args in [("simple", 0, 8, 16), ("simple", 65, 8, 16), ("simple", 1, 0, 16),
-                 ("simple", 1, 8, 24), ("ll", 1, 8, 12), ("zc", 1, 8, 8)]:
+                 ("simple", 1, 8, 24), ("ll", 1, 8, 12), ("zc", 1, 8, 8), ("zcd", 1, 8, 8)]:
         with pytest.raises(oracle.OracleError):
             oracle.Conn(*args)

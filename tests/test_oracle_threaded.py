@@ -21,6 +21,7 @@ CASES = [
     ("simple", 1, 1, 16), ("simple", 3, 2, 64), ("simple", 8, 4, 4096), ("simple", 16, 8, 1024),
     ("ll", 1, 1, 8), ("ll", 2, 3, 64), ("ll", 8, 4, 2048),
     ("zc", 1, 1, 16), ("zc", 4, 1, 256), ("zc", 16, 1, 4096),
+    ("zcd", 1, 1, 16), ("zcd", 4, 1, 256), ("zcd", 16, 1, 4096),
 ]
 
 

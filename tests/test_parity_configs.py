@@ -82,13 +82,14 @@ def test_w3_simple_32_channels_1gib():
     conn.close()
 
 
-def test_w4_zero_copy_single_pair():
+@pytest.mark.parametrize("proto", ["zc", "zcd"])
+def test_w4_zero_copy_single_pair(proto):
     torch = _torch()
-    cfg = W.W4_PAIR
+    cfg = W.W4_PAIR if proto == "zc" else W.W4D_PAIR
     log("case: W4 pair " + str(cfg))
     A = synth.fp32_uniform_bytes(cfg["nbytes"], synth.workload_seed(4))
     conn = W.make_conn(cfg)
-    ocn = oracle.Conn("zc", cfg["nchannels"], 1, cfg["slot_bytes"])
+    ocn = oracle.Conn(proto, cfg["nchannels"], 1, cfg["slot_bytes"])
     a = to_dev(A)
     b = torch.zeros_like(a)
     conn.run(a, b, A.size)
@@ -100,9 +101,10 @@ def test_w4_zero_copy_single_pair():
     conn.close()
 
 
-def test_w4_eight_endpoint_ring():
+@pytest.mark.parametrize("proto", ["zc", "zcd"])
+def test_w4_eight_endpoint_ring(proto):
     torch = _torch()
-    cfg = W.W4_RING
+    cfg = W.W4_RING if proto == "zc" else W.W4D_RING
     n = cfg["endpoints"]
     log("case: W4 ring " + str(cfg))
     ring = W.make_ring(cfg)
@@ -116,7 +118,7 @@ def test_w4_eight_endpoint_ring():
     S = cfg["slice_bytes"]
     for r in range(n):
         d = (r + 1) % n
-        ocn = oracle.Conn("zc", cfg["channels_per_edge"], 1, cfg["slot_bytes"])
+        ocn = oracle.Conn(proto, cfg["channels_per_edge"], 1, cfg["slot_bytes"])
         Bd = np.zeros(S, dtype=np.uint8)
         ocn.run(np.ascontiguousarray(A[r * S:(r + 1) * S]), Bd)
         assert np.array_equal(got[d * S:(d + 1) * S], Bd), ("edge", r, d)

@@ -14,7 +14,7 @@ def _sizes(n, total, seed, lo=0, hi=16):
 
 
 @pytest.mark.parametrize("fifo_loc", ["device", "host"])
-@pytest.mark.parametrize("proto", ["simple", "ll", "zc"])
+@pytest.mark.parametrize("proto", ["simple", "ll", "zc", "zcd"])
 def test_message_list_matches_separate_transfers(proto, fifo_loc):
     sizes = _sizes(300, 6 << 20, 11, lo=0, hi=17)  # > 128 messages: several launches
     sizes[3] = 0  # a zero-size message is skipped
@@ -27,6 +27,7 @@ def test_message_list_shapes(lanes, block):
     sizes = [1, 15, 16, 17, 4095, 100_003, 1 << 20, 7, (1 << 20) + 9]
     run_message_list("simple", 8, 2, 64 << 10, sizes, lanes=lanes, block=block, base_off=0)
     run_message_list("zc", 8, 1, 64 << 10, sizes, lanes=lanes, block=block, base_off=5)
+    run_message_list("zcd", 8, 1, 64 << 10, sizes, lanes=lanes, block=block, base_off=7)
 
 
 def test_message_list_rejects_bad_arguments():

@@ -23,13 +23,14 @@ def test_ll(fifo_loc, nch, nslots, lanes):
     run_transfers("ll", nch, nslots, 2048, SIZES, fifo_loc=fifo_loc, lanes=lanes, kind="int32")
 
 
+@pytest.mark.parametrize("proto", ["zc", "zcd"])
 @pytest.mark.parametrize("fifo_loc", ["device", "host"])
 @pytest.mark.parametrize("nch,lanes", [(1, 1), (2, 2), (4, 3)])
-def test_zerocopy(fifo_loc, nch, lanes):
-    run_transfers("zc", nch, 8, 4096, SIZES, fifo_loc=fifo_loc, lanes=lanes)
+def test_zerocopy(proto, fifo_loc, nch, lanes):
+    run_transfers(proto, nch, 8, 4096, SIZES, fifo_loc=fifo_loc, lanes=lanes)
 
 
-@pytest.mark.parametrize("proto", ["simple", "ll", "zc"])
+@pytest.mark.parametrize("proto", ["simple", "ll", "zc", "zcd"])
 @pytest.mark.parametrize("src_off,dst_off", [(1, 0), (0, 3), (5, 11), (8, 8), (15, 1)])
 def test_misaligned(proto, src_off, dst_off):
     run_transfers(proto, 2, 3, 512, [1, 100, 5000, 33333], src_off=src_off, dst_off=dst_off,
@@ -38,13 +39,13 @@ def test_misaligned(proto, src_off, dst_off):
 
 @pytest.mark.parametrize("block", [64, 512, 1024])
 def test_block_sizes(block):
-    for proto in ("simple", "ll", "zc"):
+    for proto in ("simple", "ll", "zc", "zcd"):
         run_transfers(proto, 2, 4, 8192, [100_000, 7], block=block, lanes=2)
 
 
 @pytest.mark.parametrize("ctrl_loc", [1, 2])
 def test_control_words_either_side(ctrl_loc):
-    for proto in ("simple", "ll", "zc"):
+    for proto in ("simple", "ll", "zc", "zcd"):
         for fifo_loc in ("device", "host"):
             run_transfers(proto, 2, 2, 1024, [20_000, 3], fifo_loc=fifo_loc, ctrl_loc=ctrl_loc)
 
@@ -52,12 +53,12 @@ def test_control_words_either_side(ctrl_loc):
 @pytest.mark.parametrize("xcd_pairing", [-1, 1])
 def test_xcd_pairing_either_way(xcd_pairing):
     # 8 channels x 1 lane -> 16 workgroups: the pairing remap is active when on
-    for proto in ("simple", "ll", "zc"):
+    for proto in ("simple", "ll", "zc", "zcd"):
         run_transfers(proto, 8, 2, 4096, [1 << 20, 4097], xcd_pairing=xcd_pairing)
 
 
 @pytest.mark.parametrize("fifo_loc", ["device", "host"])
-@pytest.mark.parametrize("proto", ["simple", "ll", "zc"])
+@pytest.mark.parametrize("proto", ["simple", "ll", "zc", "zcd"])
 def test_fenced_ordering(proto, fifo_loc):
     # the scoped-fence ordering must give the same bytes and counters
     run_transfers(proto, 3, 2, 4096, SIZES, fifo_loc=fifo_loc, lanes=2, ordering=1,
@@ -74,7 +75,7 @@ def test_many_steps_through_few_slots():
         run_transfers(proto, 8, 2, 4096, [16 << 20], lanes=2, block=512)
 
 
-@pytest.mark.parametrize("proto", ["simple", "zc"])
+@pytest.mark.parametrize("proto", ["simple", "zc", "zcd"])
 @pytest.mark.parametrize("src_off,dst_off", [(3, 7), (1, 1), (0, 9), (12, 0)])
 def test_misaligned_large_pipelined(proto, src_off, dst_off):
     # lane slices that fit one register batch take the pipelined producer
