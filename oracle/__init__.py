@@ -20,9 +20,9 @@ SRCS = [os.path.join(HERE, f) for f in ("oracle.c", "threaded.c", "oracle.h",
                                         "oracle_internal.h")]
 LIB = os.path.join(HERE, "liboracle.so")
 
-SIMPLE, LL, ZC, ZCD = 0, 1, 2, 3
+SIMPLE, LL, ZC, ZCD, RELAY = 0, 1, 2, 3, 4
 PROTO_NAMES = {"simple": SIMPLE, "ll": LL, "zc": ZC, "zerocopy": ZC, "zcd": ZCD,
-               "zerocopy_direct": ZCD}
+               "zerocopy_direct": ZCD, "relay": RELAY}
 
 OP_RECV_SETUP, OP_SEND_SETUP, OP_CONNECT_BATCH = 0, 1, 2
 
@@ -42,6 +42,7 @@ MUT = {
     "zc_no_reset": 6,
     "early_head": 7,
     "zc_ahead_past_end": 8,
+    "relay_early": 9,
 }
 VIOLATIONS = {
     0: "ok",
@@ -117,6 +118,9 @@ def lib():
             L.orc_conn_state.argtypes = [vp, C.c_int, u64p]
             L.orc_conn_fifo.argtypes = [vp, C.c_int, u64p]
             L.orc_conn_fifo.restype = vp
+            L.orc_conn_fifo_ex.argtypes = [vp, C.c_int, C.c_int, u64p]
+            L.orc_conn_fifo_ex.restype = vp
+            L.orc_conn_relay_state.argtypes = [vp, C.c_int, u64p]
             L.orc_enumerate.argtypes = [C.c_int, C.c_int, C.c_int, C.c_uint64, vp, C.c_uint64,
                                         C.c_int, C.c_int, C.c_int, C.c_uint64,
                                         C.POINTER(_EnumResult)]
@@ -239,9 +243,17 @@ class Conn:
         _check(lib().orc_conn_state(self._h, channel, out), "orc_conn_state")
         return {"head": out[0], "tail": out[1], "ptr_exchange": out[2], "steps": out[3]}
 
-    def fifo(self, channel: int) -> np.ndarray:
+    def relay_state(self, channel: int) -> dict:
+        """Relay connections: the send proxy's and the receive proxy's tails."""
+        out = (C.c_uint64 * 2)()
+        _check(lib().orc_conn_relay_state(self._h, channel, out), "orc_conn_relay_state")
+        return {"send_proxy_tail": out[0], "recv_proxy_tail": out[1]}
+
+    def fifo(self, channel: int, which: int = 0) -> np.ndarray:
+        """FIFO bytes of a channel; relay connections: which = 0 send, 1 staging,
+        2 receive."""
         n = C.c_uint64()
-        p = lib().orc_conn_fifo(self._h, channel, C.byref(n))
+        p = lib().orc_conn_fifo_ex(self._h, int(which), channel, C.byref(n))
         if not p:
             return np.zeros(0, dtype=np.uint8)
         return np.ctypeslib.as_array((C.c_uint8 * n.value).from_address(p)).copy()

@@ -50,6 +50,14 @@
  *      receiver, seeing tail > g, publishes head = g+1.
  *  R8  The step base persists across transfers on one connection; a step
  *      never spans two transfers.
+ *  R9  Copy-engine relay (ORC_RELAY; the shm transport's "useMemcpy" mode on
+ *      the transfer page): the producer fills the send FIFO and publishes
+ *      tail; a send proxy, seeing tail > g, copies slot g into a host staging
+ *      FIFO and publishes its own tail; a receive proxy, seeing that, copies
+ *      the staging slot into the receive FIFO and publishes a third tail; the
+ *      consumer drains the receive FIFO once that tail passes g and publishes
+ *      head, which is the producer's credit end to end.  All three FIFOs
+ *      have nslots slots of slot_bytes; a proxy copies exactly the chunk.
  */
 #include "oracle.h"
 #include "oracle_internal.h"
@@ -149,11 +157,14 @@ int orc_partition(uint64_t n, int nch, uint64_t* beg, uint64_t* len) {
 
 /* ------------------------------------------------------------ connection */
 
-/* Zero-copy modes write straight into B: no FIFO. */
-static int has_fifo(int proto) { return proto == ORC_SIMPLE || proto == ORC_LL; }
+/* FIFOs per channel: none for the zero-copy modes, three for the relay. */
+static int nfifos(int proto) {
+  return proto == ORC_RELAY ? 3 : (proto == ORC_SIMPLE || proto == ORC_LL) ? 1 : 0;
+}
+static int has_fifo(int proto) { return nfifos(proto) > 0; }
 
 orc_conn* orc_conn_new(int proto, int nch, int nslots, uint64_t slot_bytes) {
-  if (proto < ORC_SIMPLE || proto > ORC_ZCD || nch < 1 || nch > 64 || nslots < 1) return NULL;
+  if (proto < ORC_SIMPLE || proto > ORC_RELAY || nch < 1 || nch > 64 || nslots < 1) return NULL;
   if (proto == ORC_LL ? (slot_bytes < 8 || slot_bytes % 8) : (slot_bytes < 16 || slot_bytes % 16))
     return NULL;
   orc_conn* c = (orc_conn*)calloc(1, sizeof(*c));
@@ -164,7 +175,8 @@ orc_conn* orc_conn_new(int proto, int nch, int nslots, uint64_t slot_bytes) {
   c->slot_bytes = slot_bytes;
   c->step_bytes = orc_step_bytes(proto, slot_bytes);
   c->ctrl = (orc_ctrl*)calloc((size_t)nch, sizeof(orc_ctrl)); /* Reading R1: all zero */
-  if (has_fifo(proto)) c->fifo = (uint8_t*)calloc((size_t)nch * nslots, slot_bytes);
+  if (has_fifo(proto))
+    c->fifo = (uint8_t*)calloc((size_t)nfifos(proto) * nch * nslots, slot_bytes);
   if (!c->ctrl || (has_fifo(proto) && !c->fifo)) {
     orc_conn_free(c);
     return NULL;
@@ -196,13 +208,25 @@ int orc_conn_state(const orc_conn* c, int ch, uint64_t* out4) {
   return 0;
 }
 
-const uint8_t* orc_conn_fifo(const orc_conn* c, int ch, uint64_t* bytes) {
-  if (!c || ch < 0 || ch >= c->nch || !c->fifo) {
+const uint8_t* orc_conn_fifo_ex(const orc_conn* c, int which, int ch, uint64_t* bytes) {
+  if (!c || ch < 0 || ch >= c->nch || !c->fifo || which < 0 || which >= nfifos(c->proto)) {
     if (bytes) *bytes = 0;
     return NULL;
   }
-  if (bytes) *bytes = (uint64_t)c->nslots * c->slot_bytes;
-  return c->fifo + (uint64_t)ch * c->nslots * c->slot_bytes;
+  const uint64_t per = (uint64_t)c->nslots * c->slot_bytes;
+  if (bytes) *bytes = per;
+  return c->fifo + ((uint64_t)which * c->nch + (uint64_t)ch) * per;
+}
+
+const uint8_t* orc_conn_fifo(const orc_conn* c, int ch, uint64_t* bytes) {
+  return orc_conn_fifo_ex(c, 0, ch, bytes);
+}
+
+int orc_conn_relay_state(const orc_conn* c, int ch, uint64_t* out2) {
+  if (!c || ch < 0 || ch >= c->nch || !out2 || c->proto != ORC_RELAY) return ORC_E_ARG;
+  out2[0] = c->ctrl[ch].ytail;
+  out2[1] = c->ctrl[ch].gtail;
+  return 0;
 }
 
 /* ----------------------------------------------------------------- world
@@ -216,13 +240,15 @@ typedef struct {
   uint32_t pphase, pfinal;
   uint64_t cj, cline, cnpub;
   uint32_t cphase, pad;
+  uint64_t sj, rj; /* RELAY: next step of the send proxy and of the receive proxy */
 } orc_cur;
 
 typedef struct {
   const orc_conn* cfg;
   const uint8_t* A;
   uint64_t n;
-  uint8_t* meta; /* orc_ctrl[nch] | orc_cur[nch] | fill[nch*nslots] | drain[nch*nslots] | regs */
+  uint8_t* meta; /* orc_ctrl[nch] | orc_cur[nch] | fill[F][nch*nslots] | drain[F][nch*nslots] |
+                    regs, F = max(1, FIFOs) */
   uint64_t meta_bytes;
   uint8_t* fifo;
   uint8_t* B;
@@ -232,26 +258,28 @@ static orc_ctrl* W_ctrl(const world* w) { return (orc_ctrl*)w->meta; }
 static orc_cur* W_cur(const world* w) {
   return (orc_cur*)(w->meta + sizeof(orc_ctrl) * (size_t)w->cfg->nch);
 }
-/* step that last started filling each slot, -1 if none in this transfer */
-static int64_t* W_fill(const world* w) {
-  return (int64_t*)(w->meta + (sizeof(orc_ctrl) + sizeof(orc_cur)) * (size_t)w->cfg->nch);
+static int ntrack(const orc_conn* c) { return nfifos(c->proto) > 1 ? nfifos(c->proto) : 1; }
+/* step that last started filling each slot of FIFO f, -1 if none in this transfer */
+static int64_t* W_fill_in(const world* w, int f) {
+  return (int64_t*)(w->meta + (sizeof(orc_ctrl) + sizeof(orc_cur)) * (size_t)w->cfg->nch) +
+         (size_t)f * w->cfg->nch * w->cfg->nslots;
 }
-/* step whose payload was last drained from each slot, -1 if none */
-static int64_t* W_drain(const world* w) {
-  return W_fill(w) + (size_t)w->cfg->nch * w->cfg->nslots;
+/* step whose payload was last drained from each slot of FIFO f, -1 if none */
+static int64_t* W_drain_in(const world* w, int f) {
+  return W_fill_in(w, ntrack(w->cfg) + f);
 }
+static int64_t* W_fill(const world* w) { return W_fill_in(w, 0); }
 /* consumer registers of the NO_ACQUIRE mutation (one slot per channel) */
-static uint8_t* W_regs(const world* w) {
-  return (uint8_t*)(W_drain(w) + (size_t)w->cfg->nch * w->cfg->nslots);
-}
+static uint8_t* W_regs(const world* w) { return (uint8_t*)W_fill_in(w, 2 * ntrack(w->cfg)); }
 
 static uint64_t meta_size(const orc_conn* c) {
   return (sizeof(orc_ctrl) + sizeof(orc_cur)) * (uint64_t)c->nch +
-         2ull * sizeof(int64_t) * (uint64_t)c->nch * c->nslots + (uint64_t)c->nch * c->slot_bytes;
+         2ull * (uint64_t)ntrack(c) * sizeof(int64_t) * (uint64_t)c->nch * c->nslots +
+         (uint64_t)c->nch * c->slot_bytes;
 }
 
 static uint64_t fifo_size(const orc_conn* c) {
-  return has_fifo(c->proto) ? (uint64_t)c->nch * c->nslots * c->slot_bytes : 0;
+  return (uint64_t)nfifos(c->proto) * c->nch * c->nslots * c->slot_bytes;
 }
 
 /* Fills meta for a new transfer of n bytes; FIFO and B are set by the caller. */
@@ -271,9 +299,8 @@ static int world_begin(world* w, const orc_conn* c, const uint8_t* A, uint64_t n
     u[ch].k = (len[ch] + c->step_bytes - 1) / c->step_bytes;
     if (c->proto == ORC_LL && q[ch].base + u[ch].k > 0xFFFFFFFFull) return ORC_E_RANGE;
   }
-  int64_t* fill = W_fill(w);
-  int64_t* drain = W_drain(w);
-  for (int i = 0; i < c->nch * c->nslots; ++i) fill[i] = drain[i] = -1;
+  int64_t* fill = W_fill(w); /* every FIFO's fill and drain marks, contiguous */
+  for (int i = 0; i < 2 * ntrack(c) * c->nch * c->nslots; ++i) fill[i] = -1;
   return 0;
 }
 
@@ -282,10 +309,12 @@ static uint64_t chunk_len(const world* w, const orc_cur* u, uint64_t j) {
   return rest < S ? rest : S;
 }
 
-static uint8_t* slot_ptr(const world* w, int ch, uint64_t g) {
+static uint8_t* slot_ptr_in(const world* w, int f, int ch, uint64_t g) {
   const orc_conn* c = w->cfg;
-  return w->fifo + ((uint64_t)ch * c->nslots + g % (uint64_t)c->nslots) * c->slot_bytes;
+  return w->fifo + (((uint64_t)f * c->nch + (uint64_t)ch) * c->nslots + g % (uint64_t)c->nslots) *
+                       c->slot_bytes;
 }
+static uint8_t* slot_ptr(const world* w, int ch, uint64_t g) { return slot_ptr_in(w, 0, ch, g); }
 
 /* Reading R2: the credit test. */
 static int credit_ok(const world* w, const orc_ctrl* q, uint64_t g) {
@@ -293,21 +322,26 @@ static int credit_ok(const world* w, const orc_ctrl* q, uint64_t g) {
   return w->cfg->mutation == ORC_MUT_WEAK_CREDIT ? inflight <= ns : inflight < ns;
 }
 
-static int slot_free(const world* w, int ch, uint64_t g) {
-  size_t s = (size_t)ch * w->cfg->nslots + (size_t)(g % (uint64_t)w->cfg->nslots);
-  int64_t f = W_fill(w)[s];
-  return f < 0 || W_drain(w)[s] == f;
+static size_t slot_index(const world* w, int ch, uint64_t g) {
+  return (size_t)ch * w->cfg->nslots + (size_t)(g % (uint64_t)w->cfg->nslots);
 }
-
-static void mark_fill(const world* w, int ch, uint64_t g) {
-  W_fill(w)[(size_t)ch * w->cfg->nslots + (size_t)(g % (uint64_t)w->cfg->nslots)] = (int64_t)g;
+static int slot_free_in(const world* w, int f, int ch, uint64_t g) {
+  int64_t fl = W_fill_in(w, f)[slot_index(w, ch, g)];
+  return fl < 0 || W_drain_in(w, f)[slot_index(w, ch, g)] == fl;
 }
-static void mark_drain(const world* w, int ch, uint64_t g) {
-  W_drain(w)[(size_t)ch * w->cfg->nslots + (size_t)(g % (uint64_t)w->cfg->nslots)] = (int64_t)g;
+static void mark_fill_in(const world* w, int f, int ch, uint64_t g) {
+  W_fill_in(w, f)[slot_index(w, ch, g)] = (int64_t)g;
 }
-static int64_t fill_of(const world* w, int ch, uint64_t g) {
-  return W_fill(w)[(size_t)ch * w->cfg->nslots + (size_t)(g % (uint64_t)w->cfg->nslots)];
+static void mark_drain_in(const world* w, int f, int ch, uint64_t g) {
+  W_drain_in(w, f)[slot_index(w, ch, g)] = (int64_t)g;
 }
+static int64_t fill_of_in(const world* w, int f, int ch, uint64_t g) {
+  return W_fill_in(w, f)[slot_index(w, ch, g)];
+}
+static int slot_free(const world* w, int ch, uint64_t g) { return slot_free_in(w, 0, ch, g); }
+static void mark_fill(const world* w, int ch, uint64_t g) { mark_fill_in(w, 0, ch, g); }
+static void mark_drain(const world* w, int ch, uint64_t g) { mark_drain_in(w, 0, ch, g); }
+static int64_t fill_of(const world* w, int ch, uint64_t g) { return fill_of_in(w, 0, ch, g); }
 
 /* LL line helpers, Reading R4. */
 static uint64_t ll_lines(uint64_t L) { return (L + 3) / 4; }
@@ -326,7 +360,7 @@ static uint32_t get32(const uint8_t* p) {
 }
 
 /* ------------------------------------------------------------------ actors */
-enum { ACT_PROD = 0, ACT_CONS = 1, ACT_PUB = 2, N_ACT = 3 };
+enum { ACT_PROD = 0, ACT_CONS = 1, ACT_PUB = 2, ACT_SPROXY = 3, ACT_RPROXY = 4, N_ACT = 5 };
 
 /* Whether the ZC producer, having written step pj, takes step pj+1's
  * address before it publishes tail (the kernels' pipelined order). */
@@ -342,6 +376,7 @@ static int prod_enabled(const world* w, int ch) {
   uint64_t g = q->base + u->pj;
   switch (c->proto) {
     case ORC_SIMPLE:
+    case ORC_RELAY:
       return u->pj < u->k && (u->pphase != 0 || credit_ok(w, q, g));
     case ORC_LL:
       if (u->pj == u->k) return !u->pfinal;
@@ -372,6 +407,8 @@ static int cons_enabled(const world* w, int ch) {
       const uint8_t* line = slot_ptr(w, ch, g) + 8 * u->cline;
       return get32(line + 4) == (uint32_t)(g + 1);
     }
+    case ORC_RELAY: /* the receive proxy's tail */
+      return u->cphase == 0 ? q->gtail > g : 1;
     default: /* ORC_ZC and ORC_ZCD receiver, completion cursor */
       return q->tail > g;
   }
@@ -385,9 +422,25 @@ static int pub_enabled(const world* w, int ch) {
   return u->cnpub < u->k && (c->mutation == ORC_MUT_ZC_NO_WAIT || q->ptrx == 0);
 }
 
+/* RELAY proxies: the send proxy moves step g once tail > g, the receive
+ * proxy once the send proxy's tail > g. */
+static int proxy_enabled(const world* w, int ch, int act) {
+  const orc_conn* c = w->cfg;
+  if (c->proto != ORC_RELAY) return 0;
+  const orc_ctrl* q = &W_ctrl(w)[ch];
+  const orc_cur* u = &W_cur(w)[ch];
+  if (act == ACT_SPROXY)
+    return u->sj < u->k && (c->mutation == ORC_MUT_RELAY_EARLY || q->tail > q->base + u->sj);
+  return u->rj < u->k && q->ytail > q->base + u->rj;
+}
+
 static int enabled(const world* w, int ch, int act) {
-  return act == ACT_PROD ? prod_enabled(w, ch) : act == ACT_CONS ? cons_enabled(w, ch)
-                                                                  : pub_enabled(w, ch);
+  switch (act) {
+    case ACT_PROD: return prod_enabled(w, ch);
+    case ACT_CONS: return cons_enabled(w, ch);
+    case ACT_PUB: return pub_enabled(w, ch);
+    default: return proxy_enabled(w, ch, act);
+  }
 }
 
 /* SIMPLE producer of step g: copy the chunk into slot g mod nslots, then
@@ -632,7 +685,47 @@ static int zcd_prod(world* w, int ch) {
   return 0;
 }
 
+/* RELAY proxy step: copy the chunk of step g from FIFO `from` to FIFO `to`
+ * (the slot there must be free: its previous step drained), then publish
+ * the proxy's tail = g+1. */
+static int relay_move(world* w, int ch, int from, int to, uint64_t* cursor, uint64_t* tail_out) {
+  const orc_ctrl* q = &W_ctrl(w)[ch];
+  orc_cur* u = &W_cur(w)[ch];
+  uint64_t g = q->base + *cursor;
+  if (fill_of_in(w, from, ch, g) != (int64_t)g) return ORC_V_READ_UNFILLED;
+  if (!slot_free_in(w, to, ch, g)) return ORC_V_OVERWRITE;
+  memcpy(slot_ptr_in(w, to, ch, g), slot_ptr_in(w, from, ch, g), (size_t)chunk_len(w, u, *cursor));
+  mark_drain_in(w, from, ch, g);
+  mark_fill_in(w, to, ch, g);
+  *tail_out = g + 1;
+  (*cursor)++;
+  return 0;
+}
+
+/* RELAY consumer: once the receive proxy's tail passes g, copy receive slot
+ * g into B, then publish head = g+1 (the producer's credit). */
+static int relay_cons(world* w, int ch) {
+  const orc_conn* c = w->cfg;
+  orc_ctrl* q = &W_ctrl(w)[ch];
+  orc_cur* u = &W_cur(w)[ch];
+  uint64_t g = q->base + u->cj;
+  if (u->cphase == 0) {
+    if (fill_of_in(w, 2, ch, g) != (int64_t)g) return ORC_V_READ_UNFILLED;
+    memcpy(w->B + u->beg + u->cj * c->step_bytes, slot_ptr_in(w, 2, ch, g),
+           (size_t)chunk_len(w, u, u->cj));
+    mark_drain_in(w, 2, ch, g);
+    u->cphase = 1;
+  } else {
+    q->head = g + 1;
+    u->cphase = 0;
+    u->cj++;
+  }
+  return 0;
+}
+
 static int fire(world* w, int ch, int act, uint64_t budget) {
+  orc_ctrl* rq = &W_ctrl(w)[ch];
+  orc_cur* ru = &W_cur(w)[ch];
   switch (w->cfg->proto) {
     case ORC_SIMPLE:
       return act == ACT_PROD ? simple_prod(w, ch) : simple_cons(w, ch);
@@ -640,6 +733,13 @@ static int fire(world* w, int ch, int act, uint64_t budget) {
       return act == ACT_PROD ? ll_prod(w, ch, budget) : ll_cons(w, ch, budget);
     case ORC_ZCD:
       return act == ACT_PROD ? zcd_prod(w, ch) : zc_done(w, ch);
+    case ORC_RELAY:
+      switch (act) {
+        case ACT_PROD: return simple_prod(w, ch);
+        case ACT_CONS: return relay_cons(w, ch);
+        case ACT_SPROXY: return relay_move(w, ch, 0, 1, &ru->sj, &rq->ytail);
+        default: return relay_move(w, ch, 1, 2, &ru->rj, &rq->gtail);
+      }
     default:
       return act == ACT_PROD ? zc_prod(w, ch) : act == ACT_PUB ? zc_pub(w, ch) : zc_done(w, ch);
   }
@@ -662,6 +762,7 @@ static int world_done(const world* w) {
   for (int ch = 0; ch < c->nch; ++ch) {
     if (u[ch].pj != u[ch].k || u[ch].cj != u[ch].k) return 0;
     if (c->proto == ORC_LL && !u[ch].pfinal) return 0;
+    if (c->proto == ORC_RELAY && (u[ch].sj != u[ch].k || u[ch].rj != u[ch].k)) return 0;
   }
   return 1;
 }
@@ -672,7 +773,8 @@ static int final_counters_ok(const world* w, int* bad_ch) {
   const orc_cur* u = W_cur(w);
   for (int ch = 0; ch < w->cfg->nch; ++ch) {
     uint64_t want = q[ch].base + u[ch].k;
-    if (q[ch].head != want || q[ch].tail != want || q[ch].ptrx != 0) {
+    if (q[ch].head != want || q[ch].tail != want || q[ch].ptrx != 0 ||
+        (w->cfg->proto == ORC_RELAY && (q[ch].ytail != want || q[ch].gtail != want))) {
       *bad_ch = ch;
       return 0;
     }
@@ -710,7 +812,7 @@ int orc_run(orc_conn* c, const uint8_t* A, uint8_t* B, uint64_t n) {
   while (!world_done(&w)) {
     int moved = 0;
     for (int ch = 0; ch < c->nch && !rc; ++ch) {
-      static const int order[N_ACT] = {ACT_PROD, ACT_PUB, ACT_CONS};
+      static const int order[N_ACT] = {ACT_PROD, ACT_PUB, ACT_SPROXY, ACT_RPROXY, ACT_CONS};
       for (int a = 0; a < N_ACT && !rc; ++a) {
         if (!enabled(&w, ch, order[a])) continue;
         rc = fire(&w, ch, order[a], ~0ull);
@@ -825,7 +927,9 @@ static const char* vname(int v) {
 }
 
 static const char* aname(int act) {
-  return act == ACT_PROD ? "producer" : act == ACT_CONS ? "consumer" : "publisher";
+  static const char* names[N_ACT] = {"producer", "consumer", "publisher", "send proxy",
+                                     "receive proxy"};
+  return act >= 0 && act < N_ACT ? names[act] : "?";
 }
 
 typedef struct {

@@ -18,7 +18,10 @@
  *  - the LL idea of a completion flag carried inside the data
  *    ("RDMA and GPUDirect" series article, section 四.1, signalling option 2);
  *  - the host-silent post/poll steady state ("Intra-Node Transport (P2P)",
- *    section 4, "POST / POLL").
+ *    section 4, "POST / POLL");
+ *  - the copy-engine relay of the shm transport's "useMemcpy" mode on the
+ *    transfer page: host proxy threads move each step from the send FIFO to a
+ *    host staging FIFO and on to the receive FIFO with memory copies.
  *
  * Readings of what the pages leave open are listed in the implementation
  * file next to the code that takes them.
@@ -37,6 +40,7 @@ extern "C" {
 #define ORC_LL 1
 #define ORC_ZC 2
 #define ORC_ZCD 3 /* zero-copy with the destination known before the launch (no ptrExchange) */
+#define ORC_RELAY 4 /* SIMPLE relayed by host proxies: send FIFO -> staging FIFO -> receive FIFO */
 
 /* error returns (negative) */
 #define ORC_E_ARG (-1)
@@ -69,6 +73,7 @@ extern "C" {
 #define ORC_MUT_EARLY_HEAD 7  /* SIMPLE/LL: consumer frees the slot (head) before reading it */
 #define ORC_MUT_ZC_AHEAD_PAST_END 8 /* ZC take-ahead order: also waits for an address after the
                                        transfer's last step */
+#define ORC_MUT_RELAY_EARLY 9 /* RELAY: the send proxy copies a slot without waiting for tail */
 
 /* producer program orders: the pages' order, and the orders the GPU kernels
  * use where they differ from it (each must stay safe and confluent) */
@@ -105,9 +110,9 @@ int orc_run(orc_conn* c, const uint8_t* A, uint8_t* B, uint64_t n);
 int orc_run_pingpong(orc_conn* fwd, orc_conn* rev, const uint8_t* a, uint8_t* b, uint8_t* c,
                      uint64_t n, int iters);
 /* Threaded mode: the same transfer with the producer and consumer of every
- * channel as actors on nthreads real threads (1 .. 2 x channels; more are
- * clamped), handing off through C11 atomics.  Its end state must equal
- * orc_run's. */
+ * channel (and, for RELAY, its two proxies) as actors on nthreads real
+ * threads (1 .. the number of actors; more are clamped), handing off through
+ * C11 atomics.  Its end state must equal orc_run's. */
 int orc_run_threaded(orc_conn* c, const uint8_t* A, uint8_t* B, uint64_t n, int nthreads);
 /* Threaded ping-pong (SIMPLE or LL): endpoint X and endpoint Y on two
  * threads, pinned to two distinct cores when the process may use two;
@@ -117,6 +122,11 @@ int orc_pingpong_threaded(orc_conn* fwd, orc_conn* rev, const uint8_t* a, uint8_
 /* out = {head, tail, ptrExchange, steps (the persistent step base)} */
 int orc_conn_state(const orc_conn* c, int channel, uint64_t* out4);
 const uint8_t* orc_conn_fifo(const orc_conn* c, int channel, uint64_t* bytes);
+/* RELAY: FIFO `which` of a channel (0 send, 1 staging, 2 receive); for other
+ * modes which = 0 is the one FIFO */
+const uint8_t* orc_conn_fifo_ex(const orc_conn* c, int which, int channel, uint64_t* bytes);
+/* RELAY: out = {send proxy's tail, receive proxy's tail} of a channel */
+int orc_conn_relay_state(const orc_conn* c, int channel, uint64_t* out2);
 
 /* ---- exhaustive interleaving check ---- */
 typedef struct {

@@ -19,6 +19,11 @@
  *    each line until its flag is g+1 ("RDMA and GPUDirect" section 四.1,
  *    option 2) and then publishes head; the producer writes its final step
  *    count to tail once at the end (Reading R4).
+ *  - Copy-engine relay (the shm transport's useMemcpy mode): a send proxy,
+ *    seeing tail > g, copies send slot g into the staging FIFO and publishes
+ *    its tail; a receive proxy copies staging slot g into the receive FIFO
+ *    once that tail passes g and publishes its own tail, which the consumer
+ *    polls; head stays the producer's credit end to end.
  *  - Zero-copy: the receiver publishes the next destination whenever the
  *    word is 0 and publishes head once tail passes a step; the producer
  *    takes the address, clears the word, writes the chunk into B there and
@@ -26,10 +31,11 @@
  *    producer writes the chunk at its own offset of B and publishes tail,
  *    and the receiver only answers tail with head.
  *
- * Each channel has two actors (producer; consumer or receiver).  Actors are
- * dealt round-robin to the threads; a thread sweeps its actors, each taking
- * whatever action is ready without blocking, so any thread count from 1 to
- * 2 x channels makes progress.
+ * Each channel has two actors (producer; consumer or receiver), four for the
+ * relay (plus the two proxies).  Actors are dealt round-robin to the
+ * threads; a thread sweeps its actors, each taking whatever action is ready
+ * without blocking, so any thread count from 1 to the number of actors makes
+ * progress.
  */
 #define _GNU_SOURCE
 #include <pthread.h>
@@ -50,6 +56,8 @@ typedef struct {
   _Atomic uint64_t* head;
   _Atomic uint64_t* tail;
   _Atomic uint64_t* ptrx;
+  _Atomic uint64_t* ytail; /* relay: send proxy's tail */
+  _Atomic uint64_t* gtail; /* relay: receive proxy's tail */
 } tconn;
 
 /* One side's cursor over one channel of one transfer. */
@@ -72,11 +80,15 @@ static int tconn_init(tconn* t, const orc_conn* c) {
   t->head = calloc((size_t)c->nch, sizeof(*t->head));
   t->tail = calloc((size_t)c->nch, sizeof(*t->tail));
   t->ptrx = calloc((size_t)c->nch, sizeof(*t->ptrx));
-  if (!t->head || !t->tail || !t->ptrx) return ORC_E_NOMEM;
+  t->ytail = calloc((size_t)c->nch, sizeof(*t->ytail));
+  t->gtail = calloc((size_t)c->nch, sizeof(*t->gtail));
+  if (!t->head || !t->tail || !t->ptrx || !t->ytail || !t->gtail) return ORC_E_NOMEM;
   for (int ch = 0; ch < c->nch; ++ch) {
     atomic_init(&t->head[ch], c->ctrl[ch].head);
     atomic_init(&t->tail[ch], c->ctrl[ch].tail);
     atomic_init(&t->ptrx[ch], c->ctrl[ch].ptrx);
+    atomic_init(&t->ytail[ch], c->ctrl[ch].ytail);
+    atomic_init(&t->gtail[ch], c->ctrl[ch].gtail);
   }
   return 0;
 }
@@ -85,6 +97,8 @@ static void tconn_free(tconn* t) {
   free(t->head);
   free(t->tail);
   free(t->ptrx);
+  free(t->ytail);
+  free(t->gtail);
 }
 
 /* Cursors of every channel for a transfer of n bytes (Reading R6). */
@@ -105,9 +119,12 @@ static uint64_t chunk(const orc_conn* c, const tside* s, uint64_t j) {
   return rest < c->step_bytes ? rest : c->step_bytes;
 }
 
-static uint8_t* slot(const orc_conn* c, int ch, uint64_t g) {
-  return c->fifo + ((uint64_t)ch * c->nslots + g % (uint64_t)c->nslots) * c->slot_bytes;
+/* Slot g of a channel in FIFO f (relay: 0 send, 1 staging, 2 receive). */
+static uint8_t* slot_in(const orc_conn* c, int f, int ch, uint64_t g) {
+  return c->fifo + (((uint64_t)f * c->nch + (uint64_t)ch) * c->nslots + g % (uint64_t)c->nslots) *
+                       c->slot_bytes;
 }
+static uint8_t* slot(const orc_conn* c, int ch, uint64_t g) { return slot_in(c, 0, ch, g); }
 
 /* Line value of `line` in a chunk of L bytes: data word in bytes 0..3 and the
  * flag in bytes 4..7, little-endian (Reading R4), as one 64-bit integer. */
@@ -143,7 +160,7 @@ static int try_prod(const tconn* t, int ch, tside* s, const uint8_t* A) {
   const uint8_t* src = A + s->beg + s->j * c->step_bytes;
   if (!credit(t, ch, g)) return 0;
   uint8_t* d = slot(c, ch, g);
-  if (c->proto == ORC_SIMPLE) {
+  if (c->proto == ORC_SIMPLE || c->proto == ORC_RELAY) {
     memcpy(d, src, (size_t)L);
     atomic_store_explicit(&t->tail[ch], g + 1, memory_order_release);
   } else {
@@ -230,6 +247,9 @@ static int cons_action(const tconn* t, int ch, tside* s, uint8_t* B) {
   if (c->proto == ORC_SIMPLE) {
     if (atomic_load_explicit(&t->tail[ch], memory_order_acquire) <= g) return 0;
     memcpy(dst, sl, (size_t)L);
+  } else if (c->proto == ORC_RELAY) {
+    if (atomic_load_explicit(&t->gtail[ch], memory_order_acquire) <= g) return 0;
+    memcpy(dst, slot_in(c, 2, ch, g), (size_t)L);
   } else {
     const uint32_t flag = (uint32_t)(g + 1);
     const uint64_t nl = (L + 3) / 4;
@@ -253,10 +273,27 @@ static int cons_action(const tconn* t, int ch, tside* s, uint8_t* B) {
   return 1;
 }
 
+/* Relay proxy: once `in` passes step g, copy slot g of FIFO `from` into
+ * FIFO `to` and publish `out` = g+1. */
+static int proxy_action(const tconn* t, int ch, tside* s, int from, int to, _Atomic uint64_t* in,
+                        _Atomic uint64_t* out) {
+  const orc_conn* c = t->c;
+  if (s->j == s->k) {
+    s->done = 1;
+    return 1;
+  }
+  const uint64_t g = s->base + s->j;
+  if (atomic_load_explicit(in, memory_order_acquire) <= g) return 0;
+  memcpy(slot_in(c, to, ch, g), slot_in(c, from, ch, g), (size_t)chunk(c, s, s->j));
+  atomic_store_explicit(out, g + 1, memory_order_release);
+  s->j++;
+  return 1;
+}
+
 /* ------------------------------------------------------------------ jobs */
 typedef struct {
   const tconn* t;
-  int ch, role; /* role 0: producer, 1: consumer / receiver */
+  int ch, role; /* 0: producer, 1: consumer / receiver, 2: send proxy, 3: receive proxy */
   tside* s;
   const uint8_t* A;
   uint8_t* B;
@@ -285,8 +322,17 @@ static void* worker(void* p) {
     for (int i = wa->id; i < jb->nactors; i += jb->nthreads) {
       actor* a = &jb->actors[i];
       if (a->s->done) continue;
-      int r = a->role == 0 ? prod_action(a->t, a->ch, a->s, a->A, a->B)
-                           : cons_action(a->t, a->ch, a->s, a->B);
+      int r;
+      switch (a->role) {
+        case 0: r = prod_action(a->t, a->ch, a->s, a->A, a->B); break;
+        case 1: r = cons_action(a->t, a->ch, a->s, a->B); break;
+        case 2:
+          r = proxy_action(a->t, a->ch, a->s, 0, 1, &a->t->tail[a->ch], &a->t->ytail[a->ch]);
+          break;
+        default:
+          r = proxy_action(a->t, a->ch, a->s, 1, 2, &a->t->ytail[a->ch], &a->t->gtail[a->ch]);
+          break;
+      }
       if (r < 0) {
         int zero = 0;
         atomic_compare_exchange_strong(&jb->err, &zero, -r);
@@ -338,6 +384,9 @@ static int end_state_ok(const tconn* t, const tside* prod, const tside* cons) {
     if (atomic_load(&t->head[ch]) != want || atomic_load(&t->tail[ch]) != want ||
         atomic_load(&t->ptrx[ch]) != 0 || cons[ch].j != cons[ch].k)
       return 0;
+    if (t->c->proto == ORC_RELAY &&
+        (atomic_load(&t->ytail[ch]) != want || atomic_load(&t->gtail[ch]) != want))
+      return 0;
   }
   return 1;
 }
@@ -347,33 +396,42 @@ static void commit(orc_conn* c, const tconn* t, const tside* prod) {
     c->ctrl[ch].head = atomic_load(&t->head[ch]);
     c->ctrl[ch].tail = atomic_load(&t->tail[ch]);
     c->ctrl[ch].ptrx = atomic_load(&t->ptrx[ch]);
+    c->ctrl[ch].ytail = atomic_load(&t->ytail[ch]);
+    c->ctrl[ch].gtail = atomic_load(&t->gtail[ch]);
     c->ctrl[ch].base = prod[ch].base + prod[ch].k; /* Reading R8 */
   }
 }
 
 int orc_run_threaded(orc_conn* c, const uint8_t* A, uint8_t* B, uint64_t n, int nthreads) {
   if (!c || (n && (!A || !B)) || nthreads < 1) return ORC_E_ARG;
-  if (nthreads > 2 * c->nch) nthreads = 2 * c->nch;
+  const int per_ch = c->proto == ORC_RELAY ? 4 : 2; /* actors per channel */
+  if (nthreads > per_ch * c->nch) nthreads = per_ch * c->nch;
   uint64_t base[64];
   for (int ch = 0; ch < c->nch; ++ch) base[ch] = c->ctrl[ch].base;
-  tside prod[64], cons[64];
+  tside prod[64], cons[64], sprx[64], rprx[64];
   sides_begin(prod, c, base, n);
   sides_begin(cons, c, base, n);
+  sides_begin(sprx, c, base, n);
+  sides_begin(rprx, c, base, n);
   if (c->proto == ORC_LL)
     for (int ch = 0; ch < c->nch; ++ch)
       if (base[ch] + prod[ch].k > 0xFFFFFFFFull) return ORC_E_RANGE;
   tconn t;
   int rc = tconn_init(&t, c);
-  actor actors[128];
+  actor actors[256];
   job jb;
   memset(&jb, 0, sizeof(jb));
   if (!rc) {
     for (int ch = 0; ch < c->nch; ++ch) {
-      actors[2 * ch] = (actor){&t, ch, 0, &prod[ch], A, B};
-      actors[2 * ch + 1] = (actor){&t, ch, 1, &cons[ch], A, B};
+      actors[per_ch * ch] = (actor){&t, ch, 0, &prod[ch], A, B};
+      actors[per_ch * ch + 1] = (actor){&t, ch, 1, &cons[ch], A, B};
+      if (per_ch == 4) {
+        actors[per_ch * ch + 2] = (actor){&t, ch, 2, &sprx[ch], A, B};
+        actors[per_ch * ch + 3] = (actor){&t, ch, 3, &rprx[ch], A, B};
+      }
     }
     jb.actors = actors;
-    jb.nactors = 2 * c->nch;
+    jb.nactors = per_ch * c->nch;
     jb.nthreads = nthreads;
     atomic_init(&jb.err, 0);
     atomic_init(&jb.actions, 0);
@@ -467,7 +525,7 @@ int orc_pingpong_threaded(orc_conn* fwd, orc_conn* rev, const uint8_t* a, uint8_
                           uint8_t* cbuf, uint64_t n, int iters, double* seconds) {
   if (!fwd || !rev || iters < 0 || fwd->nch != rev->nch || (n && (!a || !b || !cbuf)))
     return ORC_E_ARG;
-  if (fwd->proto >= ORC_ZC || rev->proto >= ORC_ZC) return ORC_E_ARG;
+  if (fwd->proto >= ORC_ZC || rev->proto >= ORC_ZC) return ORC_E_ARG; /* SIMPLE and LL only */
   tconn tf, tr;
   int rc = tconn_init(&tf, fwd);
   if (!rc) rc = tconn_init(&tr, rev);

@@ -96,7 +96,7 @@ def _replay_fifo(proto, nslots, slot_bytes, transfers, nch):
         for c, j, off, L in _chunks(len(A), nch, S):
             g = base[c] + j
             s0 = (g % nslots) * slot_bytes
-            if proto == oracle.SIMPLE:
+            if proto in (oracle.SIMPLE, oracle.RELAY):
                 fifo[c][s0:s0 + L] = A[off:off + L]
             else:
                 for i in range(0, L, 4):
@@ -121,6 +121,9 @@ CASES = [
     ("zc", 3, 1, 16, [555, 16, 0]),
     ("zcd", 1, 8, 64, [1000, 1]),
     ("zcd", 3, 1, 16, [555, 16, 0]),
+    ("relay", 1, 8, 64, [1000, 1]),
+    ("relay", 3, 2, 32, [1000, 17, 0, 333]),
+    ("relay", 2, 1, 16, [555, 16]),
 ]
 
 
@@ -146,6 +149,12 @@ def test_counters_result_and_fifo_by_replay(proto, nch, nslots, slot_bytes, size
         assert st["ptr_exchange"] == 0
         if pid in (oracle.ZC, oracle.ZCD):
             assert conn.fifo(c).size == 0
+        elif pid == oracle.RELAY:
+            # every step passes through all three FIFOs, so each holds the replay
+            for which in range(3):
+                assert bytes(conn.fifo(c, which)) == bytes(fifo[c]), which
+            rs = conn.relay_state(c)
+            assert rs["send_proxy_tail"] == rs["recv_proxy_tail"] == base[c]
         else:
             assert bytes(conn.fifo(c)) == bytes(fifo[c])
 
@@ -176,7 +185,8 @@ def test_ll_lines_interleave_payload_and_step_flags():
 
 
 @pytest.mark.parametrize("proto,slot_sizes", [("simple", [16, 32, 48]), ("ll", [8, 24]),
-                                              ("zc", [16, 48]), ("zcd", [16, 48])])
+                                              ("zc", [16, 48]), ("zcd", [16, 48]),
+                                              ("relay", [16, 32])])
 def test_edge_sizes_brute_force(proto, slot_sizes):
     pid = oracle.PROTO_NAMES[proto]
     for slot_bytes in slot_sizes:
@@ -212,7 +222,8 @@ def test_pingpong_composes_two_connections():
 
 # ------------------------------------------------------------ interleavings
 ENUM_CASES = []
-for _p, _slots in (("simple", (16, 32)), ("ll", (8, 16)), ("zc", (16,)), ("zcd", (16,))):
+for _p, _slots in (("simple", (16, 32)), ("ll", (8, 16)), ("zc", (16,)), ("zcd", (16,)),
+                   ("relay", (16,))):
     for _ns in (1, 2, 3):
         for _sb in _slots:
             for _nch in (1, 2):
@@ -249,6 +260,9 @@ MUTATION_CASES = [
     ("zc", "zc_no_wait", {"wrong_ptr"}),
     ("zc", "zc_no_reset", {"wrong_ptr", "counters"}),
     ("zcd", "early_tail", {"read_unfilled"}),
+    ("relay", "relay_early", {"read_unfilled"}),
+    ("relay", "weak_credit", {"window", "overwrite"}),
+    ("relay", "early_tail", {"read_unfilled"}),
 ]
 
 
@@ -264,7 +278,7 @@ def test_enumerator_catches_each_broken_rule(proto, mutation, expected, nslots):
 
 
 def test_correct_protocol_is_clean_under_the_same_inputs_as_the_mutations():
-    for proto in ("simple", "ll", "zc", "zcd"):
+    for proto in ("simple", "ll", "zc", "zcd", "relay"):
         pid = oracle.PROTO_NAMES[proto]
         slot_bytes = 16 if pid != oracle.LL else 8
         S = oracle.step_bytes(pid, slot_bytes)
@@ -320,6 +334,7 @@ def test_enumerator_catches_broken_rules_under_take_ahead(mutation, expected):
 
 def test_conn_rejects_bad_shapes():
     for args in [("simple", 0, 8, 16), ("simple", 65, 8, 16), ("simple", 1, 0, 16),
-                 ("simple", 1, 8, 24), ("ll", 1, 8, 12), ("zc", 1, 8, 8), ("zcd", 1, 8, 8)]:
+                 ("simple", 1, 8, 24), ("ll", 1, 8, 12), ("zc", 1, 8, 8), ("zcd", 1, 8, 8),
+                 ("relay", 1, 8, 8)]:
         with pytest.raises(oracle.OracleError):
             oracle.Conn(*args)

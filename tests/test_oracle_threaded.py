@@ -13,8 +13,10 @@ import synth
 
 
 def _end_state(conn, B, nch):
+    relay = conn.proto == oracle.RELAY
     return (B.tobytes(), [sorted(conn.state(ch).items()) for ch in range(nch)],
-            [conn.fifo(ch).tobytes() for ch in range(nch)])
+            [conn.fifo(ch, w).tobytes() for ch in range(nch) for w in range(3 if relay else 1)],
+            [sorted(conn.relay_state(ch).items()) for ch in range(nch)] if relay else None)
 
 
 CASES = [
@@ -22,13 +24,14 @@ CASES = [
     ("ll", 1, 1, 8), ("ll", 2, 3, 64), ("ll", 8, 4, 2048),
     ("zc", 1, 1, 16), ("zc", 4, 1, 256), ("zc", 16, 1, 4096),
     ("zcd", 1, 1, 16), ("zcd", 4, 1, 256), ("zcd", 16, 1, 4096),
+    ("relay", 1, 1, 16), ("relay", 3, 2, 64), ("relay", 8, 4, 4096),
 ]
 
 
 @pytest.mark.parametrize("proto,nch,nslots,slot_bytes", CASES)
 def test_threaded_mode_ends_in_the_sequential_state(proto, nch, nslots, slot_bytes):
     sizes = [0, 1, 15, 17, 4 * slot_bytes * nch + 3, 100_003]
-    for nthreads in sorted({1, 2, 3, 2 * nch}):
+    for nthreads in sorted({1, 2, 3, 2 * nch, (4 if proto == "relay" else 2) * nch}):
         seq = oracle.Conn(proto, nch, nslots, slot_bytes)
         thr = oracle.Conn(proto, nch, nslots, slot_bytes)
         for i, n in enumerate(sizes):
