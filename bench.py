@@ -5,7 +5,8 @@ value: payload GB/s of the SIMPLE copy workload with 32 channels x 8 slots x
 in HBM.  A step is one such transfer (one kernel launch holding both
 endpoints).  The other modes are measured in the same run and reported under
 "modes": the single-pair SIMPLE transfer, the LL ping-pong latency sweep,
-zero-copy (pair and 8-endpoint ring), and the host-memory FIFO.
+zero-copy (pair and 8-endpoint ring, with the destination exchanged per step
+or known before the launch), the host-memory FIFO, and the copy-engine relay.
 
 Real bytes per payload byte: SIMPLE 4 (read A, write FIFO, read FIFO, write
 B), zero-copy 2, LL 6 (read A, 8-byte lines for 4 payload bytes written and
@@ -293,6 +294,35 @@ def bench_w5(torch, T, W, synth):
             "vs_duplex_copy": round(gbs / dup_gbs, 3)}
 
 
+def bench_relay(torch, T, W, synth, dup_gbs):
+    """The copy-engine relay: one 512 MiB transfer and the host-FIFO message
+    mix, against the link's full-duplex copy rate."""
+    cfg = W.W5R
+    tot = cfg["total_bytes"]
+    n = cfg["nbytes"]
+    sizes = synth.log_uniform_message_sizes(tot, synth.workload_seed(5))
+    a = torch.from_numpy(synth.uint8_uniform(tot, synth.workload_seed(5))).to("cuda")
+    b = torch.empty_like(a)
+    conn = W.make_conn(cfg)
+    one, _ = T.time_launches(lambda: conn.run(a, b, n, T.stream), 1, 3)
+    check_no_error(conn, cfg["nchannels"], "relay")
+    ok = bool(torch.equal(a[:n], b[:n]))
+    b.zero_()
+    lst, _ = T.time_launches(lambda: W.run_message_list(conn, a, b, sizes, T.stream), 1, 3)
+    check_no_error(conn, cfg["nchannels"], "relay messages")
+    ok = ok and bool(torch.equal(a, b))
+    conn.close()
+    g1 = n / (one * 1e-3) / 1e9
+    gl = tot / (lst * 1e-3) / 1e9
+    return {"payload_gbs": round(g1, 2), "pcie_frac": round(g1 / PCIE_PEAK_GBS, 4),
+            "vs_duplex_copy": round(g1 / dup_gbs, 3), "bytes": n, "ms": round(one, 3),
+            "message_mix": {"payload_gbs": round(gl, 2), "pcie_frac": round(gl / PCIE_PEAK_GBS, 4),
+                            "messages": len(sizes)},
+            "b_equals_a": ok,
+            "note": "send FIFO (HBM) -> staging FIFO (pinned host) -> receive FIFO (HBM), each "
+                    "hop a DMA copy queued by a host proxy thread"}
+
+
 def plain_copy_ceiling(torch, T) -> dict:
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -423,6 +453,9 @@ def main() -> int:
         modes["zerocopy"] = bench_w4(torch, T, W, synth)
         log("bench: W5 host FIFO")
         modes["host_fifo_16ch_2GiB"] = bench_w5(torch, T, W, synth)
+        log("bench: copy-engine relay")
+        modes["relay_4ch_4MiB"] = bench_relay(
+            torch, T, W, synth, modes["host_fifo_16ch_2GiB"]["pinned_copy_duplex_gbs_each_way"])
         modes["plain_copy_1GiB_torch"] = plain_copy_ceiling(torch, T)
         line["modes"] = modes
     if not args.no_cpu_baseline:

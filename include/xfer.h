@@ -69,7 +69,15 @@ typedef enum {
 
 typedef enum {
   XFER_FIFO_DEVICE = 0, /* FIFO in HBM (the P2P transport's placement) */
-  XFER_FIFO_HOST = 1    /* FIFO in pinned host memory (the shm transport's placement) */
+  XFER_FIFO_HOST = 1,   /* FIFO in pinned host memory (the shm transport's placement) */
+  XFER_FIFO_RELAY = 2   /* copy-engine relay, SIMPLE only ("【NCCL】transport数据传输（二）",
+                           shmTransport, useMemcpy): the producer fills a send FIFO in HBM
+                           and publishes tail; a host send proxy copies each step into a
+                           staging FIFO in pinned host memory (device-to-host DMA) and
+                           publishes its own tail; a host receive proxy copies it on into a
+                           receive FIFO in HBM (host-to-device DMA) and publishes a third
+                           tail, which the consumer polls; head stays the producer's credit.
+                           The control words live in host memory. */
 } xfer_fifo_loc;
 
 typedef enum {
@@ -223,8 +231,22 @@ int xfer_conn_query(const xfer_conn* c, int channel, xfer_chan_state* out);
 int xfer_conn_fifo(const xfer_conn* c, int channel, void** fifo, size_t* bytes);
 
 /* Synchronous copy of one channel's FIFO into host memory host_dst of
- * `bytes` (must equal the FIFO size). */
+ * `bytes` (must equal the FIFO size).  For a relay this is the send FIFO. */
 int xfer_conn_read_fifo(const xfer_conn* c, int channel, void* host_dst, size_t bytes);
+
+/* The same for FIFO `which` of a relay connection: 0 send (HBM), 1 staging
+ * (pinned host), 2 receive (HBM); other connections take which = 0 only.
+ * Errors: INVALID_ARG (which out of range, wrong size, NULL), HIP. */
+int xfer_conn_read_fifo_ex(const xfer_conn* c, int which, int channel, void* host_dst,
+                           size_t bytes);
+
+/* A relay connection's proxy tails for one channel (they are per channel,
+ * kept in lane 0's control block): the send proxy's (steps copied into the
+ * staging FIFO) and the receive proxy's (steps copied into the receive FIFO).
+ * The caller synchronises the stream first.  Errors: INVALID_ARG (not a
+ * relay, bad channel, NULL output). */
+int xfer_conn_query_relay(const xfer_conn* c, int channel, uint64_t* send_proxy_tail,
+                          uint64_t* recv_proxy_tail);
 
 /* Sets the connection's host-side abort word; every in-kernel wait of a
  * running or later launch on it ends with XFER_ERR_ABORTED. */

@@ -9,8 +9,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libxfer.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "conn.cpp", "sched.cpp")]
-HEADERS = [os.path.join(CSRC, "xfer_internal.h"), os.path.join(ROOT, "include", "xfer.h")]
+SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "conn.cpp", "relay.cpp", "sched.cpp")]
+HEADERS = [os.path.join(CSRC, "xfer_internal.h"), os.path.join(CSRC, "relay.h"),
+           os.path.join(ROOT, "include", "xfer.h")]
 ARCH = os.environ.get("XFER_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -50,7 +51,7 @@ def build(verbose: bool = False) -> str:
         _run(cmd)
         objs.append(obj)
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs + ["-lhsa-runtime64", "-lpthread"]
     if verbose:
         print(" ".join(cmd))
     _run(cmd)

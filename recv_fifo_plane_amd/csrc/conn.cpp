@@ -16,6 +16,7 @@
 #include <string>
 #include <vector>
 
+#include "relay.h"
 #include "xfer.h"
 #include "xfer_internal.h"
 
@@ -27,8 +28,11 @@ struct xfer_conn {
   uint64_t timeout_ticks = 0;
   int device = 0;
   int scope = xfer::kScopeAgent;
-  uint8_t* fifo = nullptr;       // device view of the FIFO
+  uint8_t* fifo = nullptr;       // device view of the FIFO (a relay's send FIFO)
   void* fifo_mem = nullptr;      // allocation (device pointer or pinned host pointer)
+  uint8_t* fifo_rx = nullptr;    // relay: receive FIFO in HBM
+  uint8_t* stage = nullptr;      // relay: staging FIFO in pinned host memory
+  xfer::Relay* relay = nullptr;  // relay: the host proxies
   xfer::LaneCtrl* ctrl = nullptr;  // device view of the control blocks
   void* ctrl_mem = nullptr;
   xfer::Status* status_host = nullptr;
@@ -109,6 +113,9 @@ class NearNuma {
 void release(xfer_conn* c) {
   if (!c) return;
   DeviceGuard g(c->device);
+  relay_stop(c->relay);  // joins the proxies before their buffers go
+  if (c->fifo_rx) (void)hipFree(c->fifo_rx);
+  if (c->stage) (void)hipHostFree(c->stage);
   if (c->fifo_mem) {
     if (c->fifo_loc == XFER_FIFO_HOST)
       (void)hipHostFree(c->fifo_mem);
@@ -152,10 +159,24 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 int check_runnable(const xfer_conn* c, const char* who) {
   if (!c) return fail(XFER_ERR_INVALID_ARG, std::string(who) + ": NULL connection");
   const uint32_t err = __atomic_load_n(&c->status_host->err, __ATOMIC_ACQUIRE);
-  if (err)
+  if (err) {
+    const std::string proxy = relay_error(c->relay);
     return fail(XFER_ERR_STATE, std::string(who) + ": connection failed earlier in a kernel (" +
-                                    xfer_status_string(int(err)) + ")");
+                                    xfer_status_string(int(err)) +
+                                    (proxy.empty() ? "" : ", " + proxy) + ")");
+  }
   return XFER_OK;
+}
+
+// Hands a run to a relay connection's proxies: its messages, numbered from
+// each channel's step count before the run.
+void relay_job(const xfer_conn* c, std::vector<uint64_t> lens, uint64_t iters) {
+  if (!c->relay) return;
+  RelayJob job;
+  job.lens = std::move(lens);
+  job.iters = iters;
+  job.base = c->steps;
+  relay_submit(c->relay, job);
 }
 
 // Bookkeeping of the steps a run adds, and the LL 32-bit flag bound.
@@ -181,6 +202,8 @@ ConnArgs conn_args(const xfer_conn* c, const void* src, void* dst, uint64_t nbyt
   ConnArgs a;
   memset(&a, 0, sizeof(a));
   a.fifo = c->fifo;
+  a.fifo_rx = c->fifo_rx ? c->fifo_rx : c->fifo;
+  a.relay = c->fifo_rx ? 1u : 0u;
   a.ctrl = c->ctrl;
   a.status = c->status_dev;
   a.src = static_cast<const uint8_t*>(src);
@@ -282,8 +305,10 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
   if (slot_bytes < gran || slot_bytes % gran || slot_bytes > (size_t(1) << 30))
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: slot_bytes must be a positive multiple of " +
                                           std::to_string(gran) + " up to 1 GiB");
-  if (fifo_loc != XFER_FIFO_DEVICE && fifo_loc != XFER_FIFO_HOST)
-    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: fifo_loc must be DEVICE or HOST");
+  if (fifo_loc != XFER_FIFO_DEVICE && fifo_loc != XFER_FIFO_HOST && fifo_loc != XFER_FIFO_RELAY)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: fifo_loc must be DEVICE, HOST or RELAY");
+  if (fifo_loc == XFER_FIFO_RELAY && proto != XFER_PROTO_SIMPLE)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: the relay carries SIMPLE only");
   xfer_attr a;
   memset(&a, 0, sizeof(a));
   if (attr) a = *attr;
@@ -302,6 +327,10 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: roles must be 0, 1 or 2");
   if (a.ordering != XFER_ORDER_COHERENT && a.ordering != XFER_ORDER_FENCED)
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: ordering must be COHERENT or FENCED");
+  if (fifo_loc == XFER_FIFO_RELAY && a.ctrl_loc == XFER_CTRL_DEVICE)
+    return fail(XFER_ERR_INVALID_ARG,
+                "xfer_conn_create: a relay's control words live in host memory (its proxies poll "
+                "them)");
   const size_t fifo_bytes =
       zero_copy(proto) ? 0 : size_t(nchannels) * size_t(nslots) * slot_bytes;
   if (!zero_copy(proto) && fifo_bytes / size_t(nchannels) / size_t(nslots) != slot_bytes)
@@ -314,7 +343,7 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
   c->nslots = nslots;
   c->fifo_loc = fifo_loc;
   c->ctrl_loc = a.ctrl_loc == XFER_CTRL_DEFAULT
-                    ? (fifo_loc == XFER_FIFO_HOST ? XFER_CTRL_HOST : XFER_CTRL_DEVICE)
+                    ? (fifo_loc == XFER_FIFO_DEVICE ? XFER_CTRL_DEVICE : XFER_CTRL_HOST)
                     : a.ctrl_loc;
   c->lanes = lanes;
   c->block = block;
@@ -428,6 +457,55 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
     return hip_fail(e, "hipHostGetDevicePointer(status)");
   }
   c->status_dev = static_cast<Status*>(sdev);
+  if (fifo_loc == XFER_FIFO_RELAY) {
+    // The staging FIFO (pinned host) and the receive FIFO (HBM), both zeroed,
+    // then the two proxies.
+    e = hipHostMalloc(reinterpret_cast<void**>(&c->stage), fifo_bytes,
+                      hipHostMallocDefault | near.flag());
+    if (e != hipSuccess) {
+      c->stage = nullptr;
+      release(c);
+      return fail(XFER_ERR_NO_MEMORY, std::string("hipHostMalloc(staging FIFO): ") +
+                                          hipGetErrorString(e));
+    }
+    memset(c->stage, 0, fifo_bytes);
+    e = hipMalloc(reinterpret_cast<void**>(&c->fifo_rx), fifo_bytes);
+    if (e != hipSuccess) {
+      c->fifo_rx = nullptr;
+      release(c);
+      return fail(XFER_ERR_NO_MEMORY, std::string("hipMalloc(receive FIFO): ") +
+                                          hipGetErrorString(e));
+    }
+    e = hipMemset(c->fifo_rx, 0, fifo_bytes);
+    if (e != hipSuccess) {
+      release(c);
+      return hip_fail(e, "hipMemset(receive FIFO)");
+    }
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      release(c);
+      return hip_fail(e, "hipDeviceSynchronize");
+    }
+    RelayConfig rc;
+    rc.device = c->device;
+    rc.nch = nchannels;
+    rc.lanes = lanes;
+    rc.nslots = nslots;
+    rc.slot_bytes = slot_bytes;
+    rc.step_bytes = c->step_bytes;
+    rc.send_fifo = c->fifo;
+    rc.stage = c->stage;
+    rc.recv_fifo = c->fifo_rx;
+    rc.ctrl = static_cast<LaneCtrl*>(c->ctrl_mem);
+    rc.status = c->status_host;
+    std::string why;
+    const int r = relay_start(rc, &c->relay, &why);
+    if (r) {
+      c->relay = nullptr;
+      release(c);
+      return fail(r, "xfer_conn_create: " + why);
+    }
+  }
   e = hipDeviceSynchronize();  // the zeroing above is complete before any run
   if (e != hipSuccess) {
     release(c);
@@ -478,6 +556,7 @@ extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nb
   args.timeout_ticks = c->timeout_ticks;
   hipError_t e = launch_run1(v, args, c->block, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "xfer_run launch");
+  relay_job(c, {uint64_t(nbytes)}, uint64_t(iters));
   commit_steps(c, add);
   return XFER_OK;
 }
@@ -552,6 +631,12 @@ extern "C" int xfer_run_messages(xfer_conn* c, const void* src, void* dst, const
     hipError_t e = launch_run1(v, args, c->block, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "xfer_run_messages launch");
   }
+  if (c->relay) {
+    std::vector<uint64_t> lens;
+    lens.reserve(msgs.size());
+    for (const MsgDesc& m : msgs) lens.push_back(m.len);
+    relay_job(c, std::move(lens), 1);
+  }
   commit_steps(c, add);
   return XFER_OK;
 }
@@ -605,8 +690,11 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
   args.timeout_ticks = first->timeout_ticks;
   hipError_t e = launch_runB(v, args, first->block, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "xfer_run_batch launch");
-  for (int i = 0; i < n; ++i)
-    if (nbytes[i]) commit_steps(conns[i], adds[size_t(i)]);
+  for (int i = 0; i < n; ++i) {
+    if (!nbytes[i]) continue;
+    relay_job(conns[i], {uint64_t(nbytes[i])}, 1);
+    commit_steps(conns[i], adds[size_t(i)]);
+  }
   return XFER_OK;
 }
 
@@ -619,10 +707,10 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
   if (fwd == rev) return fail(XFER_ERR_INVALID_ARG, "xfer_run_pingpong: fwd and rev must differ");
   if (zero_copy(fwd->proto) || fwd->proto != rev->proto || fwd->nch != rev->nch ||
       fwd->slot_bytes != rev->slot_bytes || fwd->lanes != rev->lanes || fwd->block != rev->block ||
-      fwd->ordering != rev->ordering || fwd->device != rev->device)
+      fwd->ordering != rev->ordering || fwd->device != rev->device || fwd->relay || rev->relay)
     return fail(XFER_ERR_INVALID_ARG,
                 "xfer_run_pingpong: fwd and rev must be SIMPLE or LL with equal channels, slot "
-                "size, lanes, block size, ordering and device");
+                "size, lanes, block size, ordering and device, and no relay");
   if (iters < 1) return fail(XFER_ERR_INVALID_ARG, "xfer_run_pingpong: iters must be >= 1");
   if (nbytes == 0) return XFER_OK;
   if (!a || !b || !cbuf)
@@ -715,6 +803,38 @@ extern "C" int xfer_conn_read_fifo(const xfer_conn* c, int channel, void* host_d
   DeviceGuard g(c->device);
   hipError_t e = hipMemcpy(host_dst, f, n, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "xfer_conn_read_fifo: hipMemcpy");
+  return XFER_OK;
+}
+
+extern "C" int xfer_conn_read_fifo_ex(const xfer_conn* c, int which, int channel, void* host_dst,
+                                      size_t bytes) {
+  if (!c || channel < 0 || channel >= c->nch || which < 0 || which > 2 ||
+      (which > 0 && !c->relay))
+    return fail(XFER_ERR_INVALID_ARG,
+                "xfer_conn_read_fifo_ex: bad connection or channel, or which not in 0..2 (1 and "
+                "2 need a relay)");
+  if (which == 0) return xfer_conn_read_fifo(c, channel, host_dst, bytes);
+  const size_t n = size_t(c->nslots) * c->slot_bytes;
+  if (bytes != n || !host_dst)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_read_fifo_ex: bytes must equal the FIFO size");
+  if (which == 1) {
+    memcpy(host_dst, c->stage + size_t(channel) * n, n);
+    return XFER_OK;
+  }
+  DeviceGuard g(c->device);
+  hipError_t e = hipMemcpy(host_dst, c->fifo_rx + size_t(channel) * n, n, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "xfer_conn_read_fifo_ex: hipMemcpy");
+  return XFER_OK;
+}
+
+extern "C" int xfer_conn_query_relay(const xfer_conn* c, int channel, uint64_t* send_proxy_tail,
+                                     uint64_t* recv_proxy_tail) {
+  if (!c || !c->relay || channel < 0 || channel >= c->nch || !send_proxy_tail || !recv_proxy_tail)
+    return fail(XFER_ERR_INVALID_ARG,
+                "xfer_conn_query_relay: needs a relay connection, a channel and two outputs");
+  const LaneCtrl* l = static_cast<const LaneCtrl*>(c->ctrl_mem) + size_t(channel) * size_t(c->lanes);
+  *send_proxy_tail = __atomic_load_n(&l[0].ytail, __ATOMIC_ACQUIRE);
+  *recv_proxy_tail = __atomic_load_n(&l[0].gtail, __ATOMIC_ACQUIRE);
   return XFER_OK;
 }
 

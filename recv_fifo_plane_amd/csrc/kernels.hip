@@ -357,6 +357,11 @@ __device__ __forceinline__ uint8_t* slot_of(const ConnArgs& A, uint32_t c, uint6
   return A.fifo + (static_cast<uint64_t>(c) * ns + s) * A.slot_bytes;
 }
 
+// The same slot in the FIFO the consumer drains.
+__device__ __forceinline__ uint8_t* slot_rx(const ConnArgs& A, uint32_t c, uint64_t g) {
+  return A.fifo_rx + (slot_of(A, c, g) - A.fifo);
+}
+
 __device__ __forceinline__ uint32_t chunk_len(const Side& sd, uint64_t S, uint64_t j) {
   return static_cast<uint32_t>(min(S, sd.r.len - j * S));
 }
@@ -441,18 +446,24 @@ __device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
 
 // Consumer of message m: wait for tail > g, acquire, copy the slot out,
 // head = g+1.
+//
+// On a relay connection the step reaches the consumer through the host
+// proxies: it waits on the receive proxy's tail (gtail) and drains the
+// receive FIFO; head still goes back to the producer.
 template <int SC, int ORD, bool AL>
 __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t g0,
                             uint8_t* dst, uint64_t ticks, Shared& sh) {
   using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
+  // (the proxy tails are per channel, in lane 0's control block)
+  const uint64_t* ready = A.relay ? &A.ctrl[static_cast<uint64_t>(c) * A.lanes].gtail : &sd.lc->tail;
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
     uint32_t err = 0;
     if (sd.seen <= g) {
       Deadline dl(ticks, A.status);
       uint64_t t;
-      while ((t = wave_load<SC>(&sd.lc->tail)) <= g) {
+      while ((t = wave_load<SC>(ready)) <= g) {
         if ((err = dl.expired())) break;
         __builtin_amdgcn_s_sleep(1);
       }
@@ -462,8 +473,8 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
       }
     }
     if (!err) {
-      lane_copy<O::kShared, kPolNT, false>(slot_of(A, c, g), dst + sd.r.beg + j * S, chunk_len(sd, S, j),
-                                    S, A.lanes, w);
+      lane_copy<O::kShared, kPolNT, false>(slot_rx(A, c, g), dst + sd.r.beg + j * S,
+                                           chunk_len(sd, S, j), S, A.lanes, w);
       // Our slot reads are complete before the slot is handed back: each
       // loaded value has already fed its store.  Coherent ordering needs no
       // wait for the destination stores; fenced ordering keeps its fence.

@@ -13,6 +13,12 @@ namespace xfer {
 // producer's tail and the consumer's head never share a cache line.  The
 // receive side owns tail, the send side owns head and ptrExchange ("transport
 // 建立", p2pRecvConnect listing); here both live in one block per lane.
+//
+// A relay connection (the shm transport's memcpy mode) adds the two host
+// proxies' tails: ytail (send proxy: step copied from the send FIFO into the
+// staging FIFO) and gtail (receive proxy: step copied on into the receive
+// FIFO, polled by the consumer instead of tail).  They are per channel: only
+// lane 0's are used.
 struct alignas(128) LaneCtrl {
   uint64_t tail;
   uint64_t pad0[15];
@@ -20,8 +26,12 @@ struct alignas(128) LaneCtrl {
   uint64_t pad1[15];
   uint64_t ptrx;
   uint64_t pad2[15];
+  uint64_t ytail;
+  uint64_t pad3[15];
+  uint64_t gtail;
+  uint64_t pad4[15];
 };
-static_assert(sizeof(LaneCtrl) == 384, "control block layout");
+static_assert(sizeof(LaneCtrl) == 640, "control block layout");
 
 // Per-connection status words in pinned host memory: the first in-kernel
 // failure (written once by compare-and-swap) and the host's abort request.
@@ -37,8 +47,9 @@ enum : int { kScopeAgent = 0, kScopeSystem = 1 };
 
 // Device view of one connection for one run.
 struct ConnArgs {
-  uint8_t* fifo;  // channel c, slot s: fifo + (c * nslots + s) * slot_bytes
-  LaneCtrl* ctrl; // [nch * lanes], lane (c, w) at c * lanes + w
+  uint8_t* fifo;    // channel c, slot s: fifo + (c * nslots + s) * slot_bytes (producer's)
+  uint8_t* fifo_rx; // the FIFO the consumer drains: fifo, or a relay's receive FIFO
+  LaneCtrl* ctrl;   // [nch * lanes], lane (c, w) at c * lanes + w
   Status* status; // device view of the pinned status block
   const uint8_t* src;
   uint8_t* dst;
@@ -47,7 +58,7 @@ struct ConnArgs {
   uint64_t step_bytes;
   uint32_t nch, nslots, lanes, wg_begin;
   uint32_t roles;  // bit 0: producer side runs, bit 1: consumer side runs
-  uint32_t pad;
+  uint32_t relay;  // 1: the consumer waits on gtail and drains fifo_rx
 };
 
 // One message of a launch: bytes [off, off + len) of the connection's src

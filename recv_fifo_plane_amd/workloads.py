@@ -11,6 +11,8 @@ W4  zero-copy through ptrExchange: one pair on 128 MiB, and a ring of 8
 W5  host FIFO: 16 channels x 8 x 256 KiB in pinned host memory, 2 GiB of
     messages with log-uniform sizes 1 KiB .. 64 MiB at consecutive offsets;
     the head/tail words sit in HBM, next to the side that polls them.
+W5R the copy-engine relay: host proxies move each step through a pinned
+    staging FIFO with device-to-host and host-to-device DMA copies.
 """
 from __future__ import annotations
 
@@ -42,6 +44,14 @@ W4D_RING = dict(W4_RING, name="zcd_ring_8x128MiB", proto="zcd", wgs_per_channel=
 W5 = dict(name="host_fifo_16ch_2GiB", proto="simple", nchannels=16, nslots=8,
           slot_bytes=256 << 10, fifo_loc="host", wgs_per_channel=8, block_threads=1024,
           ctrl_loc=1, total_bytes=2 << 30)
+
+# The copy-engine relay (SIMPLE through send FIFO -> pinned staging FIFO ->
+# receive FIFO, moved by two host proxies on the DMA engines): one 512 MiB
+# transfer, and the host-FIFO workload's message mix.  Few channels of large
+# slots keep the copies large (each step is one DMA copy per direction).
+W5R = dict(name="relay_4ch_4MiB", proto="simple", nchannels=4, nslots=8, slot_bytes=4 << 20,
+           fifo_loc="relay", wgs_per_channel=8, block_threads=1024, nbytes=512 << 20,
+           total_bytes=2 << 30)
 
 _ATTRS = ("wgs_per_channel", "block_threads", "ctrl_loc", "timeout_ms", "xcd_pairing", "ordering")
 

@@ -29,6 +29,7 @@ XFER_PROTO_ZEROCOPY = 2
 XFER_PROTO_ZEROCOPY_DIRECT = 3
 XFER_FIFO_DEVICE = 0
 XFER_FIFO_HOST = 1
+XFER_FIFO_RELAY = 2
 XFER_CTRL_DEFAULT = 0
 XFER_CTRL_DEVICE = 1
 XFER_CTRL_HOST = 2
@@ -42,7 +43,7 @@ XFER_MAX_BATCH = 16
 PROTOS = {"simple": XFER_PROTO_SIMPLE, "ll": XFER_PROTO_LL, "zc": XFER_PROTO_ZEROCOPY,
           "zerocopy": XFER_PROTO_ZEROCOPY, "zcd": XFER_PROTO_ZEROCOPY_DIRECT,
           "zerocopy_direct": XFER_PROTO_ZEROCOPY_DIRECT}
-FIFO_LOCS = {"device": XFER_FIFO_DEVICE, "host": XFER_FIFO_HOST}
+FIFO_LOCS = {"device": XFER_FIFO_DEVICE, "host": XFER_FIFO_HOST, "relay": XFER_FIFO_RELAY}
 
 
 class xfer_attr(C.Structure):
@@ -94,6 +95,8 @@ SIGNATURES = {
     "xfer_conn_query": (C.c_int, [_vp, C.c_int, C.POINTER(xfer_chan_state)]),
     "xfer_conn_fifo": (C.c_int, [_vp, C.c_int, C.POINTER(_vp), C.POINTER(C.c_size_t)]),
     "xfer_conn_read_fifo": (C.c_int, [_vp, C.c_int, _vp, C.c_size_t]),
+    "xfer_conn_read_fifo_ex": (C.c_int, [_vp, C.c_int, C.c_int, _vp, C.c_size_t]),
+    "xfer_conn_query_relay": (C.c_int, [_vp, C.c_int, _u64p, _u64p]),
     "xfer_conn_abort": (C.c_int, [_vp]),
     "xfer_conn_launch_shape": (C.c_int, [_vp, _ip, _ip]),
     "xfer_last_error": (C.c_char_p, []),
@@ -230,13 +233,21 @@ class Conn:
         check(lib().xfer_conn_fifo(self._h, int(channel), C.byref(p), C.byref(n)))
         return n.value
 
-    def read_fifo(self, channel: int):
+    def read_fifo(self, channel: int, which: int = 0):
+        """One channel's FIFO bytes; a relay's which = 0 send, 1 staging, 2 receive."""
         import numpy as np
         n = self.fifo_bytes(channel)
         out = np.zeros(n, dtype=np.uint8)
         if n:
-            check(lib().xfer_conn_read_fifo(self._h, int(channel), out.ctypes.data, n))
+            check(lib().xfer_conn_read_fifo_ex(self._h, int(which), int(channel), out.ctypes.data,
+                                               n))
         return out
+
+    def query_relay(self, channel: int) -> dict:
+        """A relay's proxy tails for one channel (after the stream is synchronised)."""
+        y, g = C.c_uint64(), C.c_uint64()
+        check(lib().xfer_conn_query_relay(self._h, int(channel), C.byref(y), C.byref(g)))
+        return {"send_proxy_tail": y.value, "recv_proxy_tail": g.value}
 
     def abort(self) -> None:
         check(lib().xfer_conn_abort(self._h))

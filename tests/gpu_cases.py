@@ -61,6 +61,11 @@ def describe_mismatch(got, want, before, bad, base) -> str:
         bad.size, len(runs), runs[:12], untouched)
 
 
+def oracle_proto(proto: str, fifo_loc: str) -> str:
+    """The oracle's mode for a GPU connection: a relay FIFO is its own mode."""
+    return "relay" if fifo_loc == "relay" else proto
+
+
 def compare_state(conn, oconn, nch: int, what: str) -> None:
     for c in range(nch):
         g = conn.query(c)
@@ -70,12 +75,19 @@ def compare_state(conn, oconn, nch: int, what: str) -> None:
         for k in ("head", "tail", "steps"):
             assert g[k] == o[k], (what, c, k, g, o)
         assert g["ptr_exchange"] == 0 and o["ptr_exchange"] == 0, (what, c, g, o)
-        gf = conn.read_fifo(c)
-        of = oconn.fifo(c)
-        assert gf.size == of.size, (what, c)
-        if gf.size:
-            bad = np.flatnonzero(gf != of)
-            assert bad.size == 0, (what, "fifo", c, bad.size, bad[:8])
+        relay = oconn.proto == oracle.RELAY
+        for which in range(3 if relay else 1):
+            gf = conn.read_fifo(c, which)
+            of = oconn.fifo(c, which)
+            assert gf.size == of.size, (what, c, which)
+            if gf.size:
+                bad = np.flatnonzero(gf != of)
+                assert bad.size == 0, (what, "fifo", which, c, bad.size, bad[:8])
+        if relay:
+            gr = conn.query_relay(c)
+            orr = oconn.relay_state(c)
+            assert gr["send_proxy_tail"] == orr["send_proxy_tail"], (what, c, gr, orr)
+            assert gr["recv_proxy_tail"] == orr["recv_proxy_tail"], (what, c, gr, orr)
 
 
 def run_transfers(proto: str, nch: int, nslots: int, slot_bytes: int, sizes, *,
@@ -91,7 +103,7 @@ def run_transfers(proto: str, nch: int, nslots: int, slot_bytes: int, sizes, *,
     conn = xf.Conn(proto, nch, nslots, slot_bytes, fifo_loc, wgs_per_channel=lanes,
                    block_threads=block, ctrl_loc=ctrl_loc, xcd_pairing=xcd_pairing,
                    ordering=ordering)
-    ocn = oracle.Conn(proto, nch, nslots, slot_bytes)
+    ocn = oracle.Conn(oracle_proto(proto, fifo_loc), nch, nslots, slot_bytes)
     try:
         for t, n in enumerate(sizes):
             A = payload(kind, n, seed * 7919 + t)
@@ -135,7 +147,7 @@ def run_message_list(proto: str, nch: int, nslots: int, slot_bytes: int, sizes, 
         off += s_
     conn = xf.Conn(proto, nch, nslots, slot_bytes, fifo_loc, wgs_per_channel=lanes,
                    block_threads=block, ctrl_loc=ctrl_loc)
-    ocn = oracle.Conn(proto, nch, nslots, slot_bytes)
+    ocn = oracle.Conn(oracle_proto(proto, fifo_loc), nch, nslots, slot_bytes)
     try:
         for r in range(repeat):
             A = payload(kind, base_off + total + 16, seed + r)

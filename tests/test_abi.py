@@ -46,13 +46,22 @@ def test_library_exports_every_declared_symbol():
     (1, 1, 8, 12, 0),           # LL slot not a multiple of 8
     (2, 1, 8, 8, 0),            # zero-copy step not a multiple of 16
     (3, 1, 8, 8, 0),            # zero-copy direct step not a multiple of 16
-    (0, 1, 8, 128, 2),          # unknown FIFO location
+    (0, 1, 8, 128, 3),          # unknown FIFO location
+    (1, 1, 8, 128, 2),          # the relay carries SIMPLE only
+    (2, 1, 8, 128, 2),
 ])
 def test_create_rejects_bad_arguments(args):
     with pytest.raises(xf.XferError) as e:
         xf.Conn(*args)
     assert e.value.status == X.XFER_ERR_INVALID_ARG
     assert xf.last_error()
+
+
+def test_relay_needs_host_control_words():
+    with pytest.raises(xf.XferError) as e:
+        xf.Conn("simple", 1, 8, 128, "relay", ctrl_loc=X.XFER_CTRL_DEVICE)
+    assert e.value.status == X.XFER_ERR_INVALID_ARG
+    assert "host memory" in xf.last_error()
 
 
 @pytest.mark.parametrize("attr", [dict(wgs_per_channel=17), dict(block_threads=96),

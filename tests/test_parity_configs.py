@@ -150,3 +150,30 @@ def test_w5_host_fifo_mixed_messages(one_launch_per_message):
     assert np.array_equal(to_host(b), B)
     compare_state(conn, ocn, 16, "W5")
     conn.close()
+
+
+def test_w5r_copy_engine_relay_full_size():
+    # the relay at the benchmark's shape: one 512 MiB transfer, then the
+    # host-FIFO message mix, on one connection; every FIFO and tail checked
+    torch = _torch()
+    cfg = W.W5R
+    log("case: W5R relay " + str(cfg))
+    n = cfg["nbytes"]
+    sizes = synth.log_uniform_message_sizes(cfg["total_bytes"], synth.workload_seed(5))
+    A = synth.uint8_uniform(cfg["total_bytes"], synth.workload_seed(5))
+    conn = W.make_conn(cfg)
+    ocn = oracle.Conn("relay", cfg["nchannels"], cfg["nslots"], cfg["slot_bytes"])
+    a = to_dev(A)
+    b = torch.zeros_like(a)
+    conn.run(a, b, n)
+    W.run_message_list(conn, a, b, sizes)
+    torch.cuda.synchronize()
+    B = np.zeros_like(A)
+    ocn.run(np.ascontiguousarray(A[:n]), B[:n], n)
+    off = 0
+    for s_ in sizes:
+        ocn.run(np.ascontiguousarray(A[off:off + s_]), B[off:off + s_], s_)
+        off += s_
+    assert np.array_equal(to_host(b), B)
+    compare_state(conn, ocn, cfg["nchannels"], "W5R")
+    conn.close()
