@@ -315,7 +315,8 @@ def bench_relay(torch, T, W, synth, dup_gbs):
     g1 = n / (one * 1e-3) / 1e9
     gl = tot / (lst * 1e-3) / 1e9
     return {"payload_gbs": round(g1, 2), "pcie_frac": round(g1 / PCIE_PEAK_GBS, 4),
-            "vs_duplex_copy": round(g1 / dup_gbs, 3), "bytes": n, "ms": round(one, 3),
+            "vs_duplex_copy": round(g1 / dup_gbs, 3) if dup_gbs else None,
+            "bytes": n, "ms": round(one, 3),
             "message_mix": {"payload_gbs": round(gl, 2), "pcie_frac": round(gl / PCIE_PEAK_GBS, 4),
                             "messages": len(sizes)},
             "b_equals_a": ok,
@@ -393,9 +394,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["value", "all", "copy"], default="all",
+    ap.add_argument("--only", choices=["value", "all", "copy", "zerocopy", "relay"],
+                    default="all",
                     help="value: time only the headline workload; copy: only a plain 1 GiB "
-                         "device copy (the calibration kernel of the HBM byte counters)")
+                         "device copy (the calibration kernel of the HBM byte counters); "
+                         "zerocopy, relay: only that mode (for profiling it alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -414,6 +417,15 @@ def main() -> int:
     T = Timer(torch, stream)
     if args.only == "copy":
         print(json.dumps({"plain_copy_1GiB_torch": plain_copy_ceiling(torch, T)}), flush=True)
+        return 0
+    if args.only == "zerocopy":
+        print(json.dumps({"zerocopy": bench_w4(torch, T, W, synth)}), flush=True)
+        return 0
+    if args.only == "relay":
+        # the duplex copy rate of the link is measured by the host-FIFO mode;
+        # alone, the relay reports against PCIe only
+        print(json.dumps({"relay_4ch_4MiB": bench_relay(torch, T, W, synth, None)}),
+              flush=True)
         return 0
     log("bench: W3 simple 32ch 1GiB, %d warmup + %d steps" % (args.warmup, args.steps))
     A, w3 = bench_w3(torch, T, W, synth, args.steps, args.warmup)
