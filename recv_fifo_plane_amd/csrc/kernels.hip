@@ -336,7 +336,8 @@ __device__ __forceinline__ Side make_side(const ConnArgs& A, uint32_t c, uint32_
 // Shared by the waves of a workgroup: the first failure seen by any wave.
 struct Shared {
   uint32_t err;
-  uint32_t pad;
+  uint32_t werr;    // outcome of a wait polled by one wave (wait_count)
+  uint64_t wval;    // the counter value that ended it
   uint64_t ptr[2];  // zero-copy destinations, indexed by step parity
 };
 
@@ -367,21 +368,59 @@ __device__ __forceinline__ uint32_t chunk_len(const Side& sd, uint64_t S, uint64
 }
 
 // ------------------------------------------------------------------ SIMPLE
-// Waits until step g has credit: g < head + nslots (wave-uniform poll of the
-// lane's head).  Written without a subtraction because head may run ahead
-// of g: an LL consumer whose lane owns no lines of a step has nothing to
-// wait for and frees that step at once.
-template <int SC, int ORD>
-__device__ __forceinline__ uint32_t wait_credit(const ConnArgs& A, Side& sd, uint64_t g,
-                                                uint64_t ticks) {
-  if (g < sd.seen + A.nslots) return 0;
-  Deadline dl(ticks, A.status);
-  uint64_t h;
-  while (g >= (h = wave_load<SC>(&sd.lc->head)) + A.nslots) {
-    const uint32_t err = dl.expired();
-    if (err) return err;
-    __builtin_amdgcn_s_sleep(1);
+// Waits until *p + add > g (add = nslots for a producer's credit, 0 for a
+// consumer's ready count) and returns in v the value that ended the wait.
+// Written without a subtraction because the counter may run ahead of g.
+//
+// With WG, a counter in host memory (system scope) is polled by wave 0 alone,
+// which hands the outcome to the other waves through LDS: each poll is a
+// read across PCIe, and every wave of every waiting workgroup polling at
+// once crowds out the DMA copies that share the link (they ran a third
+// slower under such polling).  Every wave of the workgroup must then reach
+// the call, and a workgroup barrier must separate two such calls (each step
+// ends with one).  Counters in HBM are polled by every wave, which is
+// cheaper than a barrier per step.
+template <int SC, bool WG>
+__device__ __forceinline__ uint32_t wait_count(const uint64_t* p, uint64_t add, uint64_t g,
+                                               uint64_t ticks, Status* st, Shared& sh,
+                                               uint64_t& v) {
+  uint32_t err = 0;
+  if constexpr (WG && SC == kScopeSystem) {
+    if (threadIdx.x < static_cast<uint32_t>(warpSize)) {
+      Deadline dl(ticks, st);
+      uint64_t x;
+      while (g >= (x = wave_load<SC>(p)) + add) {
+        if ((err = dl.expired())) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (threadIdx.x == 0) {
+        sh.werr = err;
+        sh.wval = x;
+      }
+    }
+    __syncthreads();
+    err = sh.werr;
+    v = sh.wval;
+  } else {
+    Deadline dl(ticks, st);
+    while (g >= (v = wave_load<SC>(p)) + add) {
+      if ((err = dl.expired())) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
   }
+  return err;
+}
+
+// Waits until step g has credit: g < head + nslots.  head may run ahead of
+// g: an LL consumer whose lane owns no lines of a step has nothing to wait
+// for and frees that step at once.
+template <int SC, int ORD, bool WG>
+__device__ __forceinline__ uint32_t wait_credit(const ConnArgs& A, Side& sd, uint64_t g,
+                                                uint64_t ticks, Shared& sh) {
+  if (g < sd.seen + A.nslots) return 0;
+  uint64_t h = 0;
+  const uint32_t err = wait_count<SC, WG>(&sd.lc->head, A.nslots, g, ticks, A.status, sh, h);
+  if (err) return err;
   Order<SC, ORD>::acquire();  // the consumer's reads of the slot precede our writes
   sd.seen = h;
   return 0;
@@ -400,7 +439,7 @@ __device__ bool simple_send_piped(const ConnArgs& A, uint32_t c, uint32_t w, Sid
   batch_load<kPolNT, false>(b, src + sd.r.beg, chunk_len(sd, S, 0), S, P, w);
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
-    const uint32_t err = wait_credit<SC, ORD>(A, sd, g, ticks);
+    const uint32_t err = wait_credit<SC, ORD, true>(A, sd, g, ticks, sh);
     if (!err) {
       const uint32_t L = chunk_len(sd, S, j);
       uint8_t* slot = slot_of(A, c, g);
@@ -432,7 +471,7 @@ __device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
   }
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
-    const uint32_t err = wait_credit<SC, ORD>(A, sd, g, ticks);
+    const uint32_t err = wait_credit<SC, ORD, true>(A, sd, g, ticks, sh);
     if (!err) {
       lane_copy<kPolNT, O::kShared, false>(src + sd.r.beg + j * S, slot_of(A, c, g), chunk_len(sd, S, j),
                                     S, A.lanes, w);
@@ -461,12 +500,8 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
     const uint64_t g = g0 + j;
     uint32_t err = 0;
     if (sd.seen <= g) {
-      Deadline dl(ticks, A.status);
-      uint64_t t;
-      while ((t = wave_load<SC>(ready)) <= g) {
-        if ((err = dl.expired())) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
+      uint64_t t = 0;
+      err = wait_count<SC, true>(ready, 0, g, ticks, A.status, sh, t);
       if (!err) {
         O::acquire();
         sd.seen = t;
@@ -518,7 +553,7 @@ __device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
   uint32_t err = 0;
   for (uint64_t j = 0; j < sd.r.k && !err; ++j) {
     const uint64_t g = g0 + j;
-    if ((err = wait_credit<SC, ORD>(A, sd, g, ticks))) break;
+    if ((err = wait_credit<SC, ORD, false>(A, sd, g, ticks, sh))) break;
     const uint32_t L = chunk_len(sd, S, j);
     const uint32_t nl = (L + 3u) / 4u;
     uint64_t* lines = reinterpret_cast<uint64_t*>(slot_of(A, c, g));
