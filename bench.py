@@ -104,8 +104,8 @@ def check_no_error(conn, nch: int, what: str) -> None:
             raise RuntimeError("%s: channel %d state %s" % (what, c, st))
 
 
-def bench_w3(torch, T, W, synth, steps, warmup):
-    cfg = W.W3
+def bench_w3(torch, T, W, synth, steps, warmup, cfg=None):
+    cfg = cfg or W.W3
     n = cfg["nbytes"]
     A = synth.bf16_normal_bytes(n, synth.workload_seed(3))
     a = torch.from_numpy(A).to("cuda")
@@ -461,6 +461,15 @@ def main() -> int:
         modes = {"simple_1ch_4MiB": bench_w1(torch, T, W, synth)}
         log("bench: W2 LL ping-pong sweep")
         modes["ll_pingpong"] = bench_w2(torch, T, W, synth)
+        log("bench: W3 under P2P read")
+        _, w3r = bench_w3(torch, T, W, synth, args.steps, args.warmup, W.W3R)
+        real_r = 4 * W.W3R["nbytes"] / (w3r["kernel_ms"] * 1e-3) / 1e9  # as the roofline counts
+        modes["simple_32ch_1GiB_p2p_read"] = {
+            "payload_gbs": round(w3r["payload_gbs"], 2),
+            "real_gbs": round(real_r, 1),
+            "hbm_frac": round(real_r / HBM_PEAK_GBS, 4),
+            "kernel_ms": round(w3r["kernel_ms"], 5), "b_equals_a": w3r["b_equals_a"],
+            "note": "the FIFO in the send side's memory; on one GPU both sides share one HBM"}
         log("bench: W4 zero-copy")
         modes["zerocopy"] = bench_w4(torch, T, W, synth)
         log("bench: W5 host FIFO")

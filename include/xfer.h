@@ -114,7 +114,14 @@ typedef struct {
                            2 = consumer/receiver only; a lone side ends its waits with
                            XFER_ERR_TIMEOUT (or XFER_ERR_ABORTED after xfer_conn_abort) */
   int ordering;         /* xfer_ordering */
-  int reserved;
+  int p2p_read;         /* 0 (default): write mode, the SIMPLE FIFO belongs to the receive side,
+                           which the producer writes into.  1: P2P read, the FIFO is appended
+                           to the send side's memory (after its head/ptrExchange blocks) and
+                           the consumer reads it from there; tail stays in the receive side's
+                           own blocks ("transport建立", p2pSendSetup and p2pRecvConnect
+                           listings; "【NCCL】transport数据传输（二）", SIMPLE copy mode).
+                           The protocol steps are unchanged.  SIMPLE with the FIFO and
+                           control words in HBM only; otherwise INVALID_ARG. */
 } xfer_attr;
 
 /* State of one channel, read back after the stream has been synchronised. */

@@ -22,7 +22,7 @@
 
 struct xfer_conn {
   int proto = 0, nch = 0, nslots = 0, fifo_loc = 0, ctrl_loc = 0;
-  int lanes = 1, block = 256, xcd_pairing = 0, roles = 3, ordering = 0;
+  int lanes = 1, block = 256, xcd_pairing = 0, roles = 3, ordering = 0, p2p_read = 0;
   size_t slot_bytes = 0, step_bytes = 0;
   uint32_t timeout_ms = 0;
   uint64_t timeout_ticks = 0;
@@ -33,8 +33,10 @@ struct xfer_conn {
   uint8_t* fifo_rx = nullptr;    // relay: receive FIFO in HBM
   uint8_t* stage = nullptr;      // relay: staging FIFO in pinned host memory
   xfer::Relay* relay = nullptr;  // relay: the host proxies
-  xfer::LaneCtrl* ctrl = nullptr;  // device view of the control blocks
-  void* ctrl_mem = nullptr;
+  xfer::LaneCtrl* ctrl = nullptr;  // device view of the send side's control blocks
+  void* ctrl_mem = nullptr;        // their allocation (P2P read: followed by the FIFO)
+  xfer::LaneCtrl* ctrl_rx = nullptr;  // the receive side's blocks (== ctrl in write mode)
+  void* ctrl_rx_mem = nullptr;        // P2P read: the receive side's own allocation
   xfer::Status* status_host = nullptr;
   xfer::Status* status_dev = nullptr;
   std::vector<uint64_t> steps;   // per channel, host bookkeeping of completed steps
@@ -53,6 +55,8 @@ namespace {
 
 constexpr uint32_t kDefaultTimeoutMs = 10000;
 constexpr int kDefaultBlock = 256;
+// P2P read: the FIFO starts on this boundary after the send side's control blocks.
+constexpr size_t kFifoAlign = size_t(64) << 10;
 
 int fail(int code, const std::string& msg) {
   set_error(code, msg);
@@ -128,6 +132,7 @@ void release(xfer_conn* c) {
     else
       (void)hipFree(c->ctrl_mem);
   }
+  if (c->ctrl_rx_mem) (void)hipFree(c->ctrl_rx_mem);
   if (c->status_host) (void)hipHostFree(c->status_host);
   delete c;
 }
@@ -204,7 +209,8 @@ ConnArgs conn_args(const xfer_conn* c, const void* src, void* dst, uint64_t nbyt
   a.fifo = c->fifo;
   a.fifo_rx = c->fifo_rx ? c->fifo_rx : c->fifo;
   a.relay = c->fifo_rx ? 1u : 0u;
-  a.ctrl = c->ctrl;
+  a.ctrl_tx = c->ctrl;
+  a.ctrl_rx = c->ctrl_rx;
   a.status = c->status_dev;
   a.src = static_cast<const uint8_t*>(src);
   a.dst = static_cast<uint8_t*>(dst);
@@ -331,6 +337,13 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
     return fail(XFER_ERR_INVALID_ARG,
                 "xfer_conn_create: a relay's control words live in host memory (its proxies poll "
                 "them)");
+  if (a.p2p_read != 0 && a.p2p_read != 1)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: p2p_read must be 0 or 1");
+  if (a.p2p_read &&
+      (proto != XFER_PROTO_SIMPLE || fifo_loc != XFER_FIFO_DEVICE || a.ctrl_loc == XFER_CTRL_HOST))
+    return fail(XFER_ERR_INVALID_ARG,
+                "xfer_conn_create: P2P read moves the SIMPLE FIFO of a device connection to the "
+                "send side (SIMPLE, FIFO and control words in HBM)");
   const size_t fifo_bytes =
       zero_copy(proto) ? 0 : size_t(nchannels) * size_t(nslots) * slot_bytes;
   if (!zero_copy(proto) && fifo_bytes / size_t(nchannels) / size_t(nslots) != slot_bytes)
@@ -353,6 +366,7 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
   c->xcd_pairing = a.xcd_pairing == -1 ? 0 : 1;
   c->roles = a.roles == 0 ? 3 : a.roles;
   c->ordering = a.ordering;
+  c->p2p_read = a.p2p_read;
   c->slot_bytes = slot_bytes;
   c->step_bytes = proto == XFER_PROTO_LL ? slot_bytes / 2 : slot_bytes;
   c->timeout_ms = a.timeout_ms ? a.timeout_ms : kDefaultTimeoutMs;
@@ -377,7 +391,7 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
   // FIFO: HBM, or pinned host memory mapped into the device (fine-grained,
   // so device accesses reach host memory rather than a non-coherent cache).
   NearNuma near(c->device);  // pinned host blocks below land next to the device
-  if (fifo_bytes) {
+  if (fifo_bytes && !c->p2p_read) {
     if (fifo_loc == XFER_FIFO_HOST) {
       e = hipHostMalloc(&c->fifo_mem, fifo_bytes,
                         hipHostMallocMapped | hipHostMallocCoherent | near.flag());
@@ -411,7 +425,35 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
   }
   // Control blocks: one per lane, head = tail = ptrExchange = 0.
   const size_t ctrl_bytes = sizeof(LaneCtrl) * size_t(nchannels) * size_t(lanes);
-  if (c->ctrl_loc == XFER_CTRL_HOST) {
+  if (c->p2p_read) {
+    // P2P read ("transport建立", p2pSendSetup / p2pRecvConnect listings):
+    // the SIMPLE buffer is appended to the send side's memory (its control
+    // blocks), which the receive side reads; tail sits in the receive
+    // side's own blocks.  Both allocations live in HBM.
+    const size_t fifo_off = (ctrl_bytes + kFifoAlign - 1) / kFifoAlign * kFifoAlign;
+    e = hipMalloc(&c->ctrl_mem, fifo_off + fifo_bytes);
+    if (e != hipSuccess) {
+      c->ctrl_mem = nullptr;
+      release(c);
+      return fail(XFER_ERR_NO_MEMORY, std::string("hipMalloc(send side): ") + hipGetErrorString(e));
+    }
+    e = hipMalloc(&c->ctrl_rx_mem, ctrl_bytes);
+    if (e != hipSuccess) {
+      c->ctrl_rx_mem = nullptr;
+      release(c);
+      return fail(XFER_ERR_NO_MEMORY,
+                  std::string("hipMalloc(receive side): ") + hipGetErrorString(e));
+    }
+    e = hipMemset(c->ctrl_mem, 0, fifo_off + fifo_bytes);
+    if (e == hipSuccess) e = hipMemset(c->ctrl_rx_mem, 0, ctrl_bytes);
+    if (e != hipSuccess) {
+      release(c);
+      return hip_fail(e, "hipMemset(control blocks)");
+    }
+    c->ctrl = static_cast<LaneCtrl*>(c->ctrl_mem);
+    c->ctrl_rx = static_cast<LaneCtrl*>(c->ctrl_rx_mem);
+    c->fifo = static_cast<uint8_t*>(c->ctrl_mem) + fifo_off;
+  } else if (c->ctrl_loc == XFER_CTRL_HOST) {
     e = hipHostMalloc(&c->ctrl_mem, ctrl_bytes,
                       hipHostMallocMapped | hipHostMallocCoherent | near.flag());
     if (e != hipSuccess) {
@@ -441,6 +483,7 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
     }
     c->ctrl = static_cast<LaneCtrl*>(c->ctrl_mem);
   }
+  if (!c->p2p_read) c->ctrl_rx = c->ctrl;
   // Status words (error, abort) in pinned host memory.
   void* st = nullptr;
   e = hipHostMalloc(&st, sizeof(Status), hipHostMallocMapped | hipHostMallocCoherent);
@@ -749,27 +792,30 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
 extern "C" int xfer_conn_query(const xfer_conn* c, int channel, xfer_chan_state* out) {
   if (!c || !out || channel < 0 || channel >= c->nch)
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_query: bad connection, channel or out");
-  std::vector<LaneCtrl> lanes(static_cast<size_t>(c->lanes));
-  const LaneCtrl* first = c->ctrl + size_t(channel) * size_t(c->lanes);
+  // head and ptrExchange from the send side's blocks, tail from the receive
+  // side's (one and the same array unless the connection reads P2P)
+  std::vector<LaneCtrl> tx(static_cast<size_t>(c->lanes)), rx(static_cast<size_t>(c->lanes));
+  const size_t first = size_t(channel) * size_t(c->lanes);
   const size_t bytes = sizeof(LaneCtrl) * size_t(c->lanes);
   if (c->ctrl_loc == XFER_CTRL_HOST) {
-    const LaneCtrl* hostv =
-        static_cast<const LaneCtrl*>(c->ctrl_mem) + size_t(channel) * size_t(c->lanes);
-    memcpy(lanes.data(), hostv, bytes);
+    memcpy(tx.data(), static_cast<const LaneCtrl*>(c->ctrl_mem) + first, bytes);
+    rx = tx;
   } else {
     DeviceGuard g(c->device);
-    hipError_t e = hipMemcpy(lanes.data(), first, bytes, hipMemcpyDeviceToHost);
+    hipError_t e = hipMemcpy(tx.data(), c->ctrl + first, bytes, hipMemcpyDeviceToHost);
+    if (e == hipSuccess)
+      e = hipMemcpy(rx.data(), c->ctrl_rx + first, bytes, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "xfer_conn_query: hipMemcpy");
   }
   memset(out, 0, sizeof(*out));
-  out->head = lanes[0].head;
-  out->tail = lanes[0].tail;
-  out->ptr_exchange = lanes[0].ptrx;
+  out->head = tx[0].head;
+  out->tail = rx[0].tail;
+  out->ptr_exchange = tx[0].ptrx;
   out->steps = c->steps[size_t(channel)];
   out->lanes = c->lanes;
   out->lanes_agree = 1;
-  for (const LaneCtrl& l : lanes)
-    if (l.head != lanes[0].head || l.tail != lanes[0].tail || l.ptrx != lanes[0].ptrx)
+  for (size_t w = 0; w < tx.size(); ++w)
+    if (tx[w].head != tx[0].head || rx[w].tail != rx[0].tail || tx[w].ptrx != tx[0].ptrx)
       out->lanes_agree = 0;
   out->error = int(__atomic_load_n(&c->status_host->err, __ATOMIC_ACQUIRE));
   return XFER_OK;

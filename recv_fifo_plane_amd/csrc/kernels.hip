@@ -314,7 +314,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Per-workgroup state of one side of a lane across the messages of a launch.
 struct Side {
-  LaneCtrl* lc;
+  LaneCtrl* tx;     // the send side's block of this lane: head, ptrExchange
+  LaneCtrl* rx;     // the receive side's block: tail (and a relay's proxy tails)
   uint64_t base;    // step counter at launch start (own counter: tail or head)
   uint64_t seen;    // last observed peer counter (wave-uniform)
   Range r;          // the channel's range and steps in the current message
@@ -323,11 +324,13 @@ struct Side {
 __device__ __forceinline__ Side make_side(const ConnArgs& A, uint32_t c, uint32_t w, bool producer,
                                           int sc) {
   Side s;
-  s.lc = A.ctrl + static_cast<uint64_t>(c) * A.lanes + w;
+  const uint64_t lane = static_cast<uint64_t>(c) * A.lanes + w;
+  s.tx = A.ctrl_tx + lane;
+  s.rx = A.ctrl_rx + lane;
   s.r = Range{0, 0, 0};  // set per message
   // A side is the only writer of its own counter, and the previous launch
   // that wrote it has completed, so a plain coherent load reads it.
-  const uint64_t* own = producer ? &s.lc->tail : &s.lc->head;
+  const uint64_t* own = producer ? &s.rx->tail : &s.tx->head;
   s.base = sc == kScopeSystem ? wave_load<kScopeSystem>(own) : wave_load<kScopeAgent>(own);
   s.seen = 0;
   return s;
@@ -419,7 +422,7 @@ __device__ __forceinline__ uint32_t wait_credit(const ConnArgs& A, Side& sd, uin
                                                 uint64_t ticks, Shared& sh) {
   if (g < sd.seen + A.nslots) return 0;
   uint64_t h = 0;
-  const uint32_t err = wait_count<SC, WG>(&sd.lc->head, A.nslots, g, ticks, A.status, sh, h);
+  const uint32_t err = wait_count<SC, WG>(&sd.tx->head, A.nslots, g, ticks, A.status, sh, h);
   if (err) return err;
   Order<SC, ORD>::acquire();  // the consumer's reads of the slot precede our writes
   sd.seen = h;
@@ -453,7 +456,7 @@ __device__ bool simple_send_piped(const ConnArgs& A, uint32_t c, uint32_t w, Sid
       }
     }
     if (wg_failed(sh, err, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
+    if (threadIdx.x == 0) st_u64<SC>(&sd.rx->tail, g + 1);
   }
   return true;
 }
@@ -478,7 +481,7 @@ __device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
       O::release();
     }
     if (wg_failed(sh, err, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
+    if (threadIdx.x == 0) st_u64<SC>(&sd.rx->tail, g + 1);
   }
   return true;
 }
@@ -495,7 +498,7 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
   using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
   // (the proxy tails are per channel, in lane 0's control block)
-  const uint64_t* ready = A.relay ? &A.ctrl[static_cast<uint64_t>(c) * A.lanes].gtail : &sd.lc->tail;
+  const uint64_t* ready = A.relay ? &A.ctrl_rx[static_cast<uint64_t>(c) * A.lanes].gtail : &sd.rx->tail;
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
     uint32_t err = 0;
@@ -516,7 +519,7 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
       if constexpr (ORD == kOrdFenced) O::release();
     }
     if (wg_failed(sh, err, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.lc->head, g + 1);
+    if (threadIdx.x == 0) st_u64<SC>(&sd.tx->head, g + 1);
   }
   return true;
 }
@@ -637,7 +640,7 @@ __device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
     // ordering keeps its release fence.
     if constexpr (ORD == kOrdFenced) O::release();
     if (wg_failed(sh, err, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.lc->head, g + 1);
+    if (threadIdx.x == 0) st_u64<SC>(&sd.tx->head, g + 1);
   }
   return true;
 }
@@ -645,7 +648,7 @@ __device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
 // LL has no polled tail: the producer records its final step count once.
 template <int SC>
 __device__ __forceinline__ void ll_close(Side& sd, uint64_t end_step) {
-  if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, end_step);
+  if (threadIdx.x == 0) st_u64<SC>(&sd.rx->tail, end_step);
 }
 
 // --------------------------------------------------------------- zero-copy
@@ -659,14 +662,14 @@ __device__ __forceinline__ uint32_t take_address(const ConnArgs& A, Side& sd, ui
   if (threadIdx.x < 64) {
     Deadline dl(ticks, A.status);
     uint64_t p;
-    while ((p = wave_load<SC>(&sd.lc->ptrx)) == 0) {
+    while ((p = wave_load<SC>(&sd.tx->ptrx)) == 0) {
       if ((err = dl.expired())) break;
       __builtin_amdgcn_s_sleep(1);
     }
     if (threadIdx.x == 0) {
       if (!err) {
         Order<SC, ORD>::acquire();
-        st_u64<SC>(&sd.lc->ptrx, 0);
+        st_u64<SC>(&sd.tx->ptrx, 0);
       }
       out = p;
     }
@@ -705,7 +708,7 @@ __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t 
       wait_vmcnt<0>();
     }
     if (wg_failed(sh, err, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
+    if (threadIdx.x == 0) st_u64<SC>(&sd.rx->tail, g + 1);
   }
   return true;
 }
@@ -728,7 +731,7 @@ __device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
                                   chunk_len(sd, S, j), S, A.lanes, w);
     O::release();
     if (wg_failed(sh, 0, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
+    if (threadIdx.x == 0) st_u64<SC>(&sd.rx->tail, g + 1);
   }
   return true;
 }
@@ -760,7 +763,7 @@ __device__ bool zcd_send(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
         wait_vmcnt<0>();
       }
       if (wg_failed(sh, 0, A.status)) return false;
-      if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
+      if (threadIdx.x == 0) st_u64<SC>(&sd.rx->tail, g + 1);
     }
     return true;
   }
@@ -770,7 +773,7 @@ __device__ bool zcd_send(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
                                         chunk_len(sd, S, j), S, P, w);
     O::release();
     if (wg_failed(sh, 0, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.lc->tail, g + 1);
+    if (threadIdx.x == 0) st_u64<SC>(&sd.rx->tail, g + 1);
   }
   return true;
 }
@@ -784,11 +787,11 @@ __device__ bool zcd_recv(const ConnArgs& A, Side& sd, uint64_t g0, uint64_t tick
   uint64_t done = g0;
   Deadline dl(ticks, A.status);
   while (done < end) {
-    const uint64_t t = ld_u64<SC>(&sd.lc->tail);
+    const uint64_t t = ld_u64<SC>(&sd.rx->tail);
     if (t > done) {
       Order<SC, ORD>::acquire();
       done = t;
-      st_u64<SC>(&sd.lc->head, t);
+      st_u64<SC>(&sd.tx->head, t);
       dl = Deadline(ticks, A.status);
       continue;
     }
@@ -862,18 +865,18 @@ __device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<M
   Deadline dl(ticks, A.status);
   while (ndone < total) {
     bool moved = false;
-    if (!cur.done && ld_u64<SC>(&sd.lc->ptrx) == 0) {
+    if (!cur.done && ld_u64<SC>(&sd.tx->ptrx) == 0) {
       const uint64_t addr = reinterpret_cast<uint64_t>(A.dst + cur.off + cur.r.beg + cur.j * S);
       O::release();
-      st_u64<SC>(&sd.lc->ptrx, addr);
+      st_u64<SC>(&sd.tx->ptrx, addr);
       ++cur.j;
       cur.settle(L, A, c, args.iters);
       moved = true;
     }
-    const uint64_t t = ld_u64<SC>(&sd.lc->tail);
+    const uint64_t t = ld_u64<SC>(&sd.rx->tail);
     if (t > sd.base + ndone) {
       O::acquire();
-      st_u64<SC>(&sd.lc->head, t);
+      st_u64<SC>(&sd.tx->head, t);
       ndone = t - sd.base;
       moved = true;
     }

@@ -12,7 +12,11 @@ namespace xfer {
 // has its own counters; every word sits on its own 128-byte line so the
 // producer's tail and the consumer's head never share a cache line.  The
 // receive side owns tail, the send side owns head and ptrExchange ("transport
-// 建立", p2pRecvConnect listing); here both live in one block per lane.
+// 建立", p2pRecvConnect listing).  A connection addresses them through two
+// arrays of blocks, the send side's (head, ptrExchange) and the receive
+// side's (tail, proxy tails): one array serving both in write mode, two
+// separate allocations under P2P read, where the SIMPLE FIFO follows the send
+// side's blocks in the same allocation.
 //
 // A relay connection (the shm transport's memcpy mode) adds the two host
 // proxies' tails: ytail (send proxy: step copied from the send FIFO into the
@@ -49,7 +53,8 @@ enum : int { kScopeAgent = 0, kScopeSystem = 1 };
 struct ConnArgs {
   uint8_t* fifo;    // channel c, slot s: fifo + (c * nslots + s) * slot_bytes (producer's)
   uint8_t* fifo_rx; // the FIFO the consumer drains: fifo, or a relay's receive FIFO
-  LaneCtrl* ctrl;   // [nch * lanes], lane (c, w) at c * lanes + w
+  LaneCtrl* ctrl_tx; // send side's blocks [nch * lanes], lane (c, w) at c * lanes + w
+  LaneCtrl* ctrl_rx; // receive side's blocks, same indexing (may equal ctrl_tx)
   Status* status; // device view of the pinned status block
   const uint8_t* src;
   uint8_t* dst;

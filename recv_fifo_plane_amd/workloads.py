@@ -4,6 +4,7 @@ the GPU parity tests (so the tests check exactly what the benchmark times).
 W1  SIMPLE, 1 channel, 8 x 128 KiB HBM FIFO, one producer/consumer pair, 4 MiB.
 W2  LL, 1 channel, 8 x 32 KiB, messages 8 B .. 64 KiB, in-kernel ping-pong.
 W3  SIMPLE, 32 channels x 8 x 512 KiB HBM, 1 GiB, 4 workgroups per channel side.
+    W3R: the same under P2P read (the FIFO in the send side's memory).
 W4  zero-copy through ptrExchange: one pair on 128 MiB, and a ring of 8
     logical endpoints built by the host schedule, endpoint r sending its
     128 MiB slice to (r + 1) mod 8, all edges in one launch.  W4D: the same
@@ -27,6 +28,9 @@ W2_SIZES = [8 << i for i in range(14)]  # 8 B .. 64 KiB
 
 W3 = dict(name="simple_32ch_1GiB", proto="simple", nchannels=32, nslots=8, slot_bytes=512 << 10,
           fifo_loc="device", wgs_per_channel=4, block_threads=512, nbytes=1 << 30)
+
+# The same workload with P2P read: the FIFO in the send side's memory.
+W3R = dict(W3, name="simple_32ch_1GiB_p2p_read", p2p_read=1)
 
 W4_PAIR = dict(name="zc_pair_128MiB", proto="zc", nchannels=32, nslots=1, slot_bytes=512 << 10,
                fifo_loc="device", wgs_per_channel=16, block_threads=128, nbytes=128 << 20)
@@ -53,7 +57,8 @@ W5R = dict(name="relay_4ch_4MiB", proto="simple", nchannels=4, nslots=8, slot_by
            fifo_loc="relay", wgs_per_channel=8, block_threads=1024, nbytes=512 << 20,
            total_bytes=2 << 30)
 
-_ATTRS = ("wgs_per_channel", "block_threads", "ctrl_loc", "timeout_ms", "xcd_pairing", "ordering")
+_ATTRS = ("wgs_per_channel", "block_threads", "ctrl_loc", "timeout_ms", "xcd_pairing", "ordering",
+          "p2p_read")
 
 
 def make_conn(cfg: dict, **override) -> X.Conn:

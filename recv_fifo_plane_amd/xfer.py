@@ -55,7 +55,7 @@ class xfer_attr(C.Structure):
         ("xcd_pairing", C.c_int),
         ("roles", C.c_int),
         ("ordering", C.c_int),
-        ("reserved", C.c_int),
+        ("p2p_read", C.c_int),
     ]
 
 
@@ -175,7 +175,7 @@ class Conn:
 
     def __init__(self, proto="simple", nchannels=1, nslots=8, slot_bytes=128 << 10,
                  fifo_loc="device", wgs_per_channel=0, block_threads=0, ctrl_loc=0,
-                 timeout_ms=0, xcd_pairing=0, roles=0, ordering=0, _handle=None):
+                 timeout_ms=0, xcd_pairing=0, roles=0, ordering=0, p2p_read=0, _handle=None):
         self.proto = PROTOS[proto] if isinstance(proto, str) else int(proto)
         self.nchannels = int(nchannels)
         self.nslots = int(nslots)
@@ -186,7 +186,7 @@ class Conn:
             self._h = _handle
             return
         attr = xfer_attr(int(wgs_per_channel), int(block_threads), int(ctrl_loc), int(timeout_ms),
-                         int(xcd_pairing), int(roles), int(ordering))
+                         int(xcd_pairing), int(roles), int(ordering), int(p2p_read))
         h = _vp()
         check(lib().xfer_conn_create_ex(self.proto, self.nchannels, self.nslots, self.slot_bytes,
                                         self.fifo_loc, C.byref(attr), C.byref(h)))

@@ -64,6 +64,24 @@ def test_relay_needs_host_control_words():
     assert "host memory" in xf.last_error()
 
 
+@pytest.mark.parametrize("proto,fifo_loc,attr", [
+    ("simple", "device", dict(p2p_read=2)),
+    ("simple", "device", dict(p2p_read=-1)),
+    ("ll", "device", dict(p2p_read=1)),
+    ("zc", "device", dict(p2p_read=1)),
+    ("zcd", "device", dict(p2p_read=1)),
+    ("simple", "host", dict(p2p_read=1)),
+    ("simple", "relay", dict(p2p_read=1)),
+    ("simple", "device", dict(p2p_read=1, ctrl_loc=X.XFER_CTRL_HOST)),
+])
+def test_p2p_read_is_simple_in_hbm_only(proto, fifo_loc, attr):
+    # P2P read moves the SIMPLE buffer to the send side; the pages give it no
+    # meaning for LL, zero-copy or host-memory FIFOs
+    with pytest.raises(xf.XferError) as e:
+        xf.Conn(proto, 1, 8, 128, fifo_loc, **attr)
+    assert e.value.status == X.XFER_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("attr", [dict(wgs_per_channel=17), dict(block_threads=96),
                                   dict(block_threads=2048), dict(ctrl_loc=3), dict(roles=3),
                                   dict(xcd_pairing=2)])

@@ -60,9 +60,9 @@ def test_w2_ll_pingpong(size):
     rev.close()
 
 
-def test_w3_simple_32_channels_1gib():
+@pytest.mark.parametrize("cfg", [W.W3, W.W3R], ids=["write", "p2p_read"])
+def test_w3_simple_32_channels_1gib(cfg):
     torch = _torch()
-    cfg = W.W3
     log("case: W3 " + str(cfg))
     A = synth.bf16_normal_bytes(cfg["nbytes"], synth.workload_seed(3))
     conn = W.make_conn(cfg)
