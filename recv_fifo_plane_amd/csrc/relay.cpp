@@ -65,7 +65,7 @@ void channel_steps(const RelayConfig& cfg, const RelayJob& job, int ch,
 // The HSA agents of the copies: the connection's GPU and a CPU.
 struct Agents {
   hsa_agent_t gpu{0}, cpu{0};
-  uint32_t bdf = 0;
+  uint32_t bdf = 0, domain = 0;
   bool have_gpu = false, have_cpu = false;
 };
 
@@ -78,10 +78,12 @@ hsa_status_t find_agents(hsa_agent_t a, void* p) {
     ag->cpu = a;
     ag->have_cpu = true;
   } else if (type == HSA_DEVICE_TYPE_GPU && !ag->have_gpu) {
-    uint32_t bdf = 0;
+    uint32_t bdf = 0, domain = 0;
     if (hsa_agent_get_info(a, static_cast<hsa_agent_info_t>(HSA_AMD_AGENT_INFO_BDFID), &bdf) ==
             HSA_STATUS_SUCCESS &&
-        bdf == ag->bdf) {
+        hsa_agent_get_info(a, static_cast<hsa_agent_info_t>(HSA_AMD_AGENT_INFO_DOMAIN),
+                           &domain) == HSA_STATUS_SUCCESS &&
+        bdf == ag->bdf && domain == ag->domain) {
       ag->gpu = a;
       ag->have_gpu = true;
     }
@@ -300,10 +302,12 @@ class Relay {
 
 int relay_start(const RelayConfig& cfg, Relay** out, std::string* err) {
   *out = nullptr;
-  // The GPU's HSA agent is the one at the device's PCI bus/device/function.
-  int bus = 0, dev = 0;
+  // The GPU's HSA agent is the one at the device's PCI domain and
+  // bus/device (function 0).
+  int bus = 0, dev = 0, domain = 0;
   if (hipDeviceGetAttribute(&bus, hipDeviceAttributePciBusId, cfg.device) != hipSuccess ||
-      hipDeviceGetAttribute(&dev, hipDeviceAttributePciDeviceId, cfg.device) != hipSuccess) {
+      hipDeviceGetAttribute(&dev, hipDeviceAttributePciDeviceId, cfg.device) != hipSuccess ||
+      hipDeviceGetAttribute(&domain, hipDeviceAttributePciDomainId, cfg.device) != hipSuccess) {
     *err = "relay: cannot read the device's PCI location";
     return XFER_ERR_HIP;
   }
@@ -320,6 +324,7 @@ int relay_start(const RelayConfig& cfg, Relay** out, std::string* err) {
   r->hsa_up = true;
   Agents ag;
   ag.bdf = (uint32_t(bus) << 8) | (uint32_t(dev) << 3);
+  ag.domain = uint32_t(domain);
   int rc = XFER_OK;
   if (hsa_iterate_agents(find_agents, &ag) != HSA_STATUS_SUCCESS || !ag.have_gpu || !ag.have_cpu) {
     *err = "relay: no HSA agent for the device and the host";
