@@ -144,9 +144,11 @@ typedef struct xfer_conn xfer_conn;
  * block holding head, tail and ptrExchange, zeroed (the receive side's
  * connect wires tail to its own block and head/ptrExchange to the send
  * side's, "transport建立", p2pRecvConnect listing; the shm transport keeps
- * the FIFO and tail in host memory, shmRecvConnect listing).  The
- * connection's device descriptor is uploaded to HBM ("Intra-Node Transport
- * (P2P)" section 3, connector mirror).
+ * the FIFO and tail in host memory, shmRecvConnect listing).  With
+ * attr->p2p_read the send side's blocks and the SIMPLE FIFO after them form
+ * one allocation and the receive side's blocks (tail) another
+ * (p2pSendSetup listing).  The connection's device descriptor is uploaded to
+ * HBM ("Intra-Node Transport (P2P)" section 3, connector mirror).
  *   proto       xfer_proto.
  *   nchannels   1..64 (64-bit channel masks).
  *   nslots      >= 1 FIFO slots per channel (ignored by zero-copy).
