@@ -105,14 +105,19 @@ struct Order {
   }
 };
 
+// Lane 0's v for the whole wave.  readfirstlane works on (signed) 32-bit
+// ints, so each half is held as uint32_t and widening zero-extends it.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Every lane loads the same word (one request per wave); the value is made
 // wave-uniform explicitly.
 template <int SC>
 __device__ __forceinline__ uint64_t wave_load(const uint64_t* p) {
-  const uint64_t v = ld_u64<SC>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+  return uniform_u64(ld_u64<SC>(p));
 }
 
 __device__ __forceinline__ void raise_err(Status* st, uint32_t code) {
@@ -654,17 +659,21 @@ __device__ __forceinline__ void ll_close(Side& sd, uint64_t end_step) {
 // --------------------------------------------------------------- zero-copy
 // Wave 0 waits for a published destination (the base of the step's chunk in
 // B), takes it and clears the word; the address reaches the other waves
-// through LDS (`out`) after the caller's barrier.
+// through LDS (`out`) after the caller's barrier.  `first` is the value of
+// a poll of the word that wave 0 issued earlier (0: none, or nothing was
+// published yet), so that accesses issued after that poll do not delay it.
 template <int SC, int ORD>
 __device__ __forceinline__ uint32_t take_address(const ConnArgs& A, Side& sd, uint64_t ticks,
-                                                 uint64_t& out) {
+                                                 uint64_t& out, uint64_t first = 0) {
   uint32_t err = 0;
   if (threadIdx.x < 64) {
-    Deadline dl(ticks, A.status);
-    uint64_t p;
-    while ((p = wave_load<SC>(&sd.tx->ptrx)) == 0) {
-      if ((err = dl.expired())) break;
-      __builtin_amdgcn_s_sleep(1);
+    uint64_t p = uniform_u64(first);
+    if (p == 0) {
+      Deadline dl(ticks, A.status);
+      while ((p = wave_load<SC>(&sd.tx->ptrx)) == 0) {
+        if ((err = dl.expired())) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
     }
     if (threadIdx.x == 0) {
       if (!err) {
@@ -683,7 +692,10 @@ __device__ __forceinline__ uint32_t take_address(const ConnArgs& A, Side& sd, ui
 // sees step j's taken, so wave 0 takes it while step j's stores drain
 // instead of after step j's tail: two LDS words, by step parity, keep the
 // other waves' read of step j's address clear of that write (the barrier
-// of step j separates the read of a word from its next write).
+// of step j separates the read of a word from its next write).  Wave 0's
+// first poll of the word goes out before step j+1's source loads: vector
+// memory completes in issue order, so a poll issued after them would wait
+// for all of them.
 template <int SC, int ORD>
 __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
                               const uint8_t* src, uint64_t ticks, Shared& sh) {
@@ -701,8 +713,10 @@ __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t 
     lane_tail<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, p, L, S, P, w);
     uint32_t err = 0;
     if (j + 1 < sd.r.k) {
+      uint64_t first = 0;
+      if (threadIdx.x < 64) first = ld_u64<SC>(&sd.tx->ptrx);
       batch_load<kPolNT, true>(b, src + sd.r.beg + (j + 1) * S, chunk_len(sd, S, j + 1), S, P, w);
-      err = take_address<SC, ORD>(A, sd, ticks, sh.ptr[(j + 1) & 1]);
+      err = take_address<SC, ORD>(A, sd, ticks, sh.ptr[(j + 1) & 1], first);
       wait_vmcnt<kUnroll>();
     } else {
       wait_vmcnt<0>();

@@ -101,3 +101,36 @@ def test_ll_lanes_that_own_no_lines(fifo_loc, nslots):
     # and run ahead of their producers, whose credit test must still hold
     run_transfers("ll", 2, nslots, 2048, [100_000, 5, 40_000], fifo_loc=fifo_loc, lanes=4,
                   kind="int32")
+
+
+@pytest.mark.parametrize("proto", ["zc", "zcd"])
+@pytest.mark.parametrize("lanes,block", [(16, 128), (2, 64)])
+def test_zero_copy_destination_with_bit31_of_the_low_word_set(proto, lanes, block):
+    # Destination addresses travel through ptrExchange and are made
+    # wave-uniform 32 bits at a time; an address whose low word has bit 31
+    # set must come back whole (a sign-extended half would point nowhere).
+    import numpy as np
+    import torch
+
+    import recv_fifo_plane_amd as xf
+    import synth
+    from gpu_cases import log
+    n, guard = 8 << 20, 4096
+    big = torch.zeros((2 << 30) + n + 2 * guard, dtype=torch.uint8, device="cuda")
+    low = big.data_ptr() & 0xFFFFFFFF
+    off = guard + (0 if low + guard >= 1 << 31 else (1 << 31) - low)
+    dst = big.data_ptr() + off
+    assert (dst & 0xFFFFFFFF) >= 1 << 31 and off + n + guard <= big.numel()
+    log("case: %s lanes=%d block=%d dst=%#x" % (proto, lanes, block, dst))
+    A = synth.uint8_uniform(n, 2024)
+    a = torch.from_numpy(A).to("cuda")
+    conn = xf.Conn(proto, 4, 1, 512 << 10, wgs_per_channel=lanes, block_threads=block)
+    for _ in range(2):
+        conn.run(a, dst, n)
+    torch.cuda.synchronize()
+    assert conn.query(0)["error"] == 0
+    assert np.array_equal(big[off:off + n].cpu().numpy(), A)
+    assert int(big[off - guard:off].count_nonzero()) == 0
+    assert int(big[off + n:off + n + guard].count_nonzero()) == 0
+    conn.close()
+    del big
