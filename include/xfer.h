@@ -257,6 +257,46 @@ int xfer_conn_read_fifo_ex(const xfer_conn* c, int which, int channel, void* hos
 int xfer_conn_query_relay(const xfer_conn* c, int channel, uint64_t* send_proxy_tail,
                           uint64_t* recv_proxy_tail);
 
+/* ------------------------------------------------------------ step trace
+ * Debug aid, off by default (the tracing that the pages' INFO/TRACE logs
+ * give the host side, here for the device side).  xfer_conn_set_trace
+ * gives the connection a caller-owned DEVICE buffer of nrecords records;
+ * runs queued afterwards (until it is set to NULL) stamp two events per step
+ * and side, written by the side's first thread:
+ *   producer  ACQUIRE  credit obtained (value: head seen), or for zero-copy
+ *                      the destination taken from ptrExchange (value: its
+ *                      address) and for zero-copy direct the step's own
+ *                      destination;
+ *             PUBLISH  just before tail = g+1 is stored (value: g+1); for LL,
+ *                      just before the step's lines are stored;
+ *   consumer  ACQUIRE  the step is ready (value: tail seen; LL: the flag;
+ *                      zero-copy receiver: the address it publishes, stamped
+ *                      before it is published);
+ *             PUBLISH  just before head is stored (value: the head stored).
+ * The buffer is split into nchannels x lanes x 2 rings of
+ * nrecords / (nchannels x lanes x 2) records: ring (c, w, side) starts at
+ * record ((c * lanes + w) * 2 + side) * per, and event e of global step g
+ * goes to its slot (2g + e) mod per, so each ring keeps the latest per / 2
+ * steps.  Slots never written keep the caller's contents.  Times are
+ * s_memrealtime ticks (the device's constant wall clock, 100 MHz on MI355X),
+ * comparable across workgroups: a PUBLISH precedes every ACQUIRE that
+ * depends on it.  The buffer must stay valid until the traced runs complete.
+ * Errors: INVALID_ARG (NULL connection, misaligned buffer, fewer than 2
+ * records per ring). */
+typedef struct {
+  uint64_t time;    /* s_memrealtime ticks */
+  uint64_t step;    /* global step g */
+  uint64_t value;   /* see above */
+  uint32_t channel;
+  uint16_t lane;
+  uint8_t side;     /* 0 producer, 1 consumer or receiver */
+  uint8_t event;    /* xfer_trace_event */
+} xfer_trace_rec;
+
+typedef enum { XFER_TRACE_ACQUIRE = 0, XFER_TRACE_PUBLISH = 1 } xfer_trace_event;
+
+int xfer_conn_set_trace(xfer_conn* c, void* records, size_t nrecords);
+
 /* Sets the connection's host-side abort word; every in-kernel wait of a
  * running or later launch on it ends with XFER_ERR_ABORTED. */
 int xfer_conn_abort(xfer_conn* c);

@@ -192,6 +192,19 @@ def partition(nbytes: int, nchannels: int) -> tuple[list[int], list[int]]:
 
 
 # ---------------------------------------------------------------- protocol
+def zero_copy_offsets(proto, nbytes: int, nchannels: int, slot_bytes: int) -> list[list[int]]:
+    """Per channel, the destination offset of each step of one transfer, in
+    step order: the addresses a zero-copy receiver publishes through
+    ptrExchange, one per step, and the ones a zero-copy-direct producer
+    writes to (transfer page, zero copy, both kinds; reading R7).  The
+    simulator holds its producer to exactly this sequence: taking any other
+    address is the violation "producer took an address not published for
+    its step"."""
+    beg, ln = partition(nbytes, nchannels)
+    S = step_bytes(proto, slot_bytes)
+    return [[b + j * S for j in range((n + S - 1) // S)] for b, n in zip(beg, ln)]
+
+
 class Conn:
     """A simulated connection; its counters and FIFO persist across runs."""
 

@@ -39,8 +39,15 @@ struct xfer_conn {
   void* ctrl_rx_mem = nullptr;        // P2P read: the receive side's own allocation
   xfer::Status* status_host = nullptr;
   xfer::Status* status_dev = nullptr;
+  xfer::TraceRec* trace = nullptr;  // caller's step-trace buffer (device), or nullptr
+  uint32_t trace_per = 0;           // records per (channel, lane, side) ring
   std::vector<uint64_t> steps;   // per channel, host bookkeeping of completed steps
 };
+
+static_assert(sizeof(xfer_trace_rec) == sizeof(xfer::TraceRec) &&
+                  offsetof(xfer_trace_rec, value) == offsetof(xfer::TraceRec, value) &&
+                  offsetof(xfer_trace_rec, event) == offsetof(xfer::TraceRec, event),
+              "the public trace record and the kernels' must share one layout");
 
 namespace xfer {
 
@@ -209,6 +216,8 @@ ConnArgs conn_args(const xfer_conn* c, const void* src, void* dst, uint64_t nbyt
   a.fifo = c->fifo;
   a.fifo_rx = c->fifo_rx ? c->fifo_rx : c->fifo;
   a.relay = c->fifo_rx ? 1u : 0u;
+  a.trace = c->trace;
+  a.trace_per = c->trace_per;
   a.ctrl_tx = c->ctrl;
   a.ctrl_rx = c->ctrl_rx;
   a.status = c->status_dev;
@@ -242,11 +251,11 @@ uint32_t grid_of(int pairing, uint32_t total) { return pairing ? (total + 15u) &
 // queried once: the runtime query costs far more than a launch.
 int resident_capacity(const Variant& v, int kind, int block, int* cap) {
   static std::mutex mu;
-  static std::map<std::array<int, 7>, int> cache;
+  static std::map<std::array<int, 8>, int> cache;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  const std::array<int, 7> key{dev, v.proto, v.scope, v.ordering, v.aligned, kind, block};
+  const std::array<int, 8> key{dev, v.proto, v.scope, v.ordering, v.aligned, v.trace, kind, block};
   {
     std::lock_guard<std::mutex> lk(mu);
     auto it = cache.find(key);
@@ -569,7 +578,7 @@ extern "C" int xfer_conn_destroy(xfer_conn* c) {
 }
 
 static Variant variant_of(const xfer_conn* c, bool aligned) {
-  return Variant{c->proto, c->scope, c->ordering, aligned ? 1 : 0};
+  return Variant{c->proto, c->scope, c->ordering, aligned ? 1 : 0, c->trace ? 1 : 0};
 }
 
 extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nbytes, int iters,
@@ -722,7 +731,9 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
   }
   if (!live) return XFER_OK;
   DeviceGuard g(first->device);
-  const Variant v = variant_of(first, aligned);
+  Variant v = variant_of(first, aligned);
+  for (int i = 0; i < n; ++i)
+    if (conns[i]->trace) v.trace = 1;  // untraced connections pass a null buffer
   const uint32_t grid = grid_of(first->xcd_pairing, total);
   int rc = check_resident(v, 1, first->block, grid, "xfer_run_batch");
   if (rc) return rc;
@@ -771,7 +782,8 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
   const int scope = (fwd->scope == kScopeSystem || rev->scope == kScopeSystem) ? kScopeSystem
                                                                                : kScopeAgent;
   const Variant v{fwd->proto, scope, fwd->ordering,
-                  (aligned16(a) && aligned16(b) && aligned16(cbuf)) ? 1 : 0};
+                  (aligned16(a) && aligned16(b) && aligned16(cbuf)) ? 1 : 0,
+                  (fwd->trace || rev->trace) ? 1 : 0};
   rc = check_resident(v, 2, fwd->block, total, "xfer_run_pingpong");
   if (rc) return rc;
   PingArgs args;
@@ -881,6 +893,26 @@ extern "C" int xfer_conn_query_relay(const xfer_conn* c, int channel, uint64_t* 
   const LaneCtrl* l = static_cast<const LaneCtrl*>(c->ctrl_mem) + size_t(channel) * size_t(c->lanes);
   *send_proxy_tail = __atomic_load_n(&l[0].ytail, __ATOMIC_ACQUIRE);
   *recv_proxy_tail = __atomic_load_n(&l[0].gtail, __ATOMIC_ACQUIRE);
+  return XFER_OK;
+}
+
+extern "C" int xfer_conn_set_trace(xfer_conn* c, void* records, size_t nrecords) {
+  if (!c) return fail(XFER_ERR_INVALID_ARG, "xfer_conn_set_trace: NULL connection");
+  if (!records) {
+    c->trace = nullptr;
+    c->trace_per = 0;
+    return XFER_OK;
+  }
+  if (reinterpret_cast<uintptr_t>(records) % alignof(TraceRec))
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_set_trace: records must be 8-byte aligned");
+  const size_t rings = size_t(c->nch) * size_t(c->lanes) * 2;
+  const size_t per = nrecords / rings;
+  if (per < 2 || per > 0xFFFFFFFFu)
+    return fail(XFER_ERR_INVALID_ARG,
+                "xfer_conn_set_trace: need at least 2 records per channel, lane and side (" +
+                    std::to_string(2 * rings) + " in all)");
+  c->trace = static_cast<TraceRec*>(records);
+  c->trace_per = uint32_t(per);
   return XFER_OK;
 }
 

@@ -321,17 +321,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 struct Side {
   LaneCtrl* tx;     // the send side's block of this lane: head, ptrExchange
   LaneCtrl* rx;     // the receive side's block: tail (and a relay's proxy tails)
+  TraceRec* tr;     // this (channel, lane, side)'s step-trace ring, or nullptr
   uint64_t base;    // step counter at launch start (own counter: tail or head)
   uint64_t seen;    // last observed peer counter (wave-uniform)
   Range r;          // the channel's range and steps in the current message
 };
 
+// TR: the kernel variant that writes the step trace.  Without it the trace
+// ring is a constant null, so every trace branch folds away.
+template <bool TR>
 __device__ __forceinline__ Side make_side(const ConnArgs& A, uint32_t c, uint32_t w, bool producer,
                                           int sc) {
   Side s;
   const uint64_t lane = static_cast<uint64_t>(c) * A.lanes + w;
   s.tx = A.ctrl_tx + lane;
   s.rx = A.ctrl_rx + lane;
+  s.tr = TR && A.trace ? A.trace + (lane * 2 + (producer ? 0u : 1u)) * A.trace_per : nullptr;
   s.r = Range{0, 0, 0};  // set per message
   // A side is the only writer of its own counter, and the previous launch
   // that wrote it has completed, so a plain coherent load reads it.
@@ -339,6 +344,32 @@ __device__ __forceinline__ Side make_side(const ConnArgs& A, uint32_t c, uint32_
   s.base = sc == kScopeSystem ? wave_load<kScopeSystem>(own) : wave_load<kScopeAgent>(own);
   s.seen = 0;
   return s;
+}
+
+// Step trace, written by thread 0 of a side when the connection has a trace
+// buffer: event 0 when the step is acquired (credit, a destination, or the
+// data ready), event 1 just before the step is published (tail or head),
+// at slots 2g and 2g+1 of the side's ring (modulo its size).  The ring's
+// index in the buffer names the channel, lane and side.
+__device__ __forceinline__ void trace_write(TraceRec* base, uint32_t per, uint32_t lanes,
+                                            TraceRec* ring, uint64_t g, uint32_t ev,
+                                            uint64_t value) {
+  const uint64_t region = static_cast<uint64_t>(ring - base) / per;
+  const uint64_t lane = region >> 1;
+  TraceRec r;
+  r.time = wall_clock64();
+  r.step = g;
+  r.value = value;
+  r.channel = static_cast<uint32_t>(lane / lanes);
+  r.lane = static_cast<uint16_t>(lane % lanes);
+  r.side = static_cast<uint8_t>(region & 1u);
+  r.event = static_cast<uint8_t>(ev);
+  ring[(2 * g + ev) % per] = r;
+}
+
+__device__ __forceinline__ void trace_step(const ConnArgs& A, const Side& sd, uint64_t g,
+                                           uint32_t ev, uint64_t value) {
+  if (sd.tr != nullptr) trace_write(A.trace, A.trace_per, A.lanes, sd.tr, g, ev, value);
 }
 
 // Shared by the waves of a workgroup: the first failure seen by any wave.
@@ -448,6 +479,7 @@ __device__ bool simple_send_piped(const ConnArgs& A, uint32_t c, uint32_t w, Sid
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
     const uint32_t err = wait_credit<SC, ORD, true>(A, sd, g, ticks, sh);
+    if (!err && threadIdx.x == 0) trace_step(A, sd, g, 0, sd.seen);
     if (!err) {
       const uint32_t L = chunk_len(sd, S, j);
       uint8_t* slot = slot_of(A, c, g);
@@ -461,7 +493,10 @@ __device__ bool simple_send_piped(const ConnArgs& A, uint32_t c, uint32_t w, Sid
       }
     }
     if (wg_failed(sh, err, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.rx->tail, g + 1);
+    if (threadIdx.x == 0) {
+      trace_step(A, sd, g, 1, g + 1);
+      st_u64<SC>(&sd.rx->tail, g + 1);
+    }
   }
   return true;
 }
@@ -480,13 +515,17 @@ __device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
     const uint32_t err = wait_credit<SC, ORD, true>(A, sd, g, ticks, sh);
+    if (!err && threadIdx.x == 0) trace_step(A, sd, g, 0, sd.seen);
     if (!err) {
       lane_copy<kPolNT, O::kShared, false>(src + sd.r.beg + j * S, slot_of(A, c, g), chunk_len(sd, S, j),
                                     S, A.lanes, w);
       O::release();
     }
     if (wg_failed(sh, err, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.rx->tail, g + 1);
+    if (threadIdx.x == 0) {
+      trace_step(A, sd, g, 1, g + 1);
+      st_u64<SC>(&sd.rx->tail, g + 1);
+    }
   }
   return true;
 }
@@ -515,6 +554,7 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
         sd.seen = t;
       }
     }
+    if (!err && threadIdx.x == 0) trace_step(A, sd, g, 0, sd.seen);
     if (!err) {
       lane_copy<O::kShared, kPolNT, false>(slot_rx(A, c, g), dst + sd.r.beg + j * S,
                                            chunk_len(sd, S, j), S, A.lanes, w);
@@ -524,7 +564,10 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
       if constexpr (ORD == kOrdFenced) O::release();
     }
     if (wg_failed(sh, err, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.tx->head, g + 1);
+    if (threadIdx.x == 0) {
+      trace_step(A, sd, g, 1, g + 1);
+      st_u64<SC>(&sd.tx->head, g + 1);
+    }
   }
   return true;
 }
@@ -567,6 +610,10 @@ __device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
     uint64_t* lines = reinterpret_cast<uint64_t*>(slot_of(A, c, g));
     const uint8_t* s = src + sd.r.beg + j * S;
     const uint64_t flag = static_cast<uint64_t>(static_cast<uint32_t>(g + 1)) << 32;
+    if (threadIdx.x == 0) {  // the lines are the publication: stamp before thread 0's
+      trace_step(A, sd, g, 0, sd.seen);
+      trace_step(A, sd, g, 1, g + 1);
+    }
     if (nl <= nthr * P) {  // one pass: at most one line per thread
       const uint32_t i = w * nthr + threadIdx.x;
       if (i < nl) st_u64<SC>(&lines[i], flag | ll_src_word<AL>(s, L, i));
@@ -645,7 +692,11 @@ __device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
     // ordering keeps its release fence.
     if constexpr (ORD == kOrdFenced) O::release();
     if (wg_failed(sh, err, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.tx->head, g + 1);
+    if (threadIdx.x == 0) {
+      trace_step(A, sd, g, 0, static_cast<uint64_t>(want));  // every line of the step seen
+      trace_step(A, sd, g, 1, g + 1);
+      st_u64<SC>(&sd.tx->head, g + 1);
+    }
   }
   return true;
 }
@@ -705,6 +756,7 @@ __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t 
   Batch b;
   batch_load<kPolNT, true>(b, src + sd.r.beg, chunk_len(sd, S, 0), S, P, w);
   if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh.ptr[0]), A.status)) return false;
+  if (threadIdx.x == 0) trace_step(A, sd, g0, 0, sh.ptr[0]);
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
     uint8_t* p = reinterpret_cast<uint8_t*>(sh.ptr[j & 1]);
@@ -717,12 +769,16 @@ __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t 
       if (threadIdx.x < 64) first = ld_u64<SC>(&sd.tx->ptrx);
       batch_load<kPolNT, true>(b, src + sd.r.beg + (j + 1) * S, chunk_len(sd, S, j + 1), S, P, w);
       err = take_address<SC, ORD>(A, sd, ticks, sh.ptr[(j + 1) & 1], first);
+      if (!err && threadIdx.x == 0) trace_step(A, sd, g + 1, 0, sh.ptr[(j + 1) & 1]);
       wait_vmcnt<kUnroll>();
     } else {
       wait_vmcnt<0>();
     }
     if (wg_failed(sh, err, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.rx->tail, g + 1);
+    if (threadIdx.x == 0) {
+      trace_step(A, sd, g, 1, g + 1);
+      st_u64<SC>(&sd.rx->tail, g + 1);
+    }
   }
   return true;
 }
@@ -741,11 +797,15 @@ __device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
     if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh.ptr[0]), A.status)) return false;
+    if (threadIdx.x == 0) trace_step(A, sd, g, 0, sh.ptr[0]);
     lane_copy<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, reinterpret_cast<uint8_t*>(sh.ptr[0]),
                                   chunk_len(sd, S, j), S, A.lanes, w);
     O::release();
     if (wg_failed(sh, 0, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.rx->tail, g + 1);
+    if (threadIdx.x == 0) {
+      trace_step(A, sd, g, 1, g + 1);
+      st_u64<SC>(&sd.rx->tail, g + 1);
+    }
   }
   return true;
 }
@@ -768,6 +828,7 @@ __device__ bool zcd_send(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
       const uint64_t g = g0 + j;
       uint8_t* p = dst + sd.r.beg + j * S;
       const uint32_t L = chunk_len(sd, S, j);
+      if (threadIdx.x == 0) trace_step(A, sd, g, 0, reinterpret_cast<uint64_t>(p));
       batch_store<O::kShared, true>(b, p, L, S, P, w);
       lane_tail<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, p, L, S, P, w);
       if (j + 1 < sd.r.k) {
@@ -777,17 +838,24 @@ __device__ bool zcd_send(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
         wait_vmcnt<0>();
       }
       if (wg_failed(sh, 0, A.status)) return false;
-      if (threadIdx.x == 0) st_u64<SC>(&sd.rx->tail, g + 1);
+      if (threadIdx.x == 0) {
+        trace_step(A, sd, g, 1, g + 1);
+        st_u64<SC>(&sd.rx->tail, g + 1);
+      }
     }
     return true;
   }
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
+    if (threadIdx.x == 0) trace_step(A, sd, g, 0, reinterpret_cast<uint64_t>(dst + sd.r.beg + j * S));
     lane_copy<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, dst + sd.r.beg + j * S,
                                         chunk_len(sd, S, j), S, P, w);
     O::release();
     if (wg_failed(sh, 0, A.status)) return false;
-    if (threadIdx.x == 0) st_u64<SC>(&sd.rx->tail, g + 1);
+    if (threadIdx.x == 0) {
+      trace_step(A, sd, g, 1, g + 1);
+      st_u64<SC>(&sd.rx->tail, g + 1);
+    }
   }
   return true;
 }
@@ -804,6 +872,10 @@ __device__ bool zcd_recv(const ConnArgs& A, Side& sd, uint64_t g0, uint64_t tick
     const uint64_t t = ld_u64<SC>(&sd.rx->tail);
     if (t > done) {
       Order<SC, ORD>::acquire();
+      for (uint64_t q = done; sd.tr != nullptr && q < t; ++q) {
+        trace_step(A, sd, q, 0, t);
+        trace_step(A, sd, q, 1, t);
+      }
       done = t;
       st_u64<SC>(&sd.tx->head, t);
       dl = Deadline(ticks, A.status);
@@ -875,12 +947,13 @@ __device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<M
     cur.load(L, A, c);
     cur.settle(L, A, c, args.iters);
   }
-  uint64_t ndone = 0;
+  uint64_t ndone = 0, npub = 0;
   Deadline dl(ticks, A.status);
   while (ndone < total) {
     bool moved = false;
     if (!cur.done && ld_u64<SC>(&sd.tx->ptrx) == 0) {
       const uint64_t addr = reinterpret_cast<uint64_t>(A.dst + cur.off + cur.r.beg + cur.j * S);
+      trace_step(A, sd, sd.base + npub++, 0, addr);
       O::release();
       st_u64<SC>(&sd.tx->ptrx, addr);
       ++cur.j;
@@ -890,6 +963,7 @@ __device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<M
     const uint64_t t = ld_u64<SC>(&sd.rx->tail);
     if (t > sd.base + ndone) {
       O::acquire();
+      for (uint64_t q = sd.base + ndone; sd.tr != nullptr && q < t; ++q) trace_step(A, sd, q, 1, t);
       st_u64<SC>(&sd.tx->head, t);
       ndone = t - sd.base;
       moved = true;
@@ -922,7 +996,7 @@ __device__ __forceinline__ uint32_t logical_wg(uint32_t remap, uint32_t total) {
   return 2u * ((b % 8u) * half + s % half) + s / half;
 }
 
-template <int PROTO, int SC, int ORD, bool AL, int MAXB>
+template <int PROTO, int SC, int ORD, bool AL, int MAXB, bool TR>
 __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
   __shared__ Shared sh;
   if (threadIdx.x == 0) sh.err = 0;
@@ -938,7 +1012,7 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
   const uint32_t c = pair / A.lanes, w = pair % A.lanes;
   if (c >= A.nch) return;  // padding of a paired launch (its grid is a multiple of 16)
   if (!((A.roles >> role) & 1u)) return;  // side switched off for fault injection
-  Side sd = make_side(A, c, w, role == 0, SC);
+  Side sd = make_side<TR>(A, c, w, role == 0, SC);
   const uint64_t ticks = args.timeout_ticks;
   if constexpr (PROTO == kProtoZC) {
     if (role == 1) {
@@ -977,7 +1051,7 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
 
 // Ping-pong: pair side 0 is endpoint X (send on fwd, then receive on rev),
 // side 1 is endpoint Y (receive on fwd into b, then send b on rev).
-template <int PROTO, int SC, int ORD, bool AL>
+template <int PROTO, int SC, int ORD, bool AL, bool TR>
 __global__ void __launch_bounds__(1024) ping_kernel(PingArgs args) {
   __shared__ Shared sh;
   if (threadIdx.x == 0) sh.err = 0;
@@ -988,8 +1062,8 @@ __global__ void __launch_bounds__(1024) ping_kernel(PingArgs args) {
   const ConnArgs& R = args.rev;
   const uint32_t c = pair / F.lanes, w = pair % F.lanes;
   if (c >= F.nch) return;
-  Side fs = make_side(F, c, w, side == 0, SC);
-  Side rs = make_side(R, c, w, side == 1, SC);
+  Side fs = make_side<TR>(F, c, w, side == 0, SC);
+  Side rs = make_side<TR>(R, c, w, side == 1, SC);
   fs.r = chan_range(F.nbytes, F.nch, c, F.step_bytes);
   rs.r = chan_range(R.nbytes, R.nch, c, R.step_bytes);
   const uint64_t k = fs.r.k;
@@ -1028,21 +1102,26 @@ template <int MAXB>
 using RunFn = void (*)(RunArgs<MAXB>);
 using PingFn = void (*)(PingArgs);
 
-template <int MAXB, int P, int SC, int ORD>
+template <int MAXB, int P, int SC, int ORD, bool TR>
 RunFn<MAXB> pick_run_al(bool al) {
-  return al ? run_kernel<P, SC, ORD, true, MAXB> : run_kernel<P, SC, ORD, false, MAXB>;
+  return al ? run_kernel<P, SC, ORD, true, MAXB, TR> : run_kernel<P, SC, ORD, false, MAXB, TR>;
 }
 
-template <int MAXB, int P, int SC>
+template <int MAXB, int P, int SC, bool TR>
 RunFn<MAXB> pick_run_ord(int ord, bool al) {
-  return ord == kOrdFenced ? pick_run_al<MAXB, P, SC, kOrdFenced>(al)
-                           : pick_run_al<MAXB, P, SC, kOrdCoherent>(al);
+  return ord == kOrdFenced ? pick_run_al<MAXB, P, SC, kOrdFenced, TR>(al)
+                           : pick_run_al<MAXB, P, SC, kOrdCoherent, TR>(al);
+}
+
+template <int MAXB, int P, bool TR>
+RunFn<MAXB> pick_run_tr(const Variant& v) {
+  return v.scope == kScopeSystem ? pick_run_ord<MAXB, P, kScopeSystem, TR>(v.ordering, v.aligned)
+                                 : pick_run_ord<MAXB, P, kScopeAgent, TR>(v.ordering, v.aligned);
 }
 
 template <int MAXB, int P>
 RunFn<MAXB> pick_run_sc(const Variant& v) {
-  return v.scope == kScopeSystem ? pick_run_ord<MAXB, P, kScopeSystem>(v.ordering, v.aligned)
-                                 : pick_run_ord<MAXB, P, kScopeAgent>(v.ordering, v.aligned);
+  return v.trace ? pick_run_tr<MAXB, P, true>(v) : pick_run_tr<MAXB, P, false>(v);
 }
 
 template <int MAXB>
@@ -1055,21 +1134,26 @@ RunFn<MAXB> pick_run(const Variant& v) {
   }
 }
 
-template <int P, int SC, int ORD>
+template <int P, int SC, int ORD, bool TR>
 PingFn pick_ping_al(bool al) {
-  return al ? ping_kernel<P, SC, ORD, true> : ping_kernel<P, SC, ORD, false>;
+  return al ? ping_kernel<P, SC, ORD, true, TR> : ping_kernel<P, SC, ORD, false, TR>;
 }
 
-template <int P, int SC>
+template <int P, int SC, bool TR>
 PingFn pick_ping_ord(int ord, bool al) {
-  return ord == kOrdFenced ? pick_ping_al<P, SC, kOrdFenced>(al)
-                           : pick_ping_al<P, SC, kOrdCoherent>(al);
+  return ord == kOrdFenced ? pick_ping_al<P, SC, kOrdFenced, TR>(al)
+                           : pick_ping_al<P, SC, kOrdCoherent, TR>(al);
+}
+
+template <int P, bool TR>
+PingFn pick_ping_tr(const Variant& v) {
+  return v.scope == kScopeSystem ? pick_ping_ord<P, kScopeSystem, TR>(v.ordering, v.aligned)
+                                 : pick_ping_ord<P, kScopeAgent, TR>(v.ordering, v.aligned);
 }
 
 template <int P>
 PingFn pick_ping_sc(const Variant& v) {
-  return v.scope == kScopeSystem ? pick_ping_ord<P, kScopeSystem>(v.ordering, v.aligned)
-                                 : pick_ping_ord<P, kScopeAgent>(v.ordering, v.aligned);
+  return v.trace ? pick_ping_tr<P, true>(v) : pick_ping_tr<P, false>(v);
 }
 
 PingFn pick_ping(const Variant& v) {

@@ -46,6 +46,18 @@ struct alignas(128) Status {
   uint32_t pad1[31];
 };
 
+// One step-trace record (the public xfer_trace_rec, same layout).
+struct TraceRec {
+  uint64_t time;     // s_memrealtime ticks
+  uint64_t step;     // global step g
+  uint64_t value;    // event-specific
+  uint32_t channel;
+  uint16_t lane;
+  uint8_t side;      // 0 producer, 1 consumer / receiver
+  uint8_t event;     // 0 acquire, 1 publish
+};
+static_assert(sizeof(TraceRec) == 32, "trace record layout");
+
 enum : uint32_t { kProtoSimple = 0, kProtoLL = 1, kProtoZC = 2, kProtoZCD = 3 };
 enum : int { kScopeAgent = 0, kScopeSystem = 1 };
 
@@ -64,6 +76,9 @@ struct ConnArgs {
   uint32_t nch, nslots, lanes, wg_begin;
   uint32_t roles;  // bit 0: producer side runs, bit 1: consumer side runs
   uint32_t relay;  // 1: the consumer waits on gtail and drains fifo_rx
+  TraceRec* trace;     // step trace, or nullptr: [nch * lanes * 2] rings of trace_per records
+  uint32_t trace_per;  // records per (channel, lane, side) ring
+  uint32_t pad;
 };
 
 // One message of a launch: bytes [off, off + len) of the connection's src
@@ -106,6 +121,7 @@ struct Variant {
   int scope;     // kScope*
   int ordering;  // 0: coherent accesses, 1: scoped fences
   int aligned;   // all of src/dst 16-byte aligned
+  int trace;     // 1: the variant that writes the step trace
 };
 
 hipError_t launch_run1(const Variant& v, const RunArgs<1>& a, int block, hipStream_t s);

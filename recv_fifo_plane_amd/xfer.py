@@ -98,6 +98,7 @@ SIGNATURES = {
     "xfer_conn_read_fifo_ex": (C.c_int, [_vp, C.c_int, C.c_int, _vp, C.c_size_t]),
     "xfer_conn_query_relay": (C.c_int, [_vp, C.c_int, _u64p, _u64p]),
     "xfer_conn_abort": (C.c_int, [_vp]),
+    "xfer_conn_set_trace": (C.c_int, [_vp, _vp, C.c_size_t]),
     "xfer_conn_launch_shape": (C.c_int, [_vp, _ip, _ip]),
     "xfer_last_error": (C.c_char_p, []),
     "xfer_status_string": (C.c_char_p, [C.c_int]),
@@ -252,10 +253,34 @@ class Conn:
     def abort(self) -> None:
         check(lib().xfer_conn_abort(self._h))
 
+    def set_trace(self, records, nrecords: int = 0) -> None:
+        """Step trace into a device buffer (a torch tensor of TRACE_REC_BYTES x
+        nrecords bytes, or an address with nrecords); None turns it off."""
+        if records is None:
+            check(lib().xfer_conn_set_trace(self._h, None, 0))
+            return
+        if not isinstance(records, int):
+            nrecords = records.numel() * records.element_size() // TRACE_REC_BYTES
+        check(lib().xfer_conn_set_trace(self._h, _addr(records), int(nrecords)))
+
     def launch_shape(self) -> tuple[int, int]:
         g, b = C.c_int(), C.c_int()
         check(lib().xfer_conn_launch_shape(self._h, C.byref(g), C.byref(b)))
         return g.value, b.value
+
+
+XFER_TRACE_ACQUIRE, XFER_TRACE_PUBLISH = 0, 1
+TRACE_REC_BYTES = 32
+
+
+def trace_records(raw):
+    """Decodes a step-trace buffer (bytes as a numpy uint8 array) into a
+    structured array of xfer_trace_rec."""
+    import numpy as np
+    dt = np.dtype([("time", "<u8"), ("step", "<u8"), ("value", "<u8"), ("channel", "<u4"),
+                   ("lane", "<u2"), ("side", "u1"), ("event", "u1")])
+    assert dt.itemsize == TRACE_REC_BYTES
+    return np.frombuffer(np.ascontiguousarray(raw).tobytes(), dtype=dt)
 
 
 def run_batch(conns, srcs, dsts, nbytes, stream=None) -> None:

@@ -136,3 +136,8 @@ def test_schedule_rejects_bad_arguments():
         xf.sched_peers(5, 4, 1)
     with pytest.raises(xf.XferError):
         xf.sched_ring_masks(0, 4, 65)
+
+
+def test_set_trace_rejects_a_null_connection():
+    from recv_fifo_plane_amd import xfer as X
+    assert X.lib().xfer_conn_set_trace(None, None, 0) == X.XFER_ERR_INVALID_ARG

@@ -338,3 +338,25 @@ def test_conn_rejects_bad_shapes():
                  ("relay", 1, 8, 8)]:
         with pytest.raises(oracle.OracleError):
             oracle.Conn(*args)
+
+
+@pytest.mark.parametrize("proto", ["zc", "zcd"])
+@pytest.mark.parametrize("n,nch,slot", [(0, 1, 16), (1, 1, 16), (100, 3, 16), (4097, 4, 64),
+                                        (100_003, 4, 4096), (65536, 64, 16)])
+def test_zero_copy_offsets_tile_the_transfer(proto, n, nch, slot):
+    # the published offsets of all channels, each step covering its chunk,
+    # tile [0, n) exactly once, in increasing order within a channel (the
+    # simulator holds its producer to this sequence: the zc_no_wait mutation
+    # above, a receiver offering an address out of turn, is caught as
+    # wrong_ptr)
+    offs = oracle.zero_copy_offsets(proto, n, nch, slot)
+    S = oracle.step_bytes(proto, slot)
+    assert len(offs) == nch
+    covered = np.zeros(n, dtype=np.int32)
+    beg, ln = oracle.partition(n, nch)
+    for c in range(nch):
+        assert offs[c] == sorted(offs[c])
+        for o in offs[c]:
+            covered[o:min(o + S, beg[c] + ln[c])] += 1
+    assert bool((covered == 1).all())
+

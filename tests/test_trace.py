@@ -1,0 +1,148 @@
+"""GPU tests of the step trace (xfer_conn_set_trace).  Each side's first
+thread stamps an ACQUIRE and a PUBLISH event per step with the device's
+constant wall clock, so the records must:
+- be complete: both events of every step, in their ring slots, with the
+  right channel, lane and side;
+- be ordered in time: a producer's PUBLISH of step g before the consumer's
+  ACQUIRE of it; a consumer's PUBLISH of step g - nslots (its head) before
+  the producer's ACQUIRE of step g (the credit);
+- for zero-copy, carry exactly the destination offsets of the oracle's
+  publication sequence (reading R7): taken by the producer, published by
+  the receiver."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_cases import log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+FILL = 0xAB
+
+
+def traced_run(proto, nch, nslots, slot, lanes, n, fifo_loc="device", runs=1, per=None,
+               block=256):
+    import torch
+
+    import recv_fifo_plane_amd as xf
+    from recv_fifo_plane_amd import xfer as X
+    conn = xf.Conn(proto, nch, nslots, slot, fifo_loc, wgs_per_channel=lanes,
+                   block_threads=block)
+    S = oracle.step_bytes("ll" if proto == "ll" else "simple", slot)
+    k_max = max((ln + S - 1) // S for ln in oracle.partition(n, nch)[1]) * runs
+    per = per or 2 * max(1, k_max)
+    rings = nch * lanes * 2
+    buf = torch.full((rings * per * X.TRACE_REC_BYTES,), FILL, dtype=torch.uint8, device="cuda")
+    conn.set_trace(buf)
+    A = synth.uint8_uniform(n, 4000 + n)
+    a = to_dev(A)
+    b = torch.zeros_like(a)
+    for _ in range(runs):
+        conn.run(a, b, n)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    for ch in range(nch):
+        assert conn.query(ch)["error"] == 0
+    recs = X.trace_records(buf.cpu().numpy())
+    conn.close()
+    return recs.reshape(nch, lanes, 2, per), int(b.data_ptr()), S
+
+
+def steps_of(n, nch, S):
+    return [(ln + S - 1) // S for ln in oracle.partition(n, nch)[1]]
+
+
+def check_complete(R, n, nch, lanes, S, runs=1):
+    per = R.shape[-1]
+    ks = steps_of(n, nch, S)
+    for c in range(nch):
+        for w in range(lanes):
+            for side in (0, 1):
+                ring = R[c, w, side]
+                for g in range(ks[c] * runs):
+                    for ev in (0, 1):
+                        r = ring[(2 * g + ev) % per]
+                        assert (r["step"], r["event"], r["channel"], r["lane"], r["side"]) == \
+                            (g, ev, c, w, side), (c, w, side, g, ev, r)
+                    assert ring[(2 * g) % per]["time"] <= ring[(2 * g + 1) % per]["time"]
+    return ks
+
+
+def ev(R, c, w, side, g, e):
+    return R[c, w, side][(2 * g + e) % R.shape[-1]]
+
+
+@pytest.mark.parametrize("proto,fifo_loc", [("simple", "device"), ("simple", "host"),
+                                            ("simple", "relay"), ("ll", "device")])
+def test_trace_fifo_protocols(proto, fifo_loc):
+    nch, nslots, lanes, n = 3, 2, 2, 300_001
+    slot = 16384 if proto == "ll" else 8192
+    log("case: trace %s %s" % (proto, fifo_loc))
+    R, _, S = traced_run(proto, nch, nslots, slot, lanes, n, fifo_loc=fifo_loc)
+    ks = check_complete(R, n, nch, lanes, S)
+    for c in range(nch):
+        for w in range(lanes):
+            for g in range(ks[c]):
+                if proto == "ll":
+                    # a lane whose first line lies past the step's chunk has
+                    # no line to wait for, and the producer stamps before its
+                    # first thread's line
+                    L = min(S, oracle.partition(n, nch)[1][c] - g * S)
+                    if w * 256 >= (L + 3) // 4:
+                        continue
+                assert ev(R, c, w, 0, g, 1)["time"] < ev(R, c, w, 1, g, 0)["time"], (c, w, g)
+                if g >= nslots:
+                    assert ev(R, c, w, 1, g - nslots, 1)["time"] < ev(R, c, w, 0, g, 0)["time"]
+
+
+@pytest.mark.parametrize("proto", ["zc", "zcd"])
+def test_trace_zero_copy_offsets_match_the_oracle(proto):
+    nch, lanes, slot, n = 4, 2, 4096, 100_003
+    log("case: trace %s offsets" % proto)
+    R, dst, S = traced_run(proto, nch, 8, slot, lanes, n)
+    ks = check_complete(R, n, nch, lanes, S)
+    want = oracle.zero_copy_offsets(proto, n, nch, slot)
+    for c in range(nch):
+        assert len(want[c]) == ks[c]
+        for w in range(lanes):
+            got = [int(ev(R, c, w, 0, g, 0)["value"]) - dst for g in range(ks[c])]
+            assert got == want[c], (c, w, got[:4], want[c][:4])
+            for g in range(ks[c]):
+                assert ev(R, c, w, 0, g, 1)["time"] < ev(R, c, w, 1, g, 1)["time"]
+                if proto == "zc":
+                    pub = ev(R, c, w, 1, g, 0)
+                    assert int(pub["value"]) - dst == want[c][g]
+                    assert pub["time"] < ev(R, c, w, 0, g, 0)["time"], (c, w, g)
+
+
+def test_trace_ring_keeps_the_latest_steps_over_runs():
+    # 3 runs of 8 steps per channel through rings of 6 records: each ring
+    # holds the last 3 steps, numbered globally across the runs
+    nch, lanes = 1, 1
+    R, _, S = traced_run("simple", nch, 2, 4096, lanes, 8 * 4096, runs=3, per=6)
+    for side in (0, 1):
+        ring = R[0, 0, side]
+        assert sorted(set(int(x) for x in ring["step"])) == [21, 22, 23]
+        for i in range(6):
+            assert (2 * int(ring[i]["step"]) + int(ring[i]["event"])) % 6 == i
+
+
+def test_trace_off_writes_nothing():
+    import torch
+
+    import recv_fifo_plane_amd as xf
+    from recv_fifo_plane_amd import xfer as X
+    conn = xf.Conn("simple", 2, 2, 4096, wgs_per_channel=1)
+    buf = torch.full((2 * 2 * 8 * X.TRACE_REC_BYTES,), FILL, dtype=torch.uint8, device="cuda")
+    conn.set_trace(buf)
+    conn.set_trace(None)
+    a = torch.from_numpy(synth.uint8_uniform(50_000, 1)).to("cuda")
+    b = torch.zeros_like(a)
+    conn.run(a, b, a.numel())
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert bool((buf == FILL).all())
+    with pytest.raises(xf.XferError):
+        conn.set_trace(buf[:X.TRACE_REC_BYTES * 4])  # fewer than 2 records per ring
+    conn.close()
