@@ -297,6 +297,17 @@ typedef enum { XFER_TRACE_ACQUIRE = 0, XFER_TRACE_PUBLISH = 1 } xfer_trace_event
 
 int xfer_conn_set_trace(xfer_conn* c, void* records, size_t nrecords);
 
+/* Debug aid for race hunting, off by default: with a non-zero seed, runs
+ * queued afterwards sleep every wave a pseudo-random 0..15 x 512 cycles
+ * (a function of the seed, the channel, lane and side, the step and the
+ * wave) where a step is acquired and where it is published, in every
+ * protocol.  Producer and consumer, and the waves of one side, then reach
+ * the shared words in orders that undisturbed runs rarely take; results must
+ * not change.  0 turns it off.  Traced or jittered connections run the
+ * debug kernel variant; the others run kernels without any of this code.
+ * Errors: INVALID_ARG (NULL connection). */
+int xfer_conn_set_jitter(xfer_conn* c, uint32_t seed);
+
 /* Sets the connection's host-side abort word; every in-kernel wait of a
  * running or later launch on it ends with XFER_ERR_ABORTED. */
 int xfer_conn_abort(xfer_conn* c);

@@ -41,6 +41,7 @@ struct xfer_conn {
   xfer::Status* status_dev = nullptr;
   xfer::TraceRec* trace = nullptr;  // caller's step-trace buffer (device), or nullptr
   uint32_t trace_per = 0;           // records per (channel, lane, side) ring
+  uint32_t jitter = 0;              // seed of the debug jitter, 0 = none
   std::vector<uint64_t> steps;   // per channel, host bookkeeping of completed steps
 };
 
@@ -218,6 +219,7 @@ ConnArgs conn_args(const xfer_conn* c, const void* src, void* dst, uint64_t nbyt
   a.relay = c->fifo_rx ? 1u : 0u;
   a.trace = c->trace;
   a.trace_per = c->trace_per;
+  a.jitter = c->jitter;
   a.ctrl_tx = c->ctrl;
   a.ctrl_rx = c->ctrl_rx;
   a.status = c->status_dev;
@@ -255,7 +257,7 @@ int resident_capacity(const Variant& v, int kind, int block, int* cap) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  const std::array<int, 8> key{dev, v.proto, v.scope, v.ordering, v.aligned, v.trace, kind, block};
+  const std::array<int, 8> key{dev, v.proto, v.scope, v.ordering, v.aligned, v.debug, kind, block};
   {
     std::lock_guard<std::mutex> lk(mu);
     auto it = cache.find(key);
@@ -577,8 +579,11 @@ extern "C" int xfer_conn_destroy(xfer_conn* c) {
   return XFER_OK;
 }
 
-static Variant variant_of(const xfer_conn* c, bool aligned) {
-  return Variant{c->proto, c->scope, c->ordering, aligned ? 1 : 0, c->trace ? 1 : 0};
+static // Runs of a traced or jittered connection take the debug kernel variant.
+bool debug_of(const xfer_conn* c) { return c->trace != nullptr || c->jitter != 0; }
+
+Variant variant_of(const xfer_conn* c, bool aligned) {
+  return Variant{c->proto, c->scope, c->ordering, aligned ? 1 : 0, debug_of(c) ? 1 : 0};
 }
 
 extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nbytes, int iters,
@@ -733,7 +738,7 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
   DeviceGuard g(first->device);
   Variant v = variant_of(first, aligned);
   for (int i = 0; i < n; ++i)
-    if (conns[i]->trace) v.trace = 1;  // untraced connections pass a null buffer
+    if (debug_of(conns[i])) v.debug = 1;  // the others pass no buffer and no seed
   const uint32_t grid = grid_of(first->xcd_pairing, total);
   int rc = check_resident(v, 1, first->block, grid, "xfer_run_batch");
   if (rc) return rc;
@@ -783,7 +788,7 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
                                                                                : kScopeAgent;
   const Variant v{fwd->proto, scope, fwd->ordering,
                   (aligned16(a) && aligned16(b) && aligned16(cbuf)) ? 1 : 0,
-                  (fwd->trace || rev->trace) ? 1 : 0};
+                  (debug_of(fwd) || debug_of(rev)) ? 1 : 0};
   rc = check_resident(v, 2, fwd->block, total, "xfer_run_pingpong");
   if (rc) return rc;
   PingArgs args;
@@ -913,6 +918,12 @@ extern "C" int xfer_conn_set_trace(xfer_conn* c, void* records, size_t nrecords)
                     std::to_string(2 * rings) + " in all)");
   c->trace = static_cast<TraceRec*>(records);
   c->trace_per = uint32_t(per);
+  return XFER_OK;
+}
+
+extern "C" int xfer_conn_set_jitter(xfer_conn* c, uint32_t seed) {
+  if (!c) return fail(XFER_ERR_INVALID_ARG, "xfer_conn_set_jitter: NULL connection");
+  c->jitter = seed;
   return XFER_OK;
 }
 

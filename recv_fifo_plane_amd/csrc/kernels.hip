@@ -322,21 +322,26 @@ struct Side {
   LaneCtrl* tx;     // the send side's block of this lane: head, ptrExchange
   LaneCtrl* rx;     // the receive side's block: tail (and a relay's proxy tails)
   TraceRec* tr;     // this (channel, lane, side)'s step-trace ring, or nullptr
+  uint32_t jit;     // jitter seed of this (channel, lane, side), 0 = none
   uint64_t base;    // step counter at launch start (own counter: tail or head)
   uint64_t seen;    // last observed peer counter (wave-uniform)
   Range r;          // the channel's range and steps in the current message
 };
 
-// TR: the kernel variant that writes the step trace.  Without it the trace
-// ring is a constant null, so every trace branch folds away.
-template <bool TR>
+// DBG: the debug kernel variant, which writes the step trace and applies
+// the jitter.  Without it the trace ring and the jitter seed are constants
+// (null, 0), so every debug branch folds away.
+template <bool DBG>
 __device__ __forceinline__ Side make_side(const ConnArgs& A, uint32_t c, uint32_t w, bool producer,
                                           int sc) {
   Side s;
   const uint64_t lane = static_cast<uint64_t>(c) * A.lanes + w;
   s.tx = A.ctrl_tx + lane;
   s.rx = A.ctrl_rx + lane;
-  s.tr = TR && A.trace ? A.trace + (lane * 2 + (producer ? 0u : 1u)) * A.trace_per : nullptr;
+  s.tr = DBG && A.trace ? A.trace + (lane * 2 + (producer ? 0u : 1u)) * A.trace_per : nullptr;
+  s.jit = DBG && A.jitter ? (A.jitter ^ static_cast<uint32_t>(lane * 2 + (producer ? 0u : 1u)) *
+                                            0x9E3779B9u) | 1u
+                          : 0u;
   s.r = Range{0, 0, 0};  // set per message
   // A side is the only writer of its own counter, and the previous launch
   // that wrote it has completed, so a plain coherent load reads it.
@@ -370,6 +375,21 @@ __device__ __forceinline__ void trace_write(TraceRec* base, uint32_t per, uint32
 __device__ __forceinline__ void trace_step(const ConnArgs& A, const Side& sd, uint64_t g,
                                            uint32_t ev, uint64_t value) {
   if (sd.tr != nullptr) trace_write(A.trace, A.trace_per, A.lanes, sd.tr, g, ev, value);
+}
+
+// Jitter (debug variant): each wave sleeps a pseudo-random 0..15 x 512
+// cycles at point p of step g, a function of the side's seed, g, p and the
+// wave, so producer and consumer, and the waves of one side, reach their
+// accesses in orders that undisturbed runs rarely take.  Wave-uniform;
+// every wait stays bounded, it only starts later.
+__device__ __forceinline__ void jitter(const Side& sd, uint64_t g, uint32_t p) {
+  if (sd.jit == 0) return;
+  uint32_t h = sd.jit ^ static_cast<uint32_t>(g) * 0x85EBCA6Bu ^ (p + 1u) * 0xC2B2AE35u ^
+               (threadIdx.x >> 6) * 0x27D4EB2Fu;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  for (uint32_t i = h & 15u; i > 0; --i) __builtin_amdgcn_s_sleep(8);
 }
 
 // Shared by the waves of a workgroup: the first failure seen by any wave.
@@ -481,6 +501,7 @@ __device__ bool simple_send_piped(const ConnArgs& A, uint32_t c, uint32_t w, Sid
     const uint32_t err = wait_credit<SC, ORD, true>(A, sd, g, ticks, sh);
     if (!err && threadIdx.x == 0) trace_step(A, sd, g, 0, sd.seen);
     if (!err) {
+      jitter(sd, g, 0);
       const uint32_t L = chunk_len(sd, S, j);
       uint8_t* slot = slot_of(A, c, g);
       batch_store<O::kShared, false>(b, slot, L, S, P, w);
@@ -492,6 +513,7 @@ __device__ bool simple_send_piped(const ConnArgs& A, uint32_t c, uint32_t w, Sid
         wait_vmcnt<0>();
       }
     }
+    jitter(sd, g, 1);
     if (wg_failed(sh, err, A.status)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 1, g + 1);
@@ -517,10 +539,12 @@ __device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
     const uint32_t err = wait_credit<SC, ORD, true>(A, sd, g, ticks, sh);
     if (!err && threadIdx.x == 0) trace_step(A, sd, g, 0, sd.seen);
     if (!err) {
+      jitter(sd, g, 0);
       lane_copy<kPolNT, O::kShared, false>(src + sd.r.beg + j * S, slot_of(A, c, g), chunk_len(sd, S, j),
                                     S, A.lanes, w);
       O::release();
     }
+    jitter(sd, g, 1);
     if (wg_failed(sh, err, A.status)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 1, g + 1);
@@ -556,6 +580,7 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
     }
     if (!err && threadIdx.x == 0) trace_step(A, sd, g, 0, sd.seen);
     if (!err) {
+      jitter(sd, g, 0);
       lane_copy<O::kShared, kPolNT, false>(slot_rx(A, c, g), dst + sd.r.beg + j * S,
                                            chunk_len(sd, S, j), S, A.lanes, w);
       // Our slot reads are complete before the slot is handed back: each
@@ -563,6 +588,7 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
       // wait for the destination stores; fenced ordering keeps its fence.
       if constexpr (ORD == kOrdFenced) O::release();
     }
+    jitter(sd, g, 1);
     if (wg_failed(sh, err, A.status)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 1, g + 1);
@@ -614,6 +640,7 @@ __device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
       trace_step(A, sd, g, 0, sd.seen);
       trace_step(A, sd, g, 1, g + 1);
     }
+    jitter(sd, g, 0);  // each wave's lines go out at its own moment
     if (nl <= nthr * P) {  // one pass: at most one line per thread
       const uint32_t i = w * nthr + threadIdx.x;
       if (i < nl) st_u64<SC>(&lines[i], flag | ll_src_word<AL>(s, L, i));
@@ -641,6 +668,7 @@ __device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
     const uint64_t* lines = reinterpret_cast<const uint64_t*>(slot_of(A, c, g));
     uint8_t* d = dst + sd.r.beg + j * S;
     uint32_t err = 0;
+    jitter(sd, g, 0);
     if (nl <= nthr * P) {  // one pass: at most one line per thread
       const uint32_t i = w * nthr + threadIdx.x;
       if (i < nl) {
@@ -691,6 +719,7 @@ __device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
     // nothing more (the destination stores may still be in flight); fenced
     // ordering keeps its release fence.
     if constexpr (ORD == kOrdFenced) O::release();
+    jitter(sd, g, 1);
     if (wg_failed(sh, err, A.status)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 0, static_cast<uint64_t>(want));  // every line of the step seen
@@ -761,6 +790,7 @@ __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t 
     const uint64_t g = g0 + j;
     uint8_t* p = reinterpret_cast<uint8_t*>(sh.ptr[j & 1]);
     const uint32_t L = chunk_len(sd, S, j);
+    jitter(sd, g, 0);
     batch_store<O::kShared, true>(b, p, L, S, P, w);
     lane_tail<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, p, L, S, P, w);
     uint32_t err = 0;
@@ -774,6 +804,7 @@ __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t 
     } else {
       wait_vmcnt<0>();
     }
+    jitter(sd, g, 1);
     if (wg_failed(sh, err, A.status)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 1, g + 1);
@@ -798,9 +829,11 @@ __device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
     const uint64_t g = g0 + j;
     if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh.ptr[0]), A.status)) return false;
     if (threadIdx.x == 0) trace_step(A, sd, g, 0, sh.ptr[0]);
+    jitter(sd, g, 0);
     lane_copy<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, reinterpret_cast<uint8_t*>(sh.ptr[0]),
                                   chunk_len(sd, S, j), S, A.lanes, w);
     O::release();
+    jitter(sd, g, 1);
     if (wg_failed(sh, 0, A.status)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 1, g + 1);
@@ -829,6 +862,7 @@ __device__ bool zcd_send(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
       uint8_t* p = dst + sd.r.beg + j * S;
       const uint32_t L = chunk_len(sd, S, j);
       if (threadIdx.x == 0) trace_step(A, sd, g, 0, reinterpret_cast<uint64_t>(p));
+      jitter(sd, g, 0);
       batch_store<O::kShared, true>(b, p, L, S, P, w);
       lane_tail<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, p, L, S, P, w);
       if (j + 1 < sd.r.k) {
@@ -837,6 +871,7 @@ __device__ bool zcd_send(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
       } else {
         wait_vmcnt<0>();
       }
+      jitter(sd, g, 1);
       if (wg_failed(sh, 0, A.status)) return false;
       if (threadIdx.x == 0) {
         trace_step(A, sd, g, 1, g + 1);
@@ -848,9 +883,11 @@ __device__ bool zcd_send(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
     if (threadIdx.x == 0) trace_step(A, sd, g, 0, reinterpret_cast<uint64_t>(dst + sd.r.beg + j * S));
+    jitter(sd, g, 0);
     lane_copy<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, dst + sd.r.beg + j * S,
                                         chunk_len(sd, S, j), S, P, w);
     O::release();
+    jitter(sd, g, 1);
     if (wg_failed(sh, 0, A.status)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 1, g + 1);
@@ -876,6 +913,7 @@ __device__ bool zcd_recv(const ConnArgs& A, Side& sd, uint64_t g0, uint64_t tick
         trace_step(A, sd, q, 0, t);
         trace_step(A, sd, q, 1, t);
       }
+      jitter(sd, t, 1);
       done = t;
       st_u64<SC>(&sd.tx->head, t);
       dl = Deadline(ticks, A.status);
@@ -953,6 +991,7 @@ __device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<M
     bool moved = false;
     if (!cur.done && ld_u64<SC>(&sd.tx->ptrx) == 0) {
       const uint64_t addr = reinterpret_cast<uint64_t>(A.dst + cur.off + cur.r.beg + cur.j * S);
+      jitter(sd, sd.base + npub, 0);
       trace_step(A, sd, sd.base + npub++, 0, addr);
       O::release();
       st_u64<SC>(&sd.tx->ptrx, addr);
@@ -996,7 +1035,7 @@ __device__ __forceinline__ uint32_t logical_wg(uint32_t remap, uint32_t total) {
   return 2u * ((b % 8u) * half + s % half) + s / half;
 }
 
-template <int PROTO, int SC, int ORD, bool AL, int MAXB, bool TR>
+template <int PROTO, int SC, int ORD, bool AL, int MAXB, bool DBG>
 __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
   __shared__ Shared sh;
   if (threadIdx.x == 0) sh.err = 0;
@@ -1012,7 +1051,7 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
   const uint32_t c = pair / A.lanes, w = pair % A.lanes;
   if (c >= A.nch) return;  // padding of a paired launch (its grid is a multiple of 16)
   if (!((A.roles >> role) & 1u)) return;  // side switched off for fault injection
-  Side sd = make_side<TR>(A, c, w, role == 0, SC);
+  Side sd = make_side<DBG>(A, c, w, role == 0, SC);
   const uint64_t ticks = args.timeout_ticks;
   if constexpr (PROTO == kProtoZC) {
     if (role == 1) {
@@ -1051,7 +1090,7 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
 
 // Ping-pong: pair side 0 is endpoint X (send on fwd, then receive on rev),
 // side 1 is endpoint Y (receive on fwd into b, then send b on rev).
-template <int PROTO, int SC, int ORD, bool AL, bool TR>
+template <int PROTO, int SC, int ORD, bool AL, bool DBG>
 __global__ void __launch_bounds__(1024) ping_kernel(PingArgs args) {
   __shared__ Shared sh;
   if (threadIdx.x == 0) sh.err = 0;
@@ -1062,8 +1101,8 @@ __global__ void __launch_bounds__(1024) ping_kernel(PingArgs args) {
   const ConnArgs& R = args.rev;
   const uint32_t c = pair / F.lanes, w = pair % F.lanes;
   if (c >= F.nch) return;
-  Side fs = make_side<TR>(F, c, w, side == 0, SC);
-  Side rs = make_side<TR>(R, c, w, side == 1, SC);
+  Side fs = make_side<DBG>(F, c, w, side == 0, SC);
+  Side rs = make_side<DBG>(R, c, w, side == 1, SC);
   fs.r = chan_range(F.nbytes, F.nch, c, F.step_bytes);
   rs.r = chan_range(R.nbytes, R.nch, c, R.step_bytes);
   const uint64_t k = fs.r.k;
@@ -1102,26 +1141,26 @@ template <int MAXB>
 using RunFn = void (*)(RunArgs<MAXB>);
 using PingFn = void (*)(PingArgs);
 
-template <int MAXB, int P, int SC, int ORD, bool TR>
+template <int MAXB, int P, int SC, int ORD, bool DBG>
 RunFn<MAXB> pick_run_al(bool al) {
-  return al ? run_kernel<P, SC, ORD, true, MAXB, TR> : run_kernel<P, SC, ORD, false, MAXB, TR>;
+  return al ? run_kernel<P, SC, ORD, true, MAXB, DBG> : run_kernel<P, SC, ORD, false, MAXB, DBG>;
 }
 
-template <int MAXB, int P, int SC, bool TR>
+template <int MAXB, int P, int SC, bool DBG>
 RunFn<MAXB> pick_run_ord(int ord, bool al) {
-  return ord == kOrdFenced ? pick_run_al<MAXB, P, SC, kOrdFenced, TR>(al)
-                           : pick_run_al<MAXB, P, SC, kOrdCoherent, TR>(al);
+  return ord == kOrdFenced ? pick_run_al<MAXB, P, SC, kOrdFenced, DBG>(al)
+                           : pick_run_al<MAXB, P, SC, kOrdCoherent, DBG>(al);
 }
 
-template <int MAXB, int P, bool TR>
-RunFn<MAXB> pick_run_tr(const Variant& v) {
-  return v.scope == kScopeSystem ? pick_run_ord<MAXB, P, kScopeSystem, TR>(v.ordering, v.aligned)
-                                 : pick_run_ord<MAXB, P, kScopeAgent, TR>(v.ordering, v.aligned);
+template <int MAXB, int P, bool DBG>
+RunFn<MAXB> pick_run_dbg(const Variant& v) {
+  return v.scope == kScopeSystem ? pick_run_ord<MAXB, P, kScopeSystem, DBG>(v.ordering, v.aligned)
+                                 : pick_run_ord<MAXB, P, kScopeAgent, DBG>(v.ordering, v.aligned);
 }
 
 template <int MAXB, int P>
 RunFn<MAXB> pick_run_sc(const Variant& v) {
-  return v.trace ? pick_run_tr<MAXB, P, true>(v) : pick_run_tr<MAXB, P, false>(v);
+  return v.debug ? pick_run_dbg<MAXB, P, true>(v) : pick_run_dbg<MAXB, P, false>(v);
 }
 
 template <int MAXB>
@@ -1134,26 +1173,26 @@ RunFn<MAXB> pick_run(const Variant& v) {
   }
 }
 
-template <int P, int SC, int ORD, bool TR>
+template <int P, int SC, int ORD, bool DBG>
 PingFn pick_ping_al(bool al) {
-  return al ? ping_kernel<P, SC, ORD, true, TR> : ping_kernel<P, SC, ORD, false, TR>;
+  return al ? ping_kernel<P, SC, ORD, true, DBG> : ping_kernel<P, SC, ORD, false, DBG>;
 }
 
-template <int P, int SC, bool TR>
+template <int P, int SC, bool DBG>
 PingFn pick_ping_ord(int ord, bool al) {
-  return ord == kOrdFenced ? pick_ping_al<P, SC, kOrdFenced, TR>(al)
-                           : pick_ping_al<P, SC, kOrdCoherent, TR>(al);
+  return ord == kOrdFenced ? pick_ping_al<P, SC, kOrdFenced, DBG>(al)
+                           : pick_ping_al<P, SC, kOrdCoherent, DBG>(al);
 }
 
-template <int P, bool TR>
-PingFn pick_ping_tr(const Variant& v) {
-  return v.scope == kScopeSystem ? pick_ping_ord<P, kScopeSystem, TR>(v.ordering, v.aligned)
-                                 : pick_ping_ord<P, kScopeAgent, TR>(v.ordering, v.aligned);
+template <int P, bool DBG>
+PingFn pick_ping_dbg(const Variant& v) {
+  return v.scope == kScopeSystem ? pick_ping_ord<P, kScopeSystem, DBG>(v.ordering, v.aligned)
+                                 : pick_ping_ord<P, kScopeAgent, DBG>(v.ordering, v.aligned);
 }
 
 template <int P>
 PingFn pick_ping_sc(const Variant& v) {
-  return v.trace ? pick_ping_tr<P, true>(v) : pick_ping_tr<P, false>(v);
+  return v.debug ? pick_ping_dbg<P, true>(v) : pick_ping_dbg<P, false>(v);
 }
 
 PingFn pick_ping(const Variant& v) {

@@ -78,7 +78,7 @@ struct ConnArgs {
   uint32_t relay;  // 1: the consumer waits on gtail and drains fifo_rx
   TraceRec* trace;     // step trace, or nullptr: [nch * lanes * 2] rings of trace_per records
   uint32_t trace_per;  // records per (channel, lane, side) ring
-  uint32_t pad;
+  uint32_t jitter;     // debug variant: seed of random delays in the step loops, 0 = none
 };
 
 // One message of a launch: bytes [off, off + len) of the connection's src
@@ -121,7 +121,7 @@ struct Variant {
   int scope;     // kScope*
   int ordering;  // 0: coherent accesses, 1: scoped fences
   int aligned;   // all of src/dst 16-byte aligned
-  int trace;     // 1: the variant that writes the step trace
+  int debug;     // 1: the debug variant (step trace, jitter)
 };
 
 hipError_t launch_run1(const Variant& v, const RunArgs<1>& a, int block, hipStream_t s);

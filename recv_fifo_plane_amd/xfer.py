@@ -99,6 +99,7 @@ SIGNATURES = {
     "xfer_conn_query_relay": (C.c_int, [_vp, C.c_int, _u64p, _u64p]),
     "xfer_conn_abort": (C.c_int, [_vp]),
     "xfer_conn_set_trace": (C.c_int, [_vp, _vp, C.c_size_t]),
+    "xfer_conn_set_jitter": (C.c_int, [_vp, C.c_uint32]),
     "xfer_conn_launch_shape": (C.c_int, [_vp, _ip, _ip]),
     "xfer_last_error": (C.c_char_p, []),
     "xfer_status_string": (C.c_char_p, [C.c_int]),
@@ -252,6 +253,10 @@ class Conn:
 
     def abort(self) -> None:
         check(lib().xfer_conn_abort(self._h))
+
+    def set_jitter(self, seed: int) -> None:
+        """Random delays in the step loops (debug); 0 turns them off."""
+        check(lib().xfer_conn_set_jitter(self._h, int(seed) & 0xFFFFFFFF))
 
     def set_trace(self, records, nrecords: int = 0) -> None:
         """Step trace into a device buffer (a torch tensor of TRACE_REC_BYTES x

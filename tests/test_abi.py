@@ -141,3 +141,8 @@ def test_schedule_rejects_bad_arguments():
 def test_set_trace_rejects_a_null_connection():
     from recv_fifo_plane_amd import xfer as X
     assert X.lib().xfer_conn_set_trace(None, None, 0) == X.XFER_ERR_INVALID_ARG
+
+
+def test_set_jitter_rejects_a_null_connection():
+    from recv_fifo_plane_amd import xfer as X
+    assert X.lib().xfer_conn_set_jitter(None, 1) == X.XFER_ERR_INVALID_ARG

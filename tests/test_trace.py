@@ -22,7 +22,7 @@ FILL = 0xAB
 
 
 def traced_run(proto, nch, nslots, slot, lanes, n, fifo_loc="device", runs=1, per=None,
-               block=256):
+               block=256, jitter=0):
     import torch
 
     import recv_fifo_plane_amd as xf
@@ -35,6 +35,8 @@ def traced_run(proto, nch, nslots, slot, lanes, n, fifo_loc="device", runs=1, pe
     rings = nch * lanes * 2
     buf = torch.full((rings * per * X.TRACE_REC_BYTES,), FILL, dtype=torch.uint8, device="cuda")
     conn.set_trace(buf)
+    if jitter:
+        conn.set_jitter(jitter)
     A = synth.uint8_uniform(n, 4000 + n)
     a = to_dev(A)
     b = torch.zeros_like(a)
@@ -73,13 +75,14 @@ def ev(R, c, w, side, g, e):
     return R[c, w, side][(2 * g + e) % R.shape[-1]]
 
 
+@pytest.mark.parametrize("jitter", [0, 0x5EED])
 @pytest.mark.parametrize("proto,fifo_loc", [("simple", "device"), ("simple", "host"),
                                             ("simple", "relay"), ("ll", "device")])
-def test_trace_fifo_protocols(proto, fifo_loc):
+def test_trace_fifo_protocols(proto, fifo_loc, jitter):
     nch, nslots, lanes, n = 3, 2, 2, 300_001
     slot = 16384 if proto == "ll" else 8192
-    log("case: trace %s %s" % (proto, fifo_loc))
-    R, _, S = traced_run(proto, nch, nslots, slot, lanes, n, fifo_loc=fifo_loc)
+    log("case: trace %s %s jitter=%#x" % (proto, fifo_loc, jitter))
+    R, _, S = traced_run(proto, nch, nslots, slot, lanes, n, fifo_loc=fifo_loc, jitter=jitter)
     ks = check_complete(R, n, nch, lanes, S)
     for c in range(nch):
         for w in range(lanes):
@@ -96,11 +99,12 @@ def test_trace_fifo_protocols(proto, fifo_loc):
                     assert ev(R, c, w, 1, g - nslots, 1)["time"] < ev(R, c, w, 0, g, 0)["time"]
 
 
+@pytest.mark.parametrize("jitter", [0, 0x5EED])
 @pytest.mark.parametrize("proto", ["zc", "zcd"])
-def test_trace_zero_copy_offsets_match_the_oracle(proto):
+def test_trace_zero_copy_offsets_match_the_oracle(proto, jitter):
     nch, lanes, slot, n = 4, 2, 4096, 100_003
-    log("case: trace %s offsets" % proto)
-    R, dst, S = traced_run(proto, nch, 8, slot, lanes, n)
+    log("case: trace %s offsets jitter=%#x" % (proto, jitter))
+    R, dst, S = traced_run(proto, nch, 8, slot, lanes, n, jitter=jitter)
     ks = check_complete(R, n, nch, lanes, S)
     want = oracle.zero_copy_offsets(proto, n, nch, slot)
     for c in range(nch):
@@ -146,3 +150,22 @@ def test_trace_off_writes_nothing():
     with pytest.raises(xf.XferError):
         conn.set_trace(buf[:X.TRACE_REC_BYTES * 4])  # fewer than 2 records per ring
     conn.close()
+
+
+def test_jitter_lengthens_the_traced_steps():
+    # the producer's acquire-to-publish span of a step holds its jitter (two
+    # points of 0..15 sleeps of 512 cycles each, several microseconds in
+    # all, hundreds of ticks of the 100 MHz clock); without jitter it is the
+    # copy alone
+    nch, lanes, n = 2, 1, 64 * 4096
+
+    def mean_span(jitter):
+        R, _, S = traced_run("simple", nch, 4, 4096, lanes, n, jitter=jitter)
+        ks = check_complete(R, n, nch, lanes, S)
+        spans = [int(ev(R, c, 0, 0, g, 1)["time"]) - int(ev(R, c, 0, 0, g, 0)["time"])
+                 for c in range(nch) for g in range(ks[c])]
+        return sum(spans) / len(spans)
+
+    plain, jittered = mean_span(0), mean_span(0xC0FFEE)
+    log("producer step span: %.1f ticks plain, %.1f with jitter" % (plain, jittered))
+    assert jittered > plain + 100
