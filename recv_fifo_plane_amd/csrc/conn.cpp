@@ -63,7 +63,8 @@ namespace {
 
 constexpr uint32_t kDefaultTimeoutMs = 10000;
 constexpr int kDefaultBlock = 256;
-// P2P read: the FIFO starts on this boundary after the send side's control blocks.
+// An HBM FIFO starts this far into its allocation (write mode), or this far
+// past the send side's control blocks (P2P read).
 constexpr size_t kFifoAlign = size_t(64) << 10;
 
 int fail(int code, const std::string& msg) {
@@ -420,18 +421,23 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
       }
       c->fifo = static_cast<uint8_t*>(dptr);
     } else {
-      e = hipMalloc(&c->fifo_mem, fifo_bytes);
+      // Large allocations start on large power-of-two boundaries, so every
+      // channel's source, slot and destination addresses would share their
+      // low bits and meet on the same HBM channels in lock step; the FIFO
+      // starts kFifoAlign into its allocation instead (measured 0.2-1 %
+      // faster on the 32-channel workload).
+      e = hipMalloc(&c->fifo_mem, fifo_bytes + kFifoAlign);
       if (e != hipSuccess) {
         c->fifo_mem = nullptr;
         release(c);
         return fail(XFER_ERR_NO_MEMORY, std::string("hipMalloc(FIFO): ") + hipGetErrorString(e));
       }
-      e = hipMemset(c->fifo_mem, 0, fifo_bytes);
+      e = hipMemset(c->fifo_mem, 0, fifo_bytes + kFifoAlign);
       if (e != hipSuccess) {
         release(c);
         return hip_fail(e, "hipMemset(FIFO)");
       }
-      c->fifo = static_cast<uint8_t*>(c->fifo_mem);
+      c->fifo = static_cast<uint8_t*>(c->fifo_mem) + kFifoAlign;
     }
   }
   // Control blocks: one per lane, head = tail = ptrExchange = 0.
