@@ -476,6 +476,7 @@ def main() -> int:
                    "slot_bytes": W.W3["slot_bytes"], "fifo": "hbm",
                    "wgs_per_channel_side": W.W3["wgs_per_channel"],
                    "block_threads": w3["block_threads"], "workgroups": w3["workgroups"],
+                   "xcd_pairing": W.W3.get("xcd_pairing", 0),
                    "payload_bytes": payload, "b_equals_a": w3["b_equals_a"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -26,8 +26,12 @@ W2 = dict(name="ll_pingpong", proto="ll", nchannels=1, nslots=8, slot_bytes=32 <
           fifo_loc="device", wgs_per_channel=1, block_threads=1024, iters=10000)
 W2_SIZES = [8 << i for i in range(14)]  # 8 B .. 64 KiB
 
+# 4 workgroups per channel side as the workload fixes them; the block size
+# and dispatch order were swept (0.911-0.914 of the roofline at 704-832
+# threads in dispatch order, 0.903 with XCD pairing at 512).
 W3 = dict(name="simple_32ch_1GiB", proto="simple", nchannels=32, nslots=8, slot_bytes=512 << 10,
-          fifo_loc="device", wgs_per_channel=4, block_threads=512, nbytes=1 << 30)
+          fifo_loc="device", wgs_per_channel=4, block_threads=768, xcd_pairing=-1,
+          nbytes=1 << 30)
 
 # The same workload with P2P read: the FIFO in the send side's memory.
 W3R = dict(W3, name="simple_32ch_1GiB_p2p_read", p2p_read=1)
