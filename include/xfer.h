@@ -106,7 +106,9 @@ typedef struct {
   int ctrl_loc;         /* xfer_ctrl_loc */
   uint32_t timeout_ms;  /* bound on every in-kernel wait; default 10000 */
   int xcd_pairing;      /* 0 (default) or 1: place each producer/consumer pair on one XCD,
-                           an XCD's producers dispatched before its consumers (the grid is
+                           an XCD's producers dispatched before its consumers (zero-copy
+                           through ptrExchange: its receivers first, since each producer
+                           waits for its receiver's first address) (the grid is
                            padded to a multiple of 16 workgroups; padding exits at once);
                            -1: dispatch order (producers on even block ids, which the
                            hardware deals to XCDs 0, 2, 4 and 6 only) */

@@ -1040,7 +1040,11 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
   __shared__ Shared sh;
   if (threadIdx.x == 0) sh.err = 0;
   __syncthreads();
-  const uint32_t lw = logical_wg(args.xcd_remap, args.total_wgs);
+  // Zero-copy through ptrExchange: each XCD dispatches its receivers first
+  // (the role bit flipped), since every producer waits for its receiver's
+  // first published address and a receiver is one busy thread.
+  const uint32_t lw = logical_wg(args.xcd_remap, args.total_wgs) ^
+                      ((PROTO == kProtoZC && args.xcd_remap) ? 1u : 0u);
   uint32_t ci = 0;
   if constexpr (MAXB > 1) {
     while (ci + 1 < args.nconn && lw >= args.conn[ci + 1].wg_begin) ++ci;
