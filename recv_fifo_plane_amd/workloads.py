@@ -19,8 +19,10 @@ from __future__ import annotations
 
 from . import xfer as X
 
+# One producer and one consumer workgroup; 512 threads measured 32.9 GB/s
+# (0.98 of one 512-thread workgroup's straight copy) against 27.7 at 256.
 W1 = dict(name="simple_1ch_4MiB", proto="simple", nchannels=1, nslots=8, slot_bytes=128 << 10,
-          fifo_loc="device", wgs_per_channel=1, block_threads=256, nbytes=4 << 20)
+          fifo_loc="device", wgs_per_channel=1, block_threads=512, nbytes=4 << 20)
 
 W2 = dict(name="ll_pingpong", proto="ll", nchannels=1, nslots=8, slot_bytes=32 << 10,
           fifo_loc="device", wgs_per_channel=1, block_threads=1024, iters=10000)
