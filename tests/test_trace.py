@@ -169,3 +169,69 @@ def test_jitter_lengthens_the_traced_steps():
     plain, jittered = mean_span(0), mean_span(0xC0FFEE)
     log("producer step span: %.1f ticks plain, %.1f with jitter" % (plain, jittered))
     assert jittered > plain + 100
+
+
+def test_trace_in_a_batch_where_only_some_connections_trace():
+    # one launch for both: the traced connection records every step, the
+    # other runs through the same (debug) kernel with no buffer and no seed
+    import torch
+
+    import recv_fifo_plane_amd as xf
+    from recv_fifo_plane_amd import xfer as X
+    n, nch, lanes, slot = 200_000, 2, 2, 8192
+    traced = xf.Conn("simple", nch, 4, slot, wgs_per_channel=lanes)
+    plain = xf.Conn("simple", nch, 4, slot, wgs_per_channel=lanes)
+    S = oracle.step_bytes("simple", slot)
+    k = max(steps_of(n, nch, S))
+    per = 2 * k
+    buf = torch.full((nch * lanes * 2 * per * X.TRACE_REC_BYTES,), FILL, dtype=torch.uint8,
+                     device="cuda")
+    traced.set_trace(buf)
+    A = synth.uint8_uniform(2 * n, 9)
+    a = to_dev(A)
+    b = torch.zeros_like(a)
+    X.run_batch([traced, plain], [a.data_ptr(), a.data_ptr() + n], [b.data_ptr(), b.data_ptr() + n],
+                [n, n])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    R = X.trace_records(buf.cpu().numpy()).reshape(nch, lanes, 2, per)
+    check_complete(R, n, nch, lanes, S)
+    for ch in range(nch):
+        assert traced.query(ch)["error"] == 0 and plain.query(ch)["error"] == 0
+    traced.close()
+    plain.close()
+
+
+def test_trace_pingpong_orders_the_round_trips():
+    # X sends on fwd then receives on rev; Y the other way round.  Round i's
+    # reply can only start after its request landed: on each channel and
+    # lane, fwd's consumer ACQUIRE of step i precedes rev's producer PUBLISH
+    # of step i, which precedes rev's consumer ACQUIRE of it.
+    import torch
+
+    import recv_fifo_plane_amd as xf
+    from recv_fifo_plane_amd import xfer as X
+    size, iters, nch, lanes, slot = 4096, 12, 1, 1, 16384
+    conns = [xf.Conn("ll", nch, 8, slot, wgs_per_channel=lanes, block_threads=256)
+             for _ in range(2)]
+    per = 2 * iters
+    bufs = [torch.full((nch * lanes * 2 * per * X.TRACE_REC_BYTES,), FILL, dtype=torch.uint8,
+                       device="cuda") for _ in range(2)]
+    for c, buf in zip(conns, bufs):
+        c.set_trace(buf)
+    a = torch.from_numpy(synth.uint8_uniform(size, 3)).to("cuda")
+    b = torch.zeros_like(a)
+    cc = torch.zeros_like(a)
+    X.run_pingpong(conns[0], conns[1], a, b, cc, size, iters)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, cc)
+    F, Rv = (X.trace_records(buf.cpu().numpy()).reshape(nch, lanes, 2, per) for buf in bufs)
+    for i in range(iters):
+        fwd_ready = ev(F, 0, 0, 1, i, 0)["time"]
+        rev_pub = ev(Rv, 0, 0, 0, i, 1)["time"]
+        rev_ready = ev(Rv, 0, 0, 1, i, 0)["time"]
+        assert ev(F, 0, 0, 0, i, 1)["time"] < fwd_ready <= rev_pub < rev_ready, i
+        if i + 1 < iters:
+            assert rev_ready <= ev(F, 0, 0, 0, i + 1, 1)["time"], i
+    for c in conns:
+        c.close()
