@@ -420,11 +420,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["value", "all", "copy", "zerocopy", "relay"],
+    ap.add_argument("--only", choices=["value", "all", "copy", "zerocopy", "relay", "ll", "host"],
                     default="all",
                     help="value: time only the headline workload; copy: only a plain 1 GiB "
                          "device copy (the calibration kernel of the HBM byte counters); "
-                         "zerocopy, relay: only that mode (for profiling it alone)")
+                         "zerocopy, relay, ll, host: only that mode (for profiling it alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -446,6 +446,12 @@ def main() -> int:
         return 0
     if args.only == "zerocopy":
         print(json.dumps({"zerocopy": bench_w4(torch, T, W, synth)}), flush=True)
+        return 0
+    if args.only == "ll":
+        print(json.dumps({"ll_pingpong": bench_w2(torch, T, W, synth)}), flush=True)
+        return 0
+    if args.only == "host":
+        print(json.dumps({"host_fifo_16ch_2GiB": bench_w5(torch, T, W, synth)}), flush=True)
         return 0
     if args.only == "relay":
         # the duplex copy rate of the link is measured by the host-FIFO mode;
