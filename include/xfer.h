@@ -194,7 +194,9 @@ int xfer_run(xfer_conn* c, const void* src, void* dst, size_t nbytes, void* stre
 /* xfer_run_batch: the transfers of n connections (n <= XFER_MAX_BATCH) in
  * ONE launch, e.g. the edges of a ring of logical endpoints.  All
  * connections must share protocol, memory scope, ordering, block size and
- * timeout.
+ * timeout.  No transfer's destination may overlap another transfer's source
+ * or destination (the connections run in no fixed order against each
+ * other); INVALID_ARG otherwise.
  * Arrays are host arrays of length n. */
 #define XFER_MAX_BATCH 16
 int xfer_run_batch(xfer_conn* const* conns, const void* const* src, void* const* dst,

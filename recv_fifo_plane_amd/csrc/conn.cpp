@@ -741,6 +741,21 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
     ++live;
   }
   if (!live) return XFER_OK;
+  // The connections' channels run in no fixed order against each other, so
+  // a destination that another transfer also writes or reads would race.
+  for (int i = 0; i < n; ++i) {
+    if (!nbytes[i]) continue;
+    for (int j = 0; j < n; ++j) {
+      if (j == i || !nbytes[j]) continue;
+      if ((j > i && overlap(dst[i], nbytes[i], dst[j], nbytes[j])) ||
+          overlap(dst[i], nbytes[i], src[j], nbytes[j]))
+        return fail(XFER_ERR_INVALID_ARG,
+                    "xfer_run_batch: transfer " + std::to_string(i) +
+                        "'s destination overlaps transfer " + std::to_string(j) +
+                        (overlap(dst[i], nbytes[i], dst[j], nbytes[j]) ? "'s destination"
+                                                                       : "'s source"));
+    }
+  }
   DeviceGuard g(first->device);
   Variant v = variant_of(first, aligned);
   for (int i = 0; i < n; ++i)

@@ -107,3 +107,29 @@ def test_grid_that_cannot_be_resident_is_refused():
         c.run(a, b, 1 << 20)
     assert e.value.status == X.XFER_ERR_INVALID_ARG
     c.close()
+
+
+def test_batch_rejects_transfers_that_overlap_each_other():
+    import torch
+    c0, c1 = xf.Conn("simple", 1, 2, 4096), xf.Conn("simple", 1, 2, 4096)
+    a, b = _bufs(1 << 16)
+    pa, pb = a.data_ptr(), b.data_ptr()
+    n = 4096
+    bad = [([pa, pa + n], [pb, pb + n // 2]),          # destinations overlap
+           ([pa, pb], [pb, pb + 2 * n]),               # 1 reads 0's destination
+           ([pa, pa + 2 * n], [pb, pa + n // 2])]      # 1 writes into 0's source
+    for src, dst in bad:
+        with pytest.raises(xf.XferError) as e:
+            X.run_batch([c0, c1], src, dst, [n, n])
+        assert e.value.status == X.XFER_ERR_INVALID_ARG
+        assert "overlaps" in str(e.value)
+    # nothing was launched and no step was counted
+    assert c0.query(0)["steps"] == 0 and c1.query(0)["steps"] == 0
+    # disjoint transfers, and an empty one next to any range, are accepted
+    a.copy_(torch.arange(1 << 16, device="cuda").to(torch.uint8))
+    X.run_batch([c0, c1], [pa, pa + n], [pb, pb + n], [n, n])
+    X.run_batch([c0, c1], [pa + 2 * n, pb], [pb + 2 * n, pb + 2 * n], [n, 0])
+    torch.cuda.synchronize()
+    assert torch.equal(a[:3 * n], b[:3 * n])
+    c0.close()
+    c1.close()
