@@ -169,9 +169,9 @@ def bench_w2(torch, T, W, synth):
     out = {}
     # One pair of connections for every size, so that the curve shows the
     # size alone: the latency also depends on where the connections' FIFO
-    # and control words sit in physical memory (measured below).
-    pairs = [(W.make_conn(cfg), W.make_conn(cfg)) for _ in range(8)]
-    fwd, rev = pairs[0]
+    # and control words sit in HBM, which place_trials picks by measurement
+    # (the spread over placements is measured below).
+    fwd, rev = W.make_conn(cfg), W.make_conn(cfg)
     for size in W.W2_SIZES:
         A = synth.int32_uniform_bytes(size, synth.workload_seed(2) + size)
         a = torch.from_numpy(A).to("cuda")
@@ -186,25 +186,35 @@ def bench_w2(torch, T, W, synth):
         out[str(size)] = {"one_way_us": round(one_way_us, 3),
                           "payload_gbs": round(size / (one_way_us * 1e-6) / 1e9, 3),
                           "ok": ok}
+    fwd.close()
+    rev.close()
     # 8 B over eight pairs of connections alive at once (so at different
-    # addresses): the spread is the placement of their FIFO and control words.
-    spread, ok = [], True
+    # addresses): with one allocation each, and with the workload's
+    # placement by measurement.
     A = synth.int32_uniform_bytes(8, synth.workload_seed(2) + 8)
     a = torch.from_numpy(A).to("cuda")
-    for f, r in pairs:
-        b = torch.zeros_like(a)
-        c = torch.zeros_like(a)
-        _, per = T.time_launches(lambda: W.run_pingpong(f, r, a, b, c, 8, iters, T.stream), 1, 3)
-        check_no_error(f, 1, "W2 placement")
-        check_no_error(r, 1, "W2 placement")
-        ok = ok and bool(torch.equal(a, b) and torch.equal(a, c))
-        spread.append(per * 1e3 / (2 * iters))
-        f.close()
-        r.close()
-    spread.sort()
-    out["placement_8B"] = {"pairs": len(spread), "min_us": round(spread[0], 3),
-                           "median_us": round(statistics.median(spread), 3),
-                           "max_us": round(spread[-1], 3), "ok": ok}
+    for key, trials in (("placement_8B_one_allocation", 0),
+                        ("placement_8B_place_trials", cfg["place_trials"])):
+        pairs = [(W.make_conn(cfg, place_trials=trials), W.make_conn(cfg, place_trials=trials))
+                 for _ in range(8)]
+        spread, ok = [], True
+        for f, r in pairs:
+            b = torch.zeros_like(a)
+            c = torch.zeros_like(a)
+            _, per = T.time_launches(lambda: W.run_pingpong(f, r, a, b, c, 8, iters, T.stream),
+                                     1, 3)
+            check_no_error(f, 1, "W2 placement")
+            check_no_error(r, 1, "W2 placement")
+            ok = ok and bool(torch.equal(a, b) and torch.equal(a, c))
+            spread.append(per * 1e3 / (2 * iters))
+        for f, r in pairs:
+            f.close()
+            r.close()
+        spread.sort()
+        out[key] = {"pairs": len(spread), "place_trials": trials,
+                    "min_us": round(spread[0], 3),
+                    "median_us": round(statistics.median(spread), 3),
+                    "max_us": round(spread[-1], 3), "ok": ok}
     big = out[str(W.W2_SIZES[-1])]
     big["real_gbs_6x"] = round(6 * big["payload_gbs"], 2)
     big["hbm_frac_6x"] = round(6 * big["payload_gbs"] / HBM_PEAK_GBS, 4)

@@ -1021,16 +1021,32 @@ __device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<M
 }
 
 // ------------------------------------------------------------------ kernels
-// Logical workgroup of this block.  Blocks are dealt round-robin to the 8
-// XCDs, so block b runs on XCD b % 8 as that XCD's (b / 8)-th block.  With
-// the remap (the host pads the grid to a multiple of 16; logical ids past
-// the real workgroups exit at once) XCD x serves the total/16 consecutive
-// pairs starting at x * total/16: its first total/16 blocks are their
-// producers, the rest their consumers.  A pair then shares one XCD, and
-// producers spread evenly over the XCDs and over each XCD's dispatch order.
+// XCD this wave runs on (hardware register XCC_ID; a read, no memory access).
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 7u;
+}
+
+// Logical workgroup of this block.  A dispatch's blocks are dealt
+// round-robin to the 8 XCDs, but each hardware queue starts the deal at an
+// XCD of its own: block b runs on XCD (b + r) % 8, with r fixed per queue
+// (measured 0, 5, 6 and 7 on different streams of one process).  With the
+// remap, the block first takes position p = (b + r) mod total, read back from
+// its XCD id, so p % 8 is its XCD whichever stream launched it; p is a
+// permutation of the grid, since r is the same for every block of the
+// dispatch.  Then (the host pads the grid to a multiple of 16; logical ids
+// past the real workgroups exit at once) XCD x serves the total/16
+// consecutive pairs starting at x * total/16: its first total/16 blocks are
+// their producers, the rest their consumers.  A pair then shares one XCD,
+// producers spread evenly over the XCDs and over each XCD's dispatch order,
+// and a channel's XCD, on which the latency of its polled lines depends,
+// does not change with the stream.
 __device__ __forceinline__ uint32_t logical_wg(uint32_t remap, uint32_t total) {
-  const uint32_t b = blockIdx.x;
-  if (!remap) return b;
+  const uint32_t b0 = blockIdx.x;
+  if (!remap) return b0;
+  uint32_t b = b0 + ((xcc_id() - b0) & 7u);
+  if (b >= total) b -= total;
   const uint32_t half = total / 16u, s = b / 8u;
   return 2u * ((b % 8u) * half + s % half) + s / half;
 }

@@ -98,7 +98,7 @@ struct RunArgs {
   uint32_t nconn;
   uint32_t iters;
   uint32_t total_wgs;
-  uint32_t xcd_remap;    // 1: logical workgroup = (b % 8) * (G / 8) + b / 8
+  uint32_t xcd_remap;    // 1: pairs on one XCD, placed by the XCD id (the kernels' logical_wg)
   uint64_t timeout_ticks;
   uint32_t nmsgs;        // single-connection launches only
   uint32_t pad;

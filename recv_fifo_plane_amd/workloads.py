@@ -24,8 +24,11 @@ from . import xfer as X
 W1 = dict(name="simple_1ch_4MiB", proto="simple", nchannels=1, nslots=8, slot_bytes=128 << 10,
           fifo_loc="device", wgs_per_channel=1, block_threads=512, nbytes=4 << 20)
 
+# Each connection's FIFO and counters are placed by measured latency at the
+# fastest of eight offsets 2 KiB apart (place_trials): the time of a small
+# message's hand-off depends on the physical granule of the polled lines.
 W2 = dict(name="ll_pingpong", proto="ll", nchannels=1, nslots=8, slot_bytes=32 << 10,
-          fifo_loc="device", wgs_per_channel=1, block_threads=1024, iters=10000)
+          fifo_loc="device", wgs_per_channel=1, block_threads=1024, iters=10000, place_trials=8)
 W2_SIZES = [8 << i for i in range(14)]  # 8 B .. 64 KiB
 
 # 4 workgroups per channel side as the workload fixes them; the block size
@@ -64,7 +67,7 @@ W5R = dict(name="relay_4ch_4MiB", proto="simple", nchannels=4, nslots=8, slot_by
            total_bytes=2 << 30)
 
 _ATTRS = ("wgs_per_channel", "block_threads", "ctrl_loc", "timeout_ms", "xcd_pairing", "ordering",
-          "p2p_read")
+          "p2p_read", "place_trials")
 
 
 def make_conn(cfg: dict, **override) -> X.Conn:

@@ -56,7 +56,17 @@ class xfer_attr(C.Structure):
         ("roles", C.c_int),
         ("ordering", C.c_int),
         ("p2p_read", C.c_int),
+        ("place_trials", C.c_int),
     ]
+
+
+def make_attr(**kw) -> xfer_attr:
+    """An xfer_attr from keyword fields; absent ones are 0 (the defaults)."""
+    names = [f[0] for f in xfer_attr._fields_]
+    bad = set(kw) - set(names)
+    if bad:
+        raise TypeError("unknown connection attribute(s): " + ", ".join(sorted(bad)))
+    return xfer_attr(*[int(kw.get(n, 0)) for n in names])
 
 
 class xfer_chan_state(C.Structure):
@@ -177,7 +187,8 @@ class Conn:
 
     def __init__(self, proto="simple", nchannels=1, nslots=8, slot_bytes=128 << 10,
                  fifo_loc="device", wgs_per_channel=0, block_threads=0, ctrl_loc=0,
-                 timeout_ms=0, xcd_pairing=0, roles=0, ordering=0, p2p_read=0, _handle=None):
+                 timeout_ms=0, xcd_pairing=0, roles=0, ordering=0, p2p_read=0, place_trials=0,
+                 _handle=None):
         self.proto = PROTOS[proto] if isinstance(proto, str) else int(proto)
         self.nchannels = int(nchannels)
         self.nslots = int(nslots)
@@ -187,8 +198,10 @@ class Conn:
         if _handle is not None:
             self._h = _handle
             return
-        attr = xfer_attr(int(wgs_per_channel), int(block_threads), int(ctrl_loc), int(timeout_ms),
-                         int(xcd_pairing), int(roles), int(ordering), int(p2p_read))
+        attr = make_attr(wgs_per_channel=wgs_per_channel, block_threads=block_threads,
+                         ctrl_loc=ctrl_loc, timeout_ms=timeout_ms, xcd_pairing=xcd_pairing,
+                         roles=roles, ordering=ordering, p2p_read=p2p_read,
+                         place_trials=place_trials)
         h = _vp()
         check(lib().xfer_conn_create_ex(self.proto, self.nchannels, self.nslots, self.slot_bytes,
                                         self.fifo_loc, C.byref(attr), C.byref(h)))
@@ -344,10 +357,7 @@ def endpoints_connect(nranks: int, recv_masks, send_masks, max_peers: int = 128,
     sm = np.ascontiguousarray(send_masks, dtype=np.uint64).reshape(nranks, nranks)
     p = PROTOS[proto] if isinstance(proto, str) else int(proto)
     fl = FIFO_LOCS[fifo_loc] if isinstance(fifo_loc, str) else int(fifo_loc)
-    a = xfer_attr(int(attr.get("wgs_per_channel", 0)), int(attr.get("block_threads", 0)),
-                  int(attr.get("ctrl_loc", 0)), int(attr.get("timeout_ms", 0)),
-                  int(attr.get("xcd_pairing", 0)), int(attr.get("roles", 0)),
-                  int(attr.get("ordering", 0)))
+    a = make_attr(**attr)
     edges = (_vp * (nranks * nranks))()
     ne = C.c_int()
     check(lib().xfer_endpoints_connect(nranks, rm.ctypes.data_as(_u64p), sm.ctypes.data_as(_u64p),

@@ -93,18 +93,25 @@ def compare_state(conn, oconn, nch: int, what: str) -> None:
 def run_transfers(proto: str, nch: int, nslots: int, slot_bytes: int, sizes, *,
                   fifo_loc="device", lanes=1, block=0, src_off=0, dst_off=0, kind="uint8",
                   seed=1, ctrl_loc=0, xcd_pairing=0, ordering=0, p2p_read=0, jitter=0,
-                  label="") -> None:
+                  place_trials=0, label="") -> None:
     """Each size is one xfer_run on the same connection; after every run the
     whole destination buffer (guards included) must equal the oracle's."""
     import recv_fifo_plane_amd as xf
     torch = torch_mod()
     what = "%s %s nch=%d nslots=%d slot=%d lanes=%d block=%d off=(%d,%d) %s ord=%d read=%d" % (
         label, proto, nch, nslots, slot_bytes, lanes, block, src_off, dst_off, fifo_loc, ordering,
-        p2p_read) + (" jitter=%#x" % jitter if jitter else "")
+        p2p_read) + (" jitter=%#x" % jitter if jitter else "") + (
+        " place_trials=%d" % place_trials if place_trials else "")
     log("case: " + what + " sizes=" + str(list(sizes)[:6]))
     conn = xf.Conn(proto, nch, nslots, slot_bytes, fifo_loc, wgs_per_channel=lanes,
                    block_threads=block, ctrl_loc=ctrl_loc, xcd_pairing=xcd_pairing,
-                   ordering=ordering, p2p_read=p2p_read)
+                   ordering=ordering, p2p_read=p2p_read, place_trials=place_trials)
+    if place_trials:
+        # the kept candidate must look like a new connection
+        for c in range(nch):
+            st = conn.query(c)
+            assert (st["head"], st["tail"], st["steps"], st["error"]) == (0, 0, 0, 0), (what, st)
+            assert not conn.read_fifo(c).any(), (what, "FIFO not zeroed", c)
     if jitter:
         conn.set_jitter(jitter)
     ocn = oracle.Conn(oracle_proto(proto, fifo_loc), nch, nslots, slot_bytes)

@@ -82,6 +82,39 @@ def test_p2p_read_is_simple_in_hbm_only(proto, fifo_loc, attr):
     assert e.value.status == X.XFER_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("proto,fifo_loc,attr", [
+    ("ll", "device", dict(place_trials=-1)),
+    ("ll", "device", dict(place_trials=9)),
+    ("zc", "device", dict(place_trials=2)),
+    ("zcd", "device", dict(place_trials=4)),
+    ("simple", "host", dict(place_trials=2)),
+    ("ll", "host", dict(place_trials=2)),
+    ("simple", "relay", dict(place_trials=2)),
+    ("ll", "device", dict(place_trials=2, ctrl_loc=X.XFER_CTRL_HOST)),
+    ("simple", "device", dict(place_trials=2, p2p_read=1)),
+])
+def test_place_trials_needs_a_polled_fifo_in_hbm(proto, fifo_loc, attr):
+    # placement by measured latency times a ping-pong through the FIFO and
+    # counters in HBM; zero-copy has no FIFO, host memory is not placed
+    with pytest.raises(xf.XferError) as e:
+        xf.Conn(proto, 1, 8, 128, fifo_loc, **attr)
+    assert e.value.status == X.XFER_ERR_INVALID_ARG
+    assert "place_trials" in xf.last_error()
+
+
+def test_attribute_struct_matches_the_header():
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "xfer.h")).read()
+    body = hdr[hdr.index("typedef struct {", hdr.index("Optional creation attributes")):
+               hdr.index("} xfer_attr;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(?:int|uint32_t)\s+(\w+);", body)
+    assert fields == [f[0] for f in X.xfer_attr._fields_]
+    with pytest.raises(TypeError):
+        X.make_attr(no_such_field=1)
+    a = X.make_attr(place_trials=3, p2p_read=1)
+    assert (a.place_trials, a.p2p_read, a.wgs_per_channel) == (3, 1, 0)
+
+
 @pytest.mark.parametrize("attr", [dict(wgs_per_channel=17), dict(block_threads=96),
                                   dict(block_threads=2048), dict(ctrl_loc=3), dict(roles=3),
                                   dict(xcd_pairing=2)])
