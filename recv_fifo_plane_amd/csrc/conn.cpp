@@ -722,8 +722,8 @@ extern "C" int xfer_conn_destroy(xfer_conn* c) {
   return XFER_OK;
 }
 
-static // Runs of a traced or jittered connection take the debug kernel variant.
-bool debug_of(const xfer_conn* c) { return c->trace != nullptr || c->jitter != 0; }
+// Runs of a traced or jittered connection take the debug kernel variant.
+static bool debug_of(const xfer_conn* c) { return c->trace != nullptr || c->jitter != 0; }
 
 Variant variant_of(const xfer_conn* c, bool aligned) {
   return Variant{c->proto, c->scope, c->ordering, aligned ? 1 : 0, debug_of(c) ? 1 : 0};

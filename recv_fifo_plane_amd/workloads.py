@@ -24,11 +24,15 @@ from . import xfer as X
 W1 = dict(name="simple_1ch_4MiB", proto="simple", nchannels=1, nslots=8, slot_bytes=128 << 10,
           fifo_loc="device", wgs_per_channel=1, block_threads=512, nbytes=4 << 20)
 
-# Each connection's FIFO and counters are placed by measured latency at the
-# fastest of eight offsets 2 KiB apart (place_trials): the time of a small
-# message's hand-off depends on the physical granule of the polled lines.
+# 16 workgroup pairs of 256 threads: a whole 16 KiB step is one line per
+# thread, so messages up to 16 KiB take one pass (swept: 1.0-1.2 us one-way
+# up to 16 KiB and 3.4 us at 64 KiB, against 3.7 and 8.6 us with one
+# 1024-thread pair).  Each connection's FIFO and counters are placed by
+# measured latency at the fastest of eight offsets 2 KiB apart
+# (place_trials): the time of a hand-off depends on the physical granule of
+# the polled lines.
 W2 = dict(name="ll_pingpong", proto="ll", nchannels=1, nslots=8, slot_bytes=32 << 10,
-          fifo_loc="device", wgs_per_channel=1, block_threads=1024, iters=10000, place_trials=8)
+          fifo_loc="device", wgs_per_channel=16, block_threads=256, iters=10000, place_trials=8)
 W2_SIZES = [8 << i for i in range(14)]  # 8 B .. 64 KiB
 
 # 4 workgroups per channel side as the workload fixes them; the block size

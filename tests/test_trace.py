@@ -100,6 +100,28 @@ def test_trace_fifo_protocols(proto, fifo_loc, jitter):
 
 
 @pytest.mark.parametrize("jitter", [0, 0x5EED])
+@pytest.mark.parametrize("nslots", [1, 3, 8, 12])
+def test_trace_ll_one_line_per_thread(nslots, jitter):
+    # steps of at most one line per thread (the one-pass path), many per
+    # transfer: every step is stamped, a step's lines are seen after the
+    # producer published them, and its slot's previous step was handed back
+    # before the producer took it again
+    nch, lanes, slot, n = 2, 2, 4096, 60_001
+    log("case: trace ll one line per thread nslots=%d jitter=%#x" % (nslots, jitter))
+    R, _, S = traced_run("ll", nch, nslots, slot, lanes, n, jitter=jitter)
+    ks = check_complete(R, n, nch, lanes, S)
+    for c in range(nch):
+        for w in range(lanes):
+            for g in range(ks[c]):
+                L = min(S, oracle.partition(n, nch)[1][c] - g * S)
+                if w * 256 >= (L + 3) // 4:
+                    continue
+                assert ev(R, c, w, 0, g, 1)["time"] < ev(R, c, w, 1, g, 0)["time"], (c, w, g)
+                if g >= nslots:
+                    assert ev(R, c, w, 1, g - nslots, 1)["time"] < ev(R, c, w, 0, g, 0)["time"]
+
+
+@pytest.mark.parametrize("jitter", [0, 0x5EED])
 @pytest.mark.parametrize("proto", ["zc", "zcd"])
 def test_trace_zero_copy_offsets_match_the_oracle(proto, jitter):
     nch, lanes, slot, n = 4, 2, 4096, 100_003
