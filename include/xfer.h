@@ -109,7 +109,13 @@ typedef struct {
                            an XCD's producers dispatched before its consumers (zero-copy
                            through ptrExchange: its receivers first, since each producer
                            waits for its receiver's first address) (the grid is
-                           padded to a multiple of 16 workgroups; padding exits at once);
+                           padded to a multiple of 16 workgroups; padding exits at once).
+                           Each hardware queue starts dealing blocks to the XCDs at an XCD
+                           of its own; where a one-time check at the first creation on a
+                           device sees a strict rotation over 8 XCDs on every stream,
+                           blocks take their place from the XCD id they read, so a pair's
+                           XCD does not depend on the stream (environment
+                           XFER_XCD_BY_ID=0 turns this off);
                            -1: dispatch order (producers on even block ids, which the
                            hardware deals to XCDs 0, 2, 4 and 6 only) */
   int roles;            /* fault injection: 0 = both sides (default), 1 = producer only,

@@ -23,6 +23,7 @@
 struct xfer_conn {
   int proto = 0, nch = 0, nslots = 0, fifo_loc = 0, ctrl_loc = 0;
   int lanes = 1, block = 256, xcd_pairing = 0, roles = 3, ordering = 0, p2p_read = 0;
+  uint32_t xcd_remap = 0;  // the kernels' remap: 0 dispatch order, 1 paired, 2 paired by XCD id
   size_t slot_bytes = 0, step_bytes = 0;
   uint32_t timeout_ms = 0;
   uint64_t timeout_ticks = 0;
@@ -250,6 +251,28 @@ uint32_t wgs_of(const xfer_conn* c) { return uint32_t(c->nch) * uint32_t(c->lane
 // logical_wg); its remap needs a grid of a multiple of 16, so the grid is
 // padded with workgroups that exit at once.
 uint32_t grid_of(int pairing, uint32_t total) { return pairing ? (total + 15u) & ~15u : total; }
+
+// Whether blocks may take their place from their XCD id on this device
+// (xcc_rotation_ok), checked once per device.
+int xcc_remap_ok(int dev, bool* ok) {
+  static std::mutex mu;
+  static std::map<int, bool> known;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = known.find(dev);
+  if (it != known.end()) {
+    *ok = it->second;
+    return XFER_OK;
+  }
+  const char* env = getenv("XFER_XCD_BY_ID");
+  if (env && env[0] == '0') {
+    known[dev] = *ok = false;
+    return XFER_OK;
+  }
+  const hipError_t e = xcc_rotation_ok(ok);
+  if (e != hipSuccess) return hip_fail(e, "xfer_conn_create: XCD deal check");
+  known[dev] = *ok;
+  return XFER_OK;
+}
 
 // Resident-workgroup capacity per (device, kernel variant, block size),
 // queried once: the runtime query costs far more than a launch.
@@ -524,6 +547,15 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
                            : fail(XFER_ERR_HIP, "device reports no wall-clock rate");
   }
   c->timeout_ticks = uint64_t(c->timeout_ms) * uint64_t(khz);
+  if (c->xcd_pairing) {
+    bool by_id = false;
+    const int rc = xcc_remap_ok(c->device, &by_id);
+    if (rc) {
+      delete c;
+      return rc;
+    }
+    c->xcd_remap = by_id ? 2u : 1u;
+  }
 
   // FIFO: HBM, or pinned host memory mapped into the device (fine-grained,
   // so device accesses reach host memory rather than a non-coherent cache).
@@ -752,7 +784,7 @@ extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nb
   args.nconn = 1;
   args.iters = uint32_t(iters);
   args.total_wgs = total;
-  args.xcd_remap = c->xcd_pairing ? 1u : 0u;
+  args.xcd_remap = c->xcd_remap;
   args.timeout_ticks = c->timeout_ticks;
   hipError_t e = launch_run1(v, args, c->block, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "xfer_run launch");
@@ -824,7 +856,7 @@ extern "C" int xfer_run_messages(xfer_conn* c, const void* src, void* dst, const
     args.nconn = 1;
     args.iters = 1;
     args.total_wgs = total;
-    args.xcd_remap = c->xcd_pairing ? 1u : 0u;
+    args.xcd_remap = c->xcd_remap;
     args.timeout_ticks = c->timeout_ticks;
     args.nmsgs = uint32_t(cnt);
     for (size_t i = 0; i < cnt; ++i) args.msgs[i] = msgs[first + i];
@@ -903,7 +935,7 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
   args.nconn = uint32_t(live);
   args.iters = 1;
   args.total_wgs = grid;
-  args.xcd_remap = first->xcd_pairing ? 1u : 0u;
+  args.xcd_remap = first->xcd_remap;
   args.timeout_ticks = first->timeout_ticks;
   hipError_t e = launch_runB(v, args, first->block, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "xfer_run_batch launch");
@@ -955,7 +987,7 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
   args.rev = conn_args(rev, b, cbuf, nbytes, 0);
   args.iters = uint32_t(iters);
   args.total_wgs = total;
-  args.xcd_remap = fwd->xcd_pairing ? 1u : 0u;
+  args.xcd_remap = fwd->xcd_remap;
   args.timeout_ticks = std::max(fwd->timeout_ticks, rev->timeout_ticks);
   hipError_t e = launch_ping(v, args, fwd->block, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "xfer_run_pingpong launch");

@@ -1031,24 +1031,34 @@ __device__ __forceinline__ uint32_t xcc_id() {
 // Logical workgroup of this block.  A dispatch's blocks are dealt
 // round-robin to the 8 XCDs, but each hardware queue starts the deal at an
 // XCD of its own: block b runs on XCD (b + r) % 8, with r fixed per queue
-// (measured 0, 5, 6 and 7 on different streams of one process).  With the
-// remap, the block first takes position p = (b + r) mod total, read back from
-// its XCD id, so p % 8 is its XCD whichever stream launched it; p is a
-// permutation of the grid, since r is the same for every block of the
-// dispatch.  Then (the host pads the grid to a multiple of 16; logical ids
-// past the real workgroups exit at once) XCD x serves the total/16
-// consecutive pairs starting at x * total/16: its first total/16 blocks are
-// their producers, the rest their consumers.  A pair then shares one XCD,
+// (measured 0, 5, 6 and 7 on different streams of one process).  Remap 1
+// takes p = b; remap 2, which the host enables only once it has seen that
+// deal on this device (xcc_rotation_ok), takes p = (b + r) mod total with r
+// read back from the block's own XCD id, so that p % 8 is its XCD
+// whichever stream launched it.  Both are permutations of the grid, the
+// second because r is the same for every block of the dispatch.  Then (the
+// host pads the grid to a multiple of 16; logical ids past the real
+// workgroups exit at once) position p % 8 serves the total/16 consecutive
+// pairs starting at (p % 8) * total/16: its first total/16 blocks are their
+// producers, the rest their consumers.  A pair then shares one XCD,
 // producers spread evenly over the XCDs and over each XCD's dispatch order,
-// and a channel's XCD, on which the latency of its polled lines depends,
-// does not change with the stream.
+// and with remap 2 a channel's XCD, on which the latency of its polled
+// lines depends, does not change with the stream.
 __device__ __forceinline__ uint32_t logical_wg(uint32_t remap, uint32_t total) {
   const uint32_t b0 = blockIdx.x;
   if (!remap) return b0;
-  uint32_t b = b0 + ((xcc_id() - b0) & 7u);
-  if (b >= total) b -= total;
+  uint32_t b = b0;
+  if (remap == 2) {
+    b += (xcc_id() - b0) & 7u;
+    if (b >= total) b -= total;
+  }
   const uint32_t half = total / 16u, s = b / 8u;
   return 2u * ((b % 8u) * half + s % half) + s / half;
+}
+
+// Records the XCD id of each block (the host's check of the deal).
+__global__ void xcc_probe_kernel(uint32_t* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();
 }
 
 template <int PROTO, int SC, int ORD, bool AL, int MAXB, bool DBG>
@@ -1238,6 +1248,37 @@ hipError_t launch_runB(const Variant& v, const RunArgs<16>& a, int block, hipStr
 
 hipError_t launch_ping(const Variant& v, const PingArgs& a, int block, hipStream_t s) {
   return launch(pick_ping(v), a, a.total_wgs, block, s);
+}
+
+// Whether the current device deals blocks to 8 XCDs in strict rotation on
+// every stream: a probe grid on each of several streams (more than the
+// hardware queues a process gets) must see XCD (x0 + b) % 8 at block b,
+// with x0 in 0..7.  A device partitioned into fewer XCDs, or any other
+// deal, fails the check.
+hipError_t xcc_rotation_ok(bool* ok) {
+  constexpr int kStreams = 8, kBlocks = 64;
+  *ok = false;
+  uint32_t* d = nullptr;
+  hipError_t e = hipMalloc(&d, sizeof(uint32_t) * kStreams * kBlocks);
+  if (e != hipSuccess) return e;
+  hipStream_t st[kStreams] = {};
+  int made = 0;
+  for (; made < kStreams && e == hipSuccess; ++made) e = hipStreamCreate(&st[made]);
+  if (e != hipSuccess) --made;
+  for (int i = 0; i < made && e == hipSuccess; ++i)
+    e = launch(xcc_probe_kernel, d + i * kBlocks, kBlocks, 64, st[i]);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  uint32_t h[kStreams * kBlocks];
+  if (e == hipSuccess) e = hipMemcpy(h, d, sizeof(h), hipMemcpyDeviceToHost);
+  bool good = e == hipSuccess && made == kStreams;
+  for (int i = 0; good && i < kStreams; ++i) {
+    const uint32_t x0 = h[i * kBlocks];
+    for (int b = 0; good && b < kBlocks; ++b) good = x0 < 8u && h[i * kBlocks + b] == (x0 + b) % 8u;
+  }
+  for (int i = 0; i < made; ++i) (void)hipStreamDestroy(st[i]);
+  (void)hipFree(d);
+  *ok = good;
+  return e;
 }
 
 hipError_t max_resident(const Variant& v, int kind, int block, int* wgs) {

@@ -98,7 +98,7 @@ struct RunArgs {
   uint32_t nconn;
   uint32_t iters;
   uint32_t total_wgs;
-  uint32_t xcd_remap;    // 1: pairs on one XCD, placed by the XCD id (the kernels' logical_wg)
+  uint32_t xcd_remap;    // 0: dispatch order; 1: pairs on one XCD; 2: the same by XCD id
   uint64_t timeout_ticks;
   uint32_t nmsgs;        // single-connection launches only
   uint32_t pad;
@@ -130,5 +130,6 @@ hipError_t launch_ping(const Variant& v, const PingArgs& a, int block, hipStream
 // Workgroups of `block` threads the device can hold resident at once for
 // the variant's kernel (batch selects the batched kernel).
 hipError_t max_resident(const Variant& v, int kind, int block, int* wgs);
+hipError_t xcc_rotation_ok(bool* ok);
 
 }  // namespace xfer
