@@ -778,7 +778,7 @@ extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nb
   const Variant v = variant_of(c, aligned16(src) && aligned16(dst));
   rc = check_resident(v, 0, c->block, total, "xfer_run");
   if (rc) return rc;
-  RunArgs<1> args;
+  RunOne args;
   memset(&args, 0, sizeof(args));
   args.conn[0] = conn_args(c, src, dst, nbytes, 0);
   args.nconn = 1;
@@ -846,9 +846,9 @@ extern "C" int xfer_run_messages(xfer_conn* c, const void* src, void* dst, const
   DeviceGuard g(c->device);
   const uint32_t total = grid_of(c->xcd_pairing, wgs_of(c));
   const Variant v = variant_of(c, aligned);
-  rc = check_resident(v, 0, c->block, total, "xfer_run_messages");
+  rc = check_resident(v, 3, c->block, total, "xfer_run_messages");
   if (rc) return rc;
-  RunArgs<1> args;
+  RunList args;
   for (size_t first = 0; first < msgs.size(); first += kMaxMsgs) {
     const size_t cnt = std::min<size_t>(kMaxMsgs, msgs.size() - first);
     memset(&args, 0, sizeof(args));
@@ -860,7 +860,7 @@ extern "C" int xfer_run_messages(xfer_conn* c, const void* src, void* dst, const
     args.timeout_ticks = c->timeout_ticks;
     args.nmsgs = uint32_t(cnt);
     for (size_t i = 0; i < cnt; ++i) args.msgs[i] = msgs[first + i];
-    hipError_t e = launch_run1(v, args, c->block, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_runL(v, args, c->block, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "xfer_run_messages launch");
   }
   if (c->relay) {
@@ -878,7 +878,7 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
   if (n < 1 || n > XFER_MAX_BATCH || !conns || !src || !dst || !nbytes)
     return fail(XFER_ERR_INVALID_ARG, "xfer_run_batch: need 1 <= n <= XFER_MAX_BATCH and arrays");
   std::vector<std::vector<uint64_t>> adds(static_cast<size_t>(n));
-  RunArgs<16> args;
+  RunBatch args;
   memset(&args, 0, sizeof(args));
   uint32_t total = 0;
   bool aligned = true;

@@ -970,8 +970,8 @@ struct StepCursor {
 // Receiver (one thread): publish the destination of the next step (the base
 // of its chunk in B) whenever the word is clear; complete steps once tail
 // passes them by publishing head.
-template <int SC, int ORD, int MAXB>
-__device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<MAXB>& args,
+template <int SC, int ORD, int MAXB, int NMSG>
+__device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<MAXB, NMSG>& args,
                         uint64_t ticks) {
   using O = Order<SC, ORD>;
   if (threadIdx.x != 0) return;
@@ -1061,8 +1061,8 @@ __global__ void xcc_probe_kernel(uint32_t* out) {
   if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();
 }
 
-template <int PROTO, int SC, int ORD, bool AL, int MAXB, bool DBG>
-__global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
+template <int PROTO, int SC, int ORD, bool AL, int MAXB, int NMSG, bool DBG>
+__global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB, NMSG> args) {
   __shared__ Shared sh;
   if (threadIdx.x == 0) sh.err = 0;
   __syncthreads();
@@ -1085,7 +1085,7 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB> args) {
   const uint64_t ticks = args.timeout_ticks;
   if constexpr (PROTO == kProtoZC) {
     if (role == 1) {
-      zc_recv<SC, ORD, MAXB>(A, c, sd, args, ticks);
+      zc_recv<SC, ORD, MAXB, NMSG>(A, c, sd, args, ticks);
       return;
     }
   }
@@ -1167,39 +1167,41 @@ __global__ void __launch_bounds__(1024) ping_kernel(PingArgs args) {
 }
 
 // --------------------------------------------------------- dispatch tables
-template <int MAXB>
-using RunFn = void (*)(RunArgs<MAXB>);
+template <int MAXB, int NMSG>
+using RunFn = void (*)(RunArgs<MAXB, NMSG>);
 using PingFn = void (*)(PingArgs);
 
-template <int MAXB, int P, int SC, int ORD, bool DBG>
-RunFn<MAXB> pick_run_al(bool al) {
-  return al ? run_kernel<P, SC, ORD, true, MAXB, DBG> : run_kernel<P, SC, ORD, false, MAXB, DBG>;
+template <int MAXB, int NMSG, int P, int SC, int ORD, bool DBG>
+RunFn<MAXB, NMSG> pick_run_al(bool al) {
+  return al ? run_kernel<P, SC, ORD, true, MAXB, NMSG, DBG>
+            : run_kernel<P, SC, ORD, false, MAXB, NMSG, DBG>;
 }
 
-template <int MAXB, int P, int SC, bool DBG>
-RunFn<MAXB> pick_run_ord(int ord, bool al) {
-  return ord == kOrdFenced ? pick_run_al<MAXB, P, SC, kOrdFenced, DBG>(al)
-                           : pick_run_al<MAXB, P, SC, kOrdCoherent, DBG>(al);
+template <int MAXB, int NMSG, int P, int SC, bool DBG>
+RunFn<MAXB, NMSG> pick_run_ord(int ord, bool al) {
+  return ord == kOrdFenced ? pick_run_al<MAXB, NMSG, P, SC, kOrdFenced, DBG>(al)
+                           : pick_run_al<MAXB, NMSG, P, SC, kOrdCoherent, DBG>(al);
 }
 
-template <int MAXB, int P, bool DBG>
-RunFn<MAXB> pick_run_dbg(const Variant& v) {
-  return v.scope == kScopeSystem ? pick_run_ord<MAXB, P, kScopeSystem, DBG>(v.ordering, v.aligned)
-                                 : pick_run_ord<MAXB, P, kScopeAgent, DBG>(v.ordering, v.aligned);
+template <int MAXB, int NMSG, int P, bool DBG>
+RunFn<MAXB, NMSG> pick_run_dbg(const Variant& v) {
+  return v.scope == kScopeSystem
+             ? pick_run_ord<MAXB, NMSG, P, kScopeSystem, DBG>(v.ordering, v.aligned)
+             : pick_run_ord<MAXB, NMSG, P, kScopeAgent, DBG>(v.ordering, v.aligned);
 }
 
-template <int MAXB, int P>
-RunFn<MAXB> pick_run_sc(const Variant& v) {
-  return v.debug ? pick_run_dbg<MAXB, P, true>(v) : pick_run_dbg<MAXB, P, false>(v);
+template <int MAXB, int NMSG, int P>
+RunFn<MAXB, NMSG> pick_run_sc(const Variant& v) {
+  return v.debug ? pick_run_dbg<MAXB, NMSG, P, true>(v) : pick_run_dbg<MAXB, NMSG, P, false>(v);
 }
 
-template <int MAXB>
-RunFn<MAXB> pick_run(const Variant& v) {
+template <int MAXB, int NMSG>
+RunFn<MAXB, NMSG> pick_run(const Variant& v) {
   switch (v.proto) {
-    case kProtoSimple: return pick_run_sc<MAXB, kProtoSimple>(v);
-    case kProtoLL: return pick_run_sc<MAXB, kProtoLL>(v);
-    case kProtoZCD: return pick_run_sc<MAXB, kProtoZCD>(v);
-    default: return pick_run_sc<MAXB, kProtoZC>(v);
+    case kProtoSimple: return pick_run_sc<MAXB, NMSG, kProtoSimple>(v);
+    case kProtoLL: return pick_run_sc<MAXB, NMSG, kProtoLL>(v);
+    case kProtoZCD: return pick_run_sc<MAXB, NMSG, kProtoZCD>(v);
+    default: return pick_run_sc<MAXB, NMSG, kProtoZC>(v);
   }
 }
 
@@ -1238,12 +1240,16 @@ static hipError_t launch(Fn fn, const Args& a, uint32_t grid, int block, hipStre
   return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(block), kargs, 0, s);
 }
 
-hipError_t launch_run1(const Variant& v, const RunArgs<1>& a, int block, hipStream_t s) {
-  return launch(pick_run<1>(v), a, a.total_wgs, block, s);
+hipError_t launch_run1(const Variant& v, const RunOne& a, int block, hipStream_t s) {
+  return launch(pick_run<1, 1>(v), a, a.total_wgs, block, s);
 }
 
-hipError_t launch_runB(const Variant& v, const RunArgs<16>& a, int block, hipStream_t s) {
-  return launch(pick_run<16>(v), a, a.total_wgs, block, s);
+hipError_t launch_runL(const Variant& v, const RunList& a, int block, hipStream_t s) {
+  return launch(pick_run<1, kMaxMsgs>(v), a, a.total_wgs, block, s);
+}
+
+hipError_t launch_runB(const Variant& v, const RunBatch& a, int block, hipStream_t s) {
+  return launch(pick_run<16, 1>(v), a, a.total_wgs, block, s);
 }
 
 hipError_t launch_ping(const Variant& v, const PingArgs& a, int block, hipStream_t s) {
@@ -1287,8 +1293,10 @@ hipError_t max_resident(const Variant& v, int kind, int block, int* wgs) {
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const void* fn = kind == 0   ? reinterpret_cast<const void*>(pick_run<1>(v))
-                   : kind == 1 ? reinterpret_cast<const void*>(pick_run<16>(v))
+  // kind: 0 one transfer, 1 a batch, 2 the ping-pong, 3 a message list
+  const void* fn = kind == 0   ? reinterpret_cast<const void*>(pick_run<1, 1>(v))
+                   : kind == 1 ? reinterpret_cast<const void*>(pick_run<16, 1>(v))
+                   : kind == 3 ? reinterpret_cast<const void*>(pick_run<1, kMaxMsgs>(v))
                                : reinterpret_cast<const void*>(pick_ping(v));
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0);
   if (e != hipSuccess) return e;

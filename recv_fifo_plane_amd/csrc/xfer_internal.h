@@ -92,7 +92,11 @@ constexpr int kMaxMsgs = 128;  // messages carried by one launch's arguments
 // order (nmsgs == 0: the single message {0, conn.nbytes}).  Every message is
 // partitioned and numbered exactly as a separate run would be; the FIFO
 // pipeline just flows from one message into the next.
-template <int MAXB>
+// NMSG: capacity of the message list.  Only message-list launches carry
+// one (kMaxMsgs); the others carry a single unused entry, since the size of
+// the argument block is paid on every launch (about 1.2 us more per launch
+// with 2 KiB more, measured on an empty kernel).
+template <int MAXB, int NMSG>
 struct RunArgs {
   ConnArgs conn[MAXB];
   uint32_t nconn;
@@ -102,9 +106,13 @@ struct RunArgs {
   uint64_t timeout_ticks;
   uint32_t nmsgs;        // single-connection launches only
   uint32_t pad;
-  MsgDesc msgs[kMaxMsgs];
+  MsgDesc msgs[NMSG];
 };
-static_assert(sizeof(RunArgs<16>) <= 4096, "kernel arguments are limited to 4 KiB");
+using RunOne = RunArgs<1, 1>;           // one transfer (xfer_run, xfer_run_loop)
+using RunList = RunArgs<1, kMaxMsgs>;   // a message list (xfer_run_messages)
+using RunBatch = RunArgs<16, 1>;        // several connections (xfer_run_batch)
+static_assert(sizeof(RunList) <= 4096 && sizeof(RunBatch) <= 4096,
+              "kernel arguments are limited to 4 KiB");
 
 struct PingArgs {
   ConnArgs fwd, rev;     // fwd: a -> b (X sends), rev: b -> c (Y sends)
@@ -124,8 +132,9 @@ struct Variant {
   int debug;     // 1: the debug variant (step trace, jitter)
 };
 
-hipError_t launch_run1(const Variant& v, const RunArgs<1>& a, int block, hipStream_t s);
-hipError_t launch_runB(const Variant& v, const RunArgs<16>& a, int block, hipStream_t s);
+hipError_t launch_run1(const Variant& v, const RunOne& a, int block, hipStream_t s);
+hipError_t launch_runL(const Variant& v, const RunList& a, int block, hipStream_t s);
+hipError_t launch_runB(const Variant& v, const RunBatch& a, int block, hipStream_t s);
 hipError_t launch_ping(const Variant& v, const PingArgs& a, int block, hipStream_t s);
 // Workgroups of `block` threads the device can hold resident at once for
 // the variant's kernel (batch selects the batched kernel).
