@@ -45,6 +45,9 @@ struct xfer_conn {
   uint32_t trace_per = 0;           // records per (channel, lane, side) ring
   uint32_t jitter = 0;              // seed of the debug jitter, 0 = none
   std::vector<uint64_t> steps;   // per channel, host bookkeeping of completed steps
+  std::vector<uint64_t> add;     // per channel, steps a run adds (scratch of the run calls)
+  int cap_one[2][2] = {{-1, -1}, {-1, -1}};  // resident capacity of a single-transfer
+                                              // launch, by [aligned][debug]; -1 unknown
 };
 
 static_assert(sizeof(xfer_trace_rec) == sizeof(xfer::TraceRec) &&
@@ -82,13 +85,13 @@ int hip_fail(hipError_t e, const char* what) {
 // Restores the caller's current device on scope exit.
 struct DeviceGuard {
   int prev = -1;
+  bool changed = false;
   explicit DeviceGuard(int dev) {
     if (hipGetDevice(&prev) != hipSuccess) prev = -1;
-    if (prev != dev) (void)hipSetDevice(dev);
+    if (prev != dev) changed = hipSetDevice(dev) == hipSuccess;
   }
   ~DeviceGuard() {
-    int cur = -1;
-    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    if (changed && prev >= 0) (void)hipSetDevice(prev);
   }
 };
 
@@ -276,12 +279,10 @@ int xcc_remap_ok(int dev, bool* ok) {
 
 // Resident-workgroup capacity per (device, kernel variant, block size),
 // queried once: the runtime query costs far more than a launch.
-int resident_capacity(const Variant& v, int kind, int block, int* cap) {
+int resident_capacity(int dev, const Variant& v, int kind, int block, int* cap) {
   static std::mutex mu;
   static std::map<std::array<int, 8>, int> cache;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipError_t e = hipSuccess;
   const std::array<int, 8> key{dev, v.proto, v.scope, v.ordering, v.aligned, v.debug, kind, block};
   {
     std::lock_guard<std::mutex> lk(mu);
@@ -298,10 +299,16 @@ int resident_capacity(const Variant& v, int kind, int block, int* cap) {
   return XFER_OK;
 }
 
-int check_resident(const Variant& v, int kind, int block, uint32_t total, const char* who) {
-  int cap = 0;
-  const int rc = resident_capacity(v, kind, block, &cap);
-  if (rc) return rc;
+// The caller has made `dev` current (DeviceGuard).  `memo`, when given, is
+// the connection's own record of this capacity.
+int check_resident(int dev, const Variant& v, int kind, int block, uint32_t total,
+                   const char* who, int* memo = nullptr) {
+  int cap = memo ? *memo : -1;
+  if (cap < 0) {
+    const int rc = resident_capacity(dev, v, kind, block, &cap);
+    if (rc) return rc;
+    if (memo) *memo = cap;
+  }
   if (int64_t(total) > int64_t(cap))
     return fail(XFER_ERR_INVALID_ARG,
                 std::string(who) + ": " + std::to_string(total) +
@@ -770,13 +777,14 @@ extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nb
   if (!src || !dst) return fail(XFER_ERR_INVALID_ARG, "xfer_run: NULL src or dst with nbytes > 0");
   if (overlap(src, nbytes, dst, nbytes))
     return fail(XFER_ERR_INVALID_ARG, "xfer_run: src and dst overlap");
-  std::vector<uint64_t> add;
+  std::vector<uint64_t>& add = c->add;  // reused: no allocation per run
   rc = plan_steps(c, nbytes, uint64_t(iters), add, "xfer_run");
   if (rc) return rc;
   DeviceGuard g(c->device);
   const uint32_t total = grid_of(c->xcd_pairing, wgs_of(c));
   const Variant v = variant_of(c, aligned16(src) && aligned16(dst));
-  rc = check_resident(v, 0, c->block, total, "xfer_run");
+  rc = check_resident(c->device, v, 0, c->block, total, "xfer_run",
+                      &c->cap_one[v.aligned][v.debug]);
   if (rc) return rc;
   RunOne args;
   memset(&args, 0, sizeof(args));
@@ -846,7 +854,7 @@ extern "C" int xfer_run_messages(xfer_conn* c, const void* src, void* dst, const
   DeviceGuard g(c->device);
   const uint32_t total = grid_of(c->xcd_pairing, wgs_of(c));
   const Variant v = variant_of(c, aligned);
-  rc = check_resident(v, 3, c->block, total, "xfer_run_messages");
+  rc = check_resident(c->device, v, 3, c->block, total, "xfer_run_messages");
   if (rc) return rc;
   RunList args;
   for (size_t first = 0; first < msgs.size(); first += kMaxMsgs) {
@@ -930,7 +938,7 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
   for (int i = 0; i < n; ++i)
     if (debug_of(conns[i])) v.debug = 1;  // the others pass no buffer and no seed
   const uint32_t grid = grid_of(first->xcd_pairing, total);
-  int rc = check_resident(v, 1, first->block, grid, "xfer_run_batch");
+  int rc = check_resident(first->device, v, 1, first->block, grid, "xfer_run_batch");
   if (rc) return rc;
   args.nconn = uint32_t(live);
   args.iters = 1;
@@ -979,7 +987,7 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
   const Variant v{fwd->proto, scope, fwd->ordering,
                   (aligned16(a) && aligned16(b) && aligned16(cbuf)) ? 1 : 0,
                   (debug_of(fwd) || debug_of(rev)) ? 1 : 0};
-  rc = check_resident(v, 2, fwd->block, total, "xfer_run_pingpong");
+  rc = check_resident(fwd->device, v, 2, fwd->block, total, "xfer_run_pingpong");
   if (rc) return rc;
   PingArgs args;
   memset(&args, 0, sizeof(args));

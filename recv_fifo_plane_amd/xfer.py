@@ -129,6 +129,8 @@ _lib = None
 def lib() -> C.CDLL:
     """Loads libxfer.so (building it first only if it does not exist)."""
     global _lib
+    if _lib is not None:  # loaded: no lock on the per-call path
+        return _lib
     with _lock:
         if _lib is None:
             if not os.path.exists(_build.LIB):
