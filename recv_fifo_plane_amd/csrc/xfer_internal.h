@@ -137,8 +137,11 @@ hipError_t launch_runL(const Variant& v, const RunList& a, int block, hipStream_
 hipError_t launch_runB(const Variant& v, const RunBatch& a, int block, hipStream_t s);
 hipError_t launch_ping(const Variant& v, const PingArgs& a, int block, hipStream_t s);
 // Workgroups of `block` threads the device can hold resident at once for
-// the variant's kernel (batch selects the batched kernel).
+// the variant's kernel of launch kind 0 (one transfer), 1 (a batch of
+// connections), 2 (the ping-pong) or 3 (a message list).
 hipError_t max_resident(const Variant& v, int kind, int block, int* wgs);
+// Whether the current device deals a launch's blocks to 8 XCDs in strict
+// rotation on every stream (the kernels may then place blocks by XCD id).
 hipError_t xcc_rotation_ok(bool* ok);
 
 }  // namespace xfer
