@@ -987,9 +987,15 @@ __device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<M
   }
   uint64_t ndone = 0, npub = 0;
   Deadline dl(ticks, A.status);
+  // The word is clear when a launch starts: each earlier launch on the
+  // connection ended with every published address taken, and a failed one
+  // leaves the connection refusing runs.  So the first address goes out
+  // without a poll, one round trip earlier.
+  bool clear = true;
   while (ndone < total) {
     bool moved = false;
-    if (!cur.done && ld_u64<SC>(&sd.tx->ptrx) == 0) {
+    if (!cur.done && (clear || ld_u64<SC>(&sd.tx->ptrx) == 0)) {
+      clear = false;
       const uint64_t addr = reinterpret_cast<uint64_t>(A.dst + cur.off + cur.r.beg + cur.j * S);
       jitter(sd, sd.base + npub, 0);
       trace_step(A, sd, sd.base + npub++, 0, addr);
