@@ -33,6 +33,10 @@
  *     and persist across runs; step g (0-based) publishes tail = g+1.
  *   - Runs on one connection must be serialised (same stream, or synchronised
  *     streams).  Two launches that overlap on one connection race.
+ *   - Host threads: calls on one connection must not overlap in time (the
+ *     connection keeps host-side step bookkeeping); calls on different
+ *     connections may come from different threads at once.  The library's
+ *     shared state (per-device checks, occupancy caches) is locked.
  */
 #ifndef XFER_H
 #define XFER_H
