@@ -37,7 +37,8 @@ W2_SIZES = [8 << i for i in range(14)]  # 8 B .. 64 KiB
 
 # 4 workgroups per channel side as the workload fixes them; the block size
 # and dispatch order were swept (0.911-0.914 of the roofline at 704-832
-# threads in dispatch order, 0.903 with XCD pairing at 512).
+# threads in dispatch order; with pairs placed on one XCD by XCD id, 0.890
+# at 768, 0.904 at 512 and 0.873 at 1024 threads).
 W3 = dict(name="simple_32ch_1GiB", proto="simple", nchannels=32, nslots=8, slot_bytes=512 << 10,
           fifo_loc="device", wgs_per_channel=4, block_threads=768, xcd_pairing=-1,
           nbytes=1 << 30)
