@@ -33,6 +33,9 @@
  *     and persist across runs; step g (0-based) publishes tail = g+1.
  *   - Runs on one connection must be serialised (same stream, or synchronised
  *     streams).  Two launches that overlap on one connection race.
+ *   - Pinned host memory (host FIFOs, staging FIFOs, host counters) is
+ *     allocated on the NUMA node closest to the GPU where the runtime names
+ *     one; environment XFER_HOST_NUMA=0 turns that off.
  *   - Host threads: calls on one connection must not overlap in time (the
  *     connection keeps host-side step bookkeeping); calls on different
  *     connections may come from different threads at once.  The library's
