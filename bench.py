@@ -110,6 +110,44 @@ def check_no_error(conn, nch: int, what: str) -> None:
             raise RuntimeError("%s: channel %d state %s" % (what, c, st))
 
 
+def chan_steps(n: int, nch: int, step: int) -> list[int]:
+    """Steps of each channel in one transfer of n bytes: contiguous channel
+    ranges of ceil(n / nch) rounded up to 16 bytes, cut into steps."""
+    per = -(-n // nch)
+    per = (per + 15) & ~15
+    out = []
+    for c in range(nch):
+        b = min(n, c * per)
+        e = min(n, b + per)
+        out.append(-(-(e - b) // step))
+    return out
+
+
+def check_counters(conn, nch: int, step: int, transfers, what: str) -> None:
+    """Every launch moved what it was given: each channel's head and tail
+    (every lane's) equal the steps of all transfers run on the connection,
+    transfers = [(nbytes, times)], and the address word is clear."""
+    exp = [0] * nch
+    for n, times in transfers:
+        for c, k in enumerate(chan_steps(n, nch, step)):
+            exp[c] += k * times
+    for c in range(nch):
+        st = conn.query(c)
+        if (st["error"] or not st["lanes_agree"] or st["ptr_exchange"] or
+                (st["head"], st["tail"], st["steps"]) != (exp[c], exp[c], exp[c])):
+            raise RuntimeError("%s: channel %d state %s, expected head = tail = %d"
+                               % (what, c, st, exp[c]))
+
+
+def final_check(torch, T, launch, a, b) -> bool:
+    """One more launch into a cleared destination, then B == A."""
+    with torch.cuda.stream(T.stream):
+        b.zero_()
+        launch()
+    torch.cuda.synchronize()
+    return bool(torch.equal(a, b))
+
+
 def bench_w3(torch, T, W, synth, steps, warmup, cfg=None):
     cfg = cfg or W.W3
     n = cfg["nbytes"]
@@ -121,14 +159,18 @@ def bench_w3(torch, T, W, synth, steps, warmup, cfg=None):
     total, per = T.time_launches(lambda: conn.run(a, b, n, s), warmup, steps)
     med = T.median()
     torch.cuda.synchronize()
-    check_no_error(conn, cfg["nchannels"], "W3")
-    ok = bool(torch.equal(a, b))
+    ok = bool(torch.equal(a, b)) and final_check(torch, T, lambda: conn.run(a, b, n, s), a, b)
+    check_counters(conn, cfg["nchannels"], cfg["slot_bytes"], [(n, warmup + steps + 1)],
+                   cfg["name"])
     g, blk = conn.launch_shape()
     conn.close()
     del a, b
     return A, {"ms_per_step": total, "kernel_ms": per, "kernel_ms_median": med,
                "payload_gbs": n / (total * 1e-3) / 1e9,
-               "b_equals_a": ok, "workgroups": g, "block_threads": blk}
+               "b_equals_a": ok, "workgroups": g, "block_threads": blk,
+               "self_check": "B == A after every timed launch and after one more launch into a "
+                             "cleared B; every channel's head = tail = %d (64 steps x %d launches)"
+                             % (64 * (warmup + steps + 1), warmup + steps + 1)}
 
 
 def bench_w1(torch, T, W, synth):
@@ -139,8 +181,9 @@ def bench_w1(torch, T, W, synth):
     conn = W.make_conn(cfg)
     total, per = T.time_launches(lambda: conn.run(a, b, n, T.stream), 5, 100)
     med, low = T.median(), min(T.last)
-    check_no_error(conn, 1, "W1")
-    ok = bool(torch.equal(a, b))
+    ok = bool(torch.equal(a, b)) and final_check(torch, T, lambda: conn.run(a, b, n, T.stream),
+                                                 a, b)
+    check_counters(conn, 1, cfg["slot_bytes"], [(n, 106)], cfg["name"])
     conn.close()
     gbs = n / (per * 1e-3) / 1e9
     # Ceiling of one workgroup copying A -> B straight (zero-copy, one channel,
@@ -148,7 +191,7 @@ def bench_w1(torch, T, W, synth):
     zc = W.make_conn(dict(cfg, proto="zc", nslots=1, slot_bytes=n))
     b.zero_()
     _, per_zc = T.time_launches(lambda: zc.run(a, b, n, T.stream), 5, 100)
-    check_no_error(zc, 1, "W1 single-workgroup copy")
+    check_counters(zc, 1, n, [(n, 105)], "W1 single-workgroup copy")
     ok = ok and bool(torch.equal(a, b))
     zc.close()
     wg = n / (per_zc * 1e-3) / 1e9
@@ -172,6 +215,7 @@ def bench_w2(torch, T, W, synth):
     # and control words sit in HBM, which place_trials picks by measurement
     # (the spread over placements is measured below).
     fwd, rev = W.make_conn(cfg), W.make_conn(cfg)
+    done = []  # (bytes, messages) each connection has carried
     for size in W.W2_SIZES:
         A = synth.int32_uniform_bytes(size, synth.workload_seed(2) + size)
         a = torch.from_numpy(A).to("cuda")
@@ -179,8 +223,9 @@ def bench_w2(torch, T, W, synth):
         c = torch.zeros_like(a)
         total, per = T.time_launches(
             lambda: W.run_pingpong(fwd, rev, a, b, c, size, iters, T.stream), 1, 3)
-        check_no_error(fwd, 1, "W2")
-        check_no_error(rev, 1, "W2")
+        done.append((size, 4 * iters))
+        check_counters(fwd, 1, cfg["slot_bytes"] // 2, done, "W2 forward")
+        check_counters(rev, 1, cfg["slot_bytes"] // 2, done, "W2 reverse")
         ok = bool(torch.equal(a, b) and torch.equal(a, c))
         one_way_us = per * 1e3 / (2 * iters)
         out[str(size)] = {"one_way_us": round(one_way_us, 3),
@@ -254,8 +299,9 @@ def bench_w4(torch, T, W, synth):
         conn = W.make_conn(cfg)
         total, per = T.time_launches(lambda: conn.run(a, b, n, T.stream), 3, 20)
         med = T.median()
-        check_no_error(conn, cfg["nchannels"], "W4 pair " + proto)
-        ok = bool(torch.equal(a, b))
+        ok = bool(torch.equal(a, b)) and final_check(
+            torch, T, lambda: conn.run(a, b, n, T.stream), a, b)
+        check_counters(conn, cfg["nchannels"], cfg["slot_bytes"], [(n, 24)], cfg["name"])
         conn.close()
         gbs = n / (per * 1e-3) / 1e9
         res[key + "pair"] = {"payload_gbs": round(gbs, 2), "real_gbs": round(2 * gbs, 2),
@@ -270,11 +316,22 @@ def bench_w4(torch, T, W, synth):
         b = torch.empty_like(a)
         total, per = T.time_launches(lambda: ring.run(a, b, T.stream), 3, 20)
         med = T.median()
-        for e in ring.edges.values():
-            check_no_error(e, cfg["channels_per_edge"], "W4 ring " + proto)
         S = cfg["slice_bytes"]
-        ok = all(bool(torch.equal(a[r * S:(r + 1) * S], b[((r + 1) % 8) * S:((r + 1) % 8 + 1) * S]))
-                 for r in range(8))
+
+        def edges_ok():
+            return all(bool(torch.equal(a[r * S:(r + 1) * S],
+                                        b[((r + 1) % 8) * S:((r + 1) % 8 + 1) * S]))
+                       for r in range(8))
+
+        ok = edges_ok()
+        with torch.cuda.stream(T.stream):
+            b.zero_()
+            ring.run(a, b, T.stream)
+        torch.cuda.synchronize()
+        ok = ok and edges_ok()
+        for e in ring.edges.values():
+            check_counters(e, cfg["channels_per_edge"], cfg["slot_bytes"], [(S, 24)],
+                           cfg["name"])
         ring.close()
         del a, b
         gbs = tot / (per * 1e-3) / 1e9
@@ -295,12 +352,14 @@ def bench_w5(torch, T, W, synth):
     # each figure: the median over 5 runs of the whole message sequence
     T.time_launches(lambda: W.run_messages(conn, a, b, sizes, T.stream), 1, 5)
     each = T.median()
-    check_no_error(conn, cfg["nchannels"], "W5")
+    check_counters(conn, cfg["nchannels"], cfg["slot_bytes"], [(s_, 6) for s_ in sizes],
+                   cfg["name"])
     ok_each = bool(torch.equal(a, b))
     b.zero_()
     T.time_launches(lambda: W.run_message_list(conn, a, b, sizes, T.stream), 1, 5)
     total = T.median()
-    check_no_error(conn, cfg["nchannels"], "W5")
+    check_counters(conn, cfg["nchannels"], cfg["slot_bytes"], [(s_, 12) for s_ in sizes],
+                   cfg["name"])
     ok = ok_each and bool(torch.equal(a, b))
     conn.close()
     gbs = tot / (total * 1e-3) / 1e9
@@ -362,11 +421,12 @@ def bench_relay(torch, T, W, synth, dup_gbs):
     b = torch.empty_like(a)
     conn = W.make_conn(cfg)
     one, _ = T.time_launches(lambda: conn.run(a, b, n, T.stream), 1, 3)
-    check_no_error(conn, cfg["nchannels"], "relay")
+    check_counters(conn, cfg["nchannels"], cfg["slot_bytes"], [(n, 4)], cfg["name"])
     ok = bool(torch.equal(a[:n], b[:n]))
     b.zero_()
     lst, _ = T.time_launches(lambda: W.run_message_list(conn, a, b, sizes, T.stream), 1, 3)
-    check_no_error(conn, cfg["nchannels"], "relay messages")
+    check_counters(conn, cfg["nchannels"], cfg["slot_bytes"],
+                   [(n, 4)] + [(s_, 4) for s_ in sizes], cfg["name"])
     ok = ok and bool(torch.equal(a, b))
     conn.close()
     g1 = n / (one * 1e-3) / 1e9
@@ -387,7 +447,26 @@ def plain_copy_ceiling(torch, T) -> dict:
     b = torch.empty_like(a)
     a.fill_(7)
     total, per = T.time_launches(lambda: b.copy_(a), 3, 20)
-    return {"bytes": n, "ms": round(per, 4), "real_gbs": round(2 * n / (per * 1e-3) / 1e9, 1)}
+    return {"bytes": n, "ms": round(per, 4), "real_gbs": round(2 * n / (per * 1e-3) / 1e9, 1),
+            "payload_gbs": round(n / (per * 1e-3) / 1e9, 1)}
+
+
+def host_cpu() -> dict:
+    """The host CPU the oracle runs on: model name and logical CPUs."""
+    model = None
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = None
+    return {"model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
 
 
 def _cpu_threads() -> int:
@@ -435,7 +514,7 @@ def cpu_baseline(A, budget_s: float = 8.0) -> dict:
         r.close()
         lat[str(size)] = round(sec * 1e6 / (2 * iters), 3)
     return {"value": round(runs_t * A.size / el_t / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu": host_cpu(),
             "sample": "%d full transfers of the 1 GiB bf16 input through 32 channels x 8 x 512 KiB "
                       "in the oracle's threaded mode (64 actors on %d threads, %.1f s)"
                       % (runs_t, threads, el_t),
@@ -496,10 +575,16 @@ def main() -> int:
     algo_bytes = 4 * payload
     achieved = algo_bytes / (w3["kernel_ms"] * 1e-3) / 1e9
     traffic = pmc_traffic()
+    log("bench: plain 1 GiB device copy (context for the value)")
+    plain = plain_copy_ceiling(torch, T)
     line = {
         "metric": METRIC,
         "value": round(w3["payload_gbs"], 2),
         "unit": "GB/s",
+        # The same 1 GiB moved by a plain device copy (read A, write B: half the
+        # bytes of the FIFO round trip): what the FIFO costs against no FIFO.
+        "plain_copy_payload_gbs": plain["payload_gbs"],
+        "fifo_vs_plain_copy": round(w3["payload_gbs"] / plain["payload_gbs"], 3),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -544,7 +629,7 @@ def main() -> int:
         modes["relay_4ch_4MiB"] = bench_relay(
             torch, T, W, synth,
             None if w5["pinned_copy_duplex_serialized"] else w5["pinned_copy_duplex_gbs_each_way"])
-        modes["plain_copy_1GiB_torch"] = plain_copy_ceiling(torch, T)
+        modes["plain_copy_1GiB_torch"] = plain
         line["modes"] = modes
     if not args.no_cpu_baseline:
         log("bench: CPU baseline (oracle)")

@@ -28,7 +28,21 @@
  *     launch; in-kernel failures (a wait that exceeded the connection's
  *     timeout, a host abort) are reported by xfer_conn_query() once the
  *     stream has been synchronised, and make every later run on that
- *     connection fail with XFER_ERR_STATE.
+ *     connection fail with XFER_ERR_STATE.  A run already queued behind the
+ *     failed one when it failed does nothing: its workgroups read the
+ *     failure beside the counters on entry and leave every word as it is.
+ *   - Launch order: the library's launches on one device run one at a time,
+ *     in the order they are made, whatever their streams.  Every launch
+ *     needs all its workgroups resident at once, and two launches sharing
+ *     the GPU could each hold part of it and wait on the rest.  Launches on
+ *     one stream are ordered by the stream; a launch on another stream than
+ *     the device's previous launch first waits on the host until the device
+ *     has finished its work (hipDeviceSynchronize), so switching streams
+ *     costs a host-side wait and is not allowed under stream capture (keep
+ *     captured runs on one stream).  Kernels of
+ *     other code running beside a launch only delay the dispatch of its
+ *     workgroups; a kernel that waits on one of this library's launches must
+ *     not hold the GPU's resources meanwhile.
  *   - Step counters are 64-bit, start at 0 when the connection is created,
  *     and persist across runs; step g (0-based) publishes tail = g+1.
  *   - Runs on one connection must be serialised (same stream, or synchronised

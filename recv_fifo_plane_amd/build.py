@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libxfer.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "conn.cpp", "relay.cpp", "sched.cpp")]
+SOURCES = [os.path.join(CSRC, f)
+           for f in ("kernels.hip", "conn.cpp", "relay.cpp", "sched.cpp")]
 HEADERS = [os.path.join(CSRC, "xfer_internal.h"), os.path.join(CSRC, "relay.h"),
            os.path.join(ROOT, "include", "xfer.h")]
 ARCH = os.environ.get("XFER_OFFLOAD_ARCH", "gfx950")

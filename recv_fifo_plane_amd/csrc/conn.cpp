@@ -41,6 +41,9 @@ struct xfer_conn {
   size_t fifo_alloc = 0, ctrl_alloc = 0, ctrl_rx_alloc = 0;  // HBM bytes of the allocations
   xfer::Status* status_host = nullptr;
   xfer::Status* status_dev = nullptr;
+  uint32_t* err_dev = nullptr;     // device view of the failure mirror beside the counters
+  uint64_t* claims = nullptr;      // debug launches: per logical workgroup, last launch claiming it
+  uint64_t launch_seq = 0;         // launches made on the connection
   xfer::TraceRec* trace = nullptr;  // caller's step-trace buffer (device), or nullptr
   uint32_t trace_per = 0;           // records per (channel, lane, side) ring
   uint32_t jitter = 0;              // seed of the debug jitter, 0 = none
@@ -71,6 +74,9 @@ constexpr int kDefaultBlock = 256;
 // An HBM FIFO starts this far into its allocation (write mode), or this far
 // past the send side's control blocks (P2P read).
 constexpr size_t kFifoAlign = size_t(64) << 10;
+// The failure mirror: one 128-byte line after the control blocks (after the
+// receive side's blocks under P2P read), in the same memory as the counters.
+constexpr size_t kErrLine = 128;
 
 int fail(int code, const std::string& msg) {
   set_error(code, msg);
@@ -147,6 +153,7 @@ void release(xfer_conn* c) {
       (void)hipFree(c->ctrl_mem);
   }
   if (c->ctrl_rx_mem) (void)hipFree(c->ctrl_rx_mem);
+  if (c->claims) (void)hipFree(c->claims);
   if (c->status_host) (void)hipHostFree(c->status_host);
   delete c;
 }
@@ -216,10 +223,14 @@ void commit_steps(xfer_conn* c, const std::vector<uint64_t>& add) {
   for (int ch = 0; ch < c->nch; ++ch) c->steps[size_t(ch)] += add[size_t(ch)];
 }
 
-ConnArgs conn_args(const xfer_conn* c, const void* src, void* dst, uint64_t nbytes,
-                   uint32_t wg_begin) {
+// Device view of one launch of c; numbers the launch (debug launches check
+// with it that no two blocks take one logical workgroup).
+ConnArgs conn_args(xfer_conn* c, const void* src, void* dst, uint64_t nbytes, uint32_t wg_begin) {
   ConnArgs a;
   memset(&a, 0, sizeof(a));
+  a.err_dev = c->err_dev;
+  a.claims = c->claims;
+  a.launch_seq = ++c->launch_seq;
   a.fifo = c->fifo;
   a.fifo_rx = c->fifo_rx ? c->fifo_rx : c->fifo;
   a.relay = c->fifo_rx ? 1u : 0u;
@@ -318,6 +329,60 @@ int check_resident(int dev, const Variant& v, int kind, int block, uint32_t tota
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The library's launches on one device run one at a time, in the order they
+// were made, whatever their streams.  Each launch needs all its workgroups
+// resident at once (producers and consumers wait on each other), and the
+// resident check above compares one grid with the whole GPU: two launches
+// that each fit but together do not could both start partly resident and
+// wait on their undispatched halves until the timeout.  On one stream,
+// stream order already serialises them, so nothing is added there (an event
+// recorded after every launch measured 3-5 us per launch).  A launch on
+// another stream than the previous launch first waits, on the host, for the
+// device to finish what it holds, and goes ahead once no other launch of
+// the library came in meanwhile.  The device is synchronised without the
+// lock held, so a thread that still has to hand a relay its job after its
+// launch is never kept from doing so.  No stream handle is kept for later
+// use: the caller may destroy a stream at any time (destroying one waits
+// for its work, so a new stream that gets the old handle carries none of
+// it).  Kernels of other code do not wait on these, so they only delay a
+// dispatch, never block it.
+class LaunchGate {
+ public:
+  template <typename Launch>
+  hipError_t run(int dev, hipStream_t s, Launch&& launch) {
+    std::unique_lock<std::mutex> lk(mu_);
+    Dev& d = devs_[dev];
+    while (d.busy && d.last != s) {
+      const uint64_t seen = d.launches;
+      lk.unlock();
+      const hipError_t e = hipDeviceSynchronize();
+      lk.lock();
+      if (e != hipSuccess) return e;
+      if (d.launches == seen) d.busy = false;  // every launch so far has completed
+    }
+    const hipError_t e = launch();
+    if (e != hipSuccess) return e;
+    d.busy = true;
+    d.last = s;
+    ++d.launches;
+    return hipSuccess;
+  }
+
+ private:
+  struct Dev {
+    bool busy = false;           // a launch may still be on the device
+    hipStream_t last = nullptr;  // the stream of the last launch (compared, never used)
+    uint64_t launches = 0;
+  };
+  std::mutex mu_;
+  std::map<int, Dev> devs_;
+};
+
+LaunchGate& gate() {
+  static LaunchGate* g = new LaunchGate();  // never destroyed: launches may come during exit
+  return *g;
+}
 
 }  // namespace
 }  // namespace xfer
@@ -613,13 +678,14 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
     // blocks), which the receive side reads; tail sits in the receive
     // side's own blocks.  Both allocations live in HBM.
     const size_t fifo_off = (ctrl_bytes + kFifoAlign - 1) / kFifoAlign * kFifoAlign;
+    const size_t rx_bytes = ctrl_bytes + kErrLine;
     e = hipMalloc(&c->ctrl_mem, fifo_off + fifo_bytes);
     if (e != hipSuccess) {
       c->ctrl_mem = nullptr;
       release(c);
       return fail(XFER_ERR_NO_MEMORY, std::string("hipMalloc(send side): ") + hipGetErrorString(e));
     }
-    e = hipMalloc(&c->ctrl_rx_mem, ctrl_bytes);
+    e = hipMalloc(&c->ctrl_rx_mem, rx_bytes);
     if (e != hipSuccess) {
       c->ctrl_rx_mem = nullptr;
       release(c);
@@ -627,7 +693,7 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
                   std::string("hipMalloc(receive side): ") + hipGetErrorString(e));
     }
     c->ctrl_alloc = fifo_off + fifo_bytes;
-    c->ctrl_rx_alloc = ctrl_bytes;
+    c->ctrl_rx_alloc = rx_bytes;
     e = hipMemset(c->ctrl_mem, 0, c->ctrl_alloc);
     if (e == hipSuccess) e = hipMemset(c->ctrl_rx_mem, 0, c->ctrl_rx_alloc);
     if (e != hipSuccess) {
@@ -637,15 +703,16 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
     c->ctrl = static_cast<LaneCtrl*>(c->ctrl_mem);
     c->ctrl_rx = static_cast<LaneCtrl*>(c->ctrl_rx_mem);
     c->fifo = static_cast<uint8_t*>(c->ctrl_mem) + fifo_off;
+    c->err_dev = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(c->ctrl_rx_mem) + ctrl_bytes);
   } else if (c->ctrl_loc == XFER_CTRL_HOST) {
-    e = hipHostMalloc(&c->ctrl_mem, ctrl_bytes,
+    e = hipHostMalloc(&c->ctrl_mem, ctrl_bytes + kErrLine,
                       hipHostMallocMapped | hipHostMallocCoherent | near.flag());
     if (e != hipSuccess) {
       c->ctrl_mem = nullptr;
       release(c);
       return fail(XFER_ERR_NO_MEMORY, std::string("hipHostMalloc(ctrl): ") + hipGetErrorString(e));
     }
-    memset(c->ctrl_mem, 0, ctrl_bytes);
+    memset(c->ctrl_mem, 0, ctrl_bytes + kErrLine);
     void* dptr = nullptr;
     e = hipHostGetDevicePointer(&dptr, c->ctrl_mem, 0);
     if (e != hipSuccess) {
@@ -653,22 +720,37 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
       return hip_fail(e, "hipHostGetDevicePointer(ctrl)");
     }
     c->ctrl = static_cast<LaneCtrl*>(dptr);
+    c->err_dev = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(dptr) + ctrl_bytes);
   } else {
-    e = hipMalloc(&c->ctrl_mem, ctrl_bytes + place_slack);
+    e = hipMalloc(&c->ctrl_mem, ctrl_bytes + place_slack + kErrLine);
     if (e != hipSuccess) {
       c->ctrl_mem = nullptr;
       release(c);
       return fail(XFER_ERR_NO_MEMORY, std::string("hipMalloc(ctrl): ") + hipGetErrorString(e));
     }
-    c->ctrl_alloc = ctrl_bytes + place_slack;
+    c->ctrl_alloc = ctrl_bytes + place_slack + kErrLine;
     e = hipMemset(c->ctrl_mem, 0, c->ctrl_alloc);
     if (e != hipSuccess) {
       release(c);
       return hip_fail(e, "hipMemset(ctrl)");
     }
     c->ctrl = static_cast<LaneCtrl*>(c->ctrl_mem);
+    c->err_dev = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(c->ctrl_mem) + ctrl_bytes +
+                                             place_slack);
   }
   if (!c->p2p_read) c->ctrl_rx = c->ctrl;
+  // Claims of the debug launches' logical workgroups, all clear.
+  e = hipMalloc(reinterpret_cast<void**>(&c->claims), sizeof(uint64_t) * wgs_of(c));
+  if (e != hipSuccess) {
+    c->claims = nullptr;
+    release(c);
+    return fail(XFER_ERR_NO_MEMORY, std::string("hipMalloc(claims): ") + hipGetErrorString(e));
+  }
+  e = hipMemset(c->claims, 0, sizeof(uint64_t) * wgs_of(c));
+  if (e != hipSuccess) {
+    release(c);
+    return hip_fail(e, "hipMemset(claims)");
+  }
   // Status words (error, abort) in pinned host memory.
   void* st = nullptr;
   e = hipHostMalloc(&st, sizeof(Status), hipHostMallocMapped | hipHostMallocCoherent);
@@ -726,6 +808,7 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
     rc.recv_fifo = c->fifo_rx;
     rc.ctrl = static_cast<LaneCtrl*>(c->ctrl_mem);
     rc.status = c->status_host;
+    rc.err_mirror = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(c->ctrl_mem) + ctrl_bytes);
     std::string why;
     const int r = relay_start(rc, &c->relay, &why);
     if (r) {
@@ -794,7 +877,8 @@ extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nb
   args.total_wgs = total;
   args.xcd_remap = c->xcd_remap;
   args.timeout_ticks = c->timeout_ticks;
-  hipError_t e = launch_run1(v, args, c->block, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gate().run(c->device, s, [&] { return launch_run1(v, args, c->block, s); });
   if (e != hipSuccess) return hip_fail(e, "xfer_run launch");
   relay_job(c, {uint64_t(nbytes)}, uint64_t(iters));
   commit_steps(c, add);
@@ -868,7 +952,8 @@ extern "C" int xfer_run_messages(xfer_conn* c, const void* src, void* dst, const
     args.timeout_ticks = c->timeout_ticks;
     args.nmsgs = uint32_t(cnt);
     for (size_t i = 0; i < cnt; ++i) args.msgs[i] = msgs[first + i];
-    hipError_t e = launch_runL(v, args, c->block, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = gate().run(c->device, s, [&] { return launch_runL(v, args, c->block, s); });
     if (e != hipSuccess) return hip_fail(e, "xfer_run_messages launch");
   }
   if (c->relay) {
@@ -893,7 +978,7 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
   int live = 0;
   const xfer_conn* first = nullptr;
   for (int i = 0; i < n; ++i) {
-    const xfer_conn* c = conns[i];
+    xfer_conn* c = conns[i];
     int rc = check_runnable(c, "xfer_run_batch");
     if (rc) return rc;
     for (int j = 0; j < i; ++j)
@@ -945,7 +1030,9 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
   args.total_wgs = grid;
   args.xcd_remap = first->xcd_remap;
   args.timeout_ticks = first->timeout_ticks;
-  hipError_t e = launch_runB(v, args, first->block, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e =
+      gate().run(first->device, s, [&] { return launch_runB(v, args, first->block, s); });
   if (e != hipSuccess) return hip_fail(e, "xfer_run_batch launch");
   for (int i = 0; i < n; ++i) {
     if (!nbytes[i]) continue;
@@ -997,7 +1084,8 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
   args.total_wgs = total;
   args.xcd_remap = fwd->xcd_remap;
   args.timeout_ticks = std::max(fwd->timeout_ticks, rev->timeout_ticks);
-  hipError_t e = launch_ping(v, args, fwd->block, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gate().run(fwd->device, s, [&] { return launch_ping(v, args, fwd->block, s); });
   if (e != hipSuccess) return hip_fail(e, "xfer_run_pingpong launch");
   commit_steps(fwd, addf);
   commit_steps(rev, addr);

@@ -50,6 +50,14 @@ __device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) {
 }
 
 template <int SC>
+__device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
+  if constexpr (SC == kScopeSystem)
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  else
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int SC>
 __device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) {
   if constexpr (SC == kScopeSystem)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -120,8 +128,12 @@ __device__ __forceinline__ uint64_t wave_load(const uint64_t* p) {
   return uniform_u64(ld_u64<SC>(p));
 }
 
-__device__ __forceinline__ void raise_err(Status* st, uint32_t code) {
-  __hip_atomic_store(&st->err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+// A failure of the connection: the host's status word (pinned host memory)
+// and its mirror beside the counters, which every later launch on the
+// connection reads on entry.
+__device__ __forceinline__ void raise_err(const ConnArgs& A, uint32_t code) {
+  __hip_atomic_store(&A.status->err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(A.err_dev, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // Bound of one wait: wall-clock ticks (s_memrealtime) plus the host abort
@@ -325,6 +337,7 @@ struct Side {
   uint32_t jit;     // jitter seed of this (channel, lane, side), 0 = none
   uint64_t base;    // step counter at launch start (own counter: tail or head)
   uint64_t seen;    // last observed peer counter (wave-uniform)
+  bool dead;        // the connection carries a failure from an earlier launch
   Range r;          // the channel's range and steps in the current message
 };
 
@@ -345,8 +358,22 @@ __device__ __forceinline__ Side make_side(const ConnArgs& A, uint32_t c, uint32_
   s.r = Range{0, 0, 0};  // set per message
   // A side is the only writer of its own counter, and the previous launch
   // that wrote it has completed, so a plain coherent load reads it.
+  // The connection's failure mirror is read in the same round trip: a
+  // launch queued behind a failed one starts on whatever that one left (a
+  // half-advanced counter, an address still in ptrExchange), so it does
+  // nothing at all.
   const uint64_t* own = producer ? &s.rx->tail : &s.tx->head;
-  s.base = sc == kScopeSystem ? wave_load<kScopeSystem>(own) : wave_load<kScopeAgent>(own);
+  uint64_t v;
+  uint32_t e;
+  if (sc == kScopeSystem) {
+    v = ld_u64<kScopeSystem>(own);
+    e = ld_u32<kScopeSystem>(A.err_dev);
+  } else {
+    v = ld_u64<kScopeAgent>(own);
+    e = ld_u32<kScopeAgent>(A.err_dev);
+  }
+  s.base = uniform_u64(v);
+  s.dead = __builtin_amdgcn_readfirstlane(e) != 0;
   s.seen = 0;
   return s;
 }
@@ -400,11 +427,11 @@ struct Shared {
   uint64_t ptr[2];  // zero-copy destinations, indexed by step parity
 };
 
-__device__ __forceinline__ bool wg_failed(Shared& sh, uint32_t local_err, Status* st) {
+__device__ __forceinline__ bool wg_failed(Shared& sh, uint32_t local_err, const ConnArgs& A) {
   if (local_err) sh.err = local_err;
   __syncthreads();
   const uint32_t e = sh.err;
-  if (e && threadIdx.x == 0) raise_err(st, e);
+  if (e && threadIdx.x == 0) raise_err(A, e);
   return e != 0;
 }
 
@@ -506,6 +533,7 @@ __device__ bool simple_send_piped(const ConnArgs& A, uint32_t c, uint32_t w, Sid
       uint8_t* slot = slot_of(A, c, g);
       batch_store<O::kShared, false>(b, slot, L, S, P, w);
       lane_tail<kPolNT, O::kShared, false>(src + sd.r.beg + j * S, slot, L, S, P, w);
+      compiler_fence();  // the next loads issue after these stores: vmcnt counts on that
       if (j + 1 < sd.r.k) {
         batch_load<kPolNT, false>(b, src + sd.r.beg + (j + 1) * S, chunk_len(sd, S, j + 1), S, P, w);
         wait_vmcnt<kUnroll>();
@@ -514,7 +542,7 @@ __device__ bool simple_send_piped(const ConnArgs& A, uint32_t c, uint32_t w, Sid
       }
     }
     jitter(sd, g, 1);
-    if (wg_failed(sh, err, A.status)) return false;
+    if (wg_failed(sh, err, A)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 1, g + 1);
       st_u64<SC>(&sd.rx->tail, g + 1);
@@ -545,7 +573,7 @@ __device__ bool simple_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
       O::release();
     }
     jitter(sd, g, 1);
-    if (wg_failed(sh, err, A.status)) return false;
+    if (wg_failed(sh, err, A)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 1, g + 1);
       st_u64<SC>(&sd.rx->tail, g + 1);
@@ -589,7 +617,7 @@ __device__ bool simple_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
       if constexpr (ORD == kOrdFenced) O::release();
     }
     jitter(sd, g, 1);
-    if (wg_failed(sh, err, A.status)) return false;
+    if (wg_failed(sh, err, A)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 1, g + 1);
       st_u64<SC>(&sd.tx->head, g + 1);
@@ -651,7 +679,7 @@ __device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
       if (i < nl) st_u64<SC>(&lines[i], flag | ll_src_word<AL>(s, L, i));
     }
   }
-  return !wg_failed(sh, err, A.status);
+  return !wg_failed(sh, err, A);
 }
 
 template <int SC, int ORD, bool AL>
@@ -720,7 +748,7 @@ __device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
     // ordering keeps its release fence.
     if constexpr (ORD == kOrdFenced) O::release();
     jitter(sd, g, 1);
-    if (wg_failed(sh, err, A.status)) return false;
+    if (wg_failed(sh, err, A)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 0, static_cast<uint64_t>(want));  // every line of the step seen
       trace_step(A, sd, g, 1, g + 1);
@@ -784,7 +812,7 @@ __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t 
   const uint32_t P = A.lanes;
   Batch b;
   batch_load<kPolNT, true>(b, src + sd.r.beg, chunk_len(sd, S, 0), S, P, w);
-  if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh.ptr[0]), A.status)) return false;
+  if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh.ptr[0]), A)) return false;
   if (threadIdx.x == 0) trace_step(A, sd, g0, 0, sh.ptr[0]);
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
@@ -793,6 +821,7 @@ __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t 
     jitter(sd, g, 0);
     batch_store<O::kShared, true>(b, p, L, S, P, w);
     lane_tail<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, p, L, S, P, w);
+    compiler_fence();  // the next loads issue after these stores: vmcnt counts on that
     uint32_t err = 0;
     if (j + 1 < sd.r.k) {
       uint64_t first = 0;
@@ -805,7 +834,7 @@ __device__ bool zc_send_piped(const ConnArgs& A, uint32_t w, Side& sd, uint64_t 
       wait_vmcnt<0>();
     }
     jitter(sd, g, 1);
-    if (wg_failed(sh, err, A.status)) return false;
+    if (wg_failed(sh, err, A)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 1, g + 1);
       st_u64<SC>(&sd.rx->tail, g + 1);
@@ -827,14 +856,14 @@ __device__ bool zc_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
   }
   for (uint64_t j = 0; j < sd.r.k; ++j) {
     const uint64_t g = g0 + j;
-    if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh.ptr[0]), A.status)) return false;
+    if (wg_failed(sh, take_address<SC, ORD>(A, sd, ticks, sh.ptr[0]), A)) return false;
     if (threadIdx.x == 0) trace_step(A, sd, g, 0, sh.ptr[0]);
     jitter(sd, g, 0);
     lane_copy<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, reinterpret_cast<uint8_t*>(sh.ptr[0]),
                                   chunk_len(sd, S, j), S, A.lanes, w);
     O::release();
     jitter(sd, g, 1);
-    if (wg_failed(sh, 0, A.status)) return false;
+    if (wg_failed(sh, 0, A)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 1, g + 1);
       st_u64<SC>(&sd.rx->tail, g + 1);
@@ -865,6 +894,7 @@ __device__ bool zcd_send(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
       jitter(sd, g, 0);
       batch_store<O::kShared, true>(b, p, L, S, P, w);
       lane_tail<kPolNT, O::kShared, true>(src + sd.r.beg + j * S, p, L, S, P, w);
+      compiler_fence();  // the next loads issue after these stores: vmcnt counts on that
       if (j + 1 < sd.r.k) {
         batch_load<kPolNT, true>(b, src + sd.r.beg + (j + 1) * S, chunk_len(sd, S, j + 1), S, P, w);
         wait_vmcnt<kUnroll>();
@@ -872,7 +902,7 @@ __device__ bool zcd_send(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
         wait_vmcnt<0>();
       }
       jitter(sd, g, 1);
-      if (wg_failed(sh, 0, A.status)) return false;
+      if (wg_failed(sh, 0, A)) return false;
       if (threadIdx.x == 0) {
         trace_step(A, sd, g, 1, g + 1);
         st_u64<SC>(&sd.rx->tail, g + 1);
@@ -888,7 +918,7 @@ __device__ bool zcd_send(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
                                         chunk_len(sd, S, j), S, P, w);
     O::release();
     jitter(sd, g, 1);
-    if (wg_failed(sh, 0, A.status)) return false;
+    if (wg_failed(sh, 0, A)) return false;
     if (threadIdx.x == 0) {
       trace_step(A, sd, g, 1, g + 1);
       st_u64<SC>(&sd.rx->tail, g + 1);
@@ -921,7 +951,7 @@ __device__ bool zcd_recv(const ConnArgs& A, Side& sd, uint64_t g0, uint64_t tick
     }
     const uint32_t e = dl.expired();
     if (e) {
-      raise_err(A.status, e);
+      raise_err(A, e);
       return false;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -988,9 +1018,10 @@ __device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<M
   uint64_t ndone = 0, npub = 0;
   Deadline dl(ticks, A.status);
   // The word is clear when a launch starts: each earlier launch on the
-  // connection ended with every published address taken, and a failed one
-  // leaves the connection refusing runs.  So the first address goes out
-  // without a poll, one round trip earlier.
+  // connection ended with every published address taken, and after a failed
+  // one every later launch returns on entry (its failure mirror is set) and
+  // the host refuses new runs.  So the first address goes out without a
+  // poll, one round trip earlier.
   bool clear = true;
   while (ndone < total) {
     bool moved = false;
@@ -1018,7 +1049,7 @@ __device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<M
     } else {
       const uint32_t e = dl.expired();
       if (e) {
-        raise_err(A.status, e);
+        raise_err(A, e);
         return;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -1062,6 +1093,31 @@ __device__ __forceinline__ uint32_t logical_wg(uint32_t remap, uint32_t total) {
   return 2u * ((b % 8u) * half + s % half) + s / half;
 }
 
+// Debug variant: the block takes logical workgroup `local` of connection A
+// for this launch.  Were the remap ever to hand one logical workgroup to two
+// blocks, another would go unserved and the pair's slot hand-backs would no
+// longer cover each other's bytes; the second claimer raises
+// XFER_ERR_INTERNAL and leaves.  Returns whether the block may go on.  Every
+// thread of the block must call it.
+template <bool DBG>
+__device__ __forceinline__ bool claim_wg(const ConnArgs& A, uint32_t local, Shared& sh) {
+  if constexpr (!DBG) {
+    return true;
+  } else {
+    if (A.claims == nullptr) return true;
+    if (threadIdx.x == 0) {
+      const uint64_t prev = __hip_atomic_exchange(&A.claims[local], A.launch_seq, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == A.launch_seq) {
+        sh.err = XFER_ERR_INTERNAL;
+        raise_err(A, XFER_ERR_INTERNAL);
+      }
+    }
+    __syncthreads();
+    return sh.err == 0;
+  }
+}
+
 // Records the XCD id of each block (the host's check of the deal).
 __global__ void xcc_probe_kernel(uint32_t* out) {
   if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();
@@ -1086,8 +1142,10 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB, NMSG> args) {
   const uint32_t pair = local >> 1, role = local & 1u;
   const uint32_t c = pair / A.lanes, w = pair % A.lanes;
   if (c >= A.nch) return;  // padding of a paired launch (its grid is a multiple of 16)
+  if (!claim_wg<DBG>(A, local, sh)) return;
   if (!((A.roles >> role) & 1u)) return;  // side switched off for fault injection
   Side sd = make_side<DBG>(A, c, w, role == 0, SC);
+  if (sd.dead) return;
   const uint64_t ticks = args.timeout_ticks;
   if constexpr (PROTO == kProtoZC) {
     if (role == 1) {
@@ -1137,8 +1195,10 @@ __global__ void __launch_bounds__(1024) ping_kernel(PingArgs args) {
   const ConnArgs& R = args.rev;
   const uint32_t c = pair / F.lanes, w = pair % F.lanes;
   if (c >= F.nch) return;
+  if (!claim_wg<DBG>(F, lw, sh)) return;
   Side fs = make_side<DBG>(F, c, w, side == 0, SC);
   Side rs = make_side<DBG>(R, c, w, side == 1, SC);
+  if (fs.dead || rs.dead) return;
   fs.r = chan_range(F.nbytes, F.nch, c, F.step_bytes);
   rs.r = chan_range(R.nbytes, R.nch, c, R.step_bytes);
   const uint64_t k = fs.r.k;

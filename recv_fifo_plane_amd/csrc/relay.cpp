@@ -172,6 +172,9 @@ class Proxy {
     uint32_t zero = 0;
     __atomic_compare_exchange_n(&cfg_.status->err, &zero, uint32_t(XFER_ERR_HIP), false,
                                 __ATOMIC_ACQ_REL, __ATOMIC_ACQUIRE);
+    zero = 0;
+    __atomic_compare_exchange_n(cfg_.err_mirror, &zero, uint32_t(XFER_ERR_HIP), false,
+                                __ATOMIC_ACQ_REL, __ATOMIC_ACQUIRE);
     __atomic_store_n(&cfg_.status->abort_flag, 1u, __ATOMIC_RELEASE);
   }
 

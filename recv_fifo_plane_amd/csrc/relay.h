@@ -26,6 +26,7 @@ struct RelayConfig {
   uint8_t* recv_fifo = nullptr;  // HBM: the consumer's FIFO
   LaneCtrl* ctrl = nullptr;      // host view of the control blocks, [nch * lanes]
   Status* status = nullptr;      // host view of the connection's status words
+  uint32_t* err_mirror = nullptr;  // host view of the failure mirror the kernels read on entry
 };
 
 // The work one run hands the proxies: its messages (byte counts, in launch

@@ -37,8 +37,9 @@ struct alignas(128) LaneCtrl {
 };
 static_assert(sizeof(LaneCtrl) == 640, "control block layout");
 
-// Per-connection status words in pinned host memory: the first in-kernel
-// failure (written once by compare-and-swap) and the host's abort request.
+// Per-connection status words in pinned host memory: the code of an
+// in-kernel failure (0 = none; a later failure may overwrite an earlier
+// code, never with 0) and the host's abort request.
 struct alignas(128) Status {
   uint32_t err;
   uint32_t pad0[31];
@@ -79,6 +80,10 @@ struct ConnArgs {
   TraceRec* trace;     // step trace, or nullptr: [nch * lanes * 2] rings of trace_per records
   uint32_t trace_per;  // records per (channel, lane, side) ring
   uint32_t jitter;     // debug variant: seed of random delays in the step loops, 0 = none
+  uint32_t* err_dev;   // mirror of status->err beside the counters (same memory and scope),
+                       // read by every workgroup on entry
+  uint64_t* claims;    // debug variant: per logical workgroup, the last launch that claimed it
+  uint64_t launch_seq; // debug variant: this launch's number on the connection (from 1)
 };
 
 // One message of a launch: bytes [off, off + len) of the connection's src

@@ -82,10 +82,6 @@ def make_conn(cfg: dict, **override) -> X.Conn:
                   **attrs)
 
 
-def _addr(t) -> int:
-    return t if isinstance(t, int) else int(t.data_ptr())
-
-
 class Ring:
     """Logical endpoints on one GPU connected by the host schedule's ring
     plan; one edge per (r, (r + 1) mod n), each with its own channels."""
@@ -107,8 +103,11 @@ class Ring:
         """Endpoint r's slice of a goes to endpoint (r+1) mod n's slice of b."""
         keys = sorted(self.edges)
         conns = [self.edges[k] for k in keys]
-        src = [_addr(a) + s * self.slice for s, _ in keys]
-        dst = [_addr(b) + d * self.slice for _, d in keys]
+        dev = conns[0].device if conns else None
+        pa = X._buf(a, self.n * self.slice, dev, "Ring.run: a")
+        pb = X._buf(b, self.n * self.slice, dev, "Ring.run: b")
+        src = [pa + s * self.slice for s, _ in keys]
+        dst = [pb + d * self.slice for _, d in keys]
         X.run_batch(conns, src, dst, [self.slice] * len(keys), stream)
 
     def close(self) -> None:
@@ -135,7 +134,9 @@ def message_offsets(sizes) -> list[int]:
 def run_messages(conn: X.Conn, a, b, sizes, stream=None) -> None:
     """One transfer (one launch) per message, at consecutive offsets of a and b."""
     off = 0
-    pa, pb = _addr(a), _addr(b)
+    total = sum(int(s) for s in sizes)
+    pa = X._buf(a, total, conn.device, "run_messages: a")
+    pb = X._buf(b, total, conn.device, "run_messages: b")
     for s in sizes:
         conn.run(pa + off, pb + off, s, stream)
         off += s

@@ -184,6 +184,43 @@ def _addr(buf) -> int:
     return int(buf.data_ptr())
 
 
+def _current_device() -> int | None:
+    try:
+        import torch
+        return torch.cuda.current_device() if torch.cuda.is_available() else None
+    except Exception:
+        return None
+
+
+def _buf(buf, nbytes: int, device: int | None, what: str) -> int:
+    """Address of a buffer the kernels will access over [0, nbytes).
+
+    An integer is taken as a raw device address: its extent is the caller's
+    responsibility.  A tensor must live on the GPU, on the connection's
+    device, be contiguous and hold at least nbytes bytes; otherwise
+    ValueError is raised before the library is called (a kernel given a
+    host address, another device's memory or too short a buffer would
+    access memory outside it)."""
+    if buf is None or isinstance(buf, int):
+        return _addr(buf)
+    if not hasattr(buf, "data_ptr"):
+        raise TypeError("%s: expected a torch tensor or an integer address, got %s"
+                        % (what, type(buf).__name__))
+    if nbytes <= 0:
+        return int(buf.data_ptr())
+    if not getattr(buf, "is_cuda", False):
+        raise ValueError("%s: tensor is not in GPU memory (device %s)" % (what, buf.device))
+    if device is not None and buf.device.index != device:
+        raise ValueError("%s: tensor is on cuda:%s, the connection on cuda:%d"
+                         % (what, buf.device.index, device))
+    if not buf.is_contiguous():
+        raise ValueError("%s: tensor is not contiguous" % what)
+    have = buf.numel() * buf.element_size()
+    if have < nbytes:
+        raise ValueError("%s: tensor holds %d bytes, the transfer touches %d" % (what, have, nbytes))
+    return int(buf.data_ptr())
+
+
 class Conn:
     """One connection (xfer_conn).  Destroy it only after its streams are idle."""
 
@@ -197,6 +234,7 @@ class Conn:
         self.slot_bytes = int(slot_bytes)
         self.fifo_loc = FIFO_LOCS[fifo_loc] if isinstance(fifo_loc, str) else int(fifo_loc)
         self._h = None
+        self.device = _current_device()  # where the library allocated it (the current device)
         if _handle is not None:
             self._h = _handle
             return
@@ -225,18 +263,31 @@ class Conn:
             pass
 
     def run(self, src, dst, nbytes: int, stream=None) -> None:
-        check(lib().xfer_run(self._h, _addr(src), _addr(dst), int(nbytes), _stream_handle(stream)))
+        n = int(nbytes)
+        s = _buf(src, n, self.device, "run: src")
+        d = _buf(dst, n, self.device, "run: dst")
+        check(lib().xfer_run(self._h, s, d, n, _stream_handle(stream)))
 
     def run_loop(self, src, dst, nbytes: int, iters: int, stream=None) -> None:
-        check(lib().xfer_run_loop(self._h, _addr(src), _addr(dst), int(nbytes), int(iters),
-                                  _stream_handle(stream)))
+        n = int(nbytes)
+        s = _buf(src, n, self.device, "run_loop: src")
+        d = _buf(dst, n, self.device, "run_loop: dst")
+        check(lib().xfer_run_loop(self._h, s, d, n, int(iters), _stream_handle(stream)))
 
     def run_messages(self, src, dst, offsets, sizes, stream=None) -> None:
         n = len(sizes)
-        offs = (C.c_size_t * max(n, 1))(*[int(x) for x in offsets])
-        szs = (C.c_size_t * max(n, 1))(*[int(x) for x in sizes])
-        check(lib().xfer_run_messages(self._h, _addr(src), _addr(dst), offs, szs, n,
-                                      _stream_handle(stream)))
+        if len(offsets) != n:
+            raise ValueError("run_messages: %d offsets for %d sizes" % (len(offsets), n))
+        offs_l = [int(x) for x in offsets]
+        szs_l = [int(x) for x in sizes]
+        if any(x < 0 for x in offs_l + szs_l):
+            raise ValueError("run_messages: negative offset or size")
+        extent = max([o + z for o, z in zip(offs_l, szs_l) if z] or [0])
+        s = _buf(src, extent, self.device, "run_messages: src")
+        d = _buf(dst, extent, self.device, "run_messages: dst")
+        offs = (C.c_size_t * max(n, 1))(*offs_l)
+        szs = (C.c_size_t * max(n, 1))(*szs_l)
+        check(lib().xfer_run_messages(self._h, s, d, offs, szs, n, _stream_handle(stream)))
 
     def query(self, channel: int) -> dict:
         st = xfer_chan_state()
@@ -281,7 +332,8 @@ class Conn:
             return
         if not isinstance(records, int):
             nrecords = records.numel() * records.element_size() // TRACE_REC_BYTES
-        check(lib().xfer_conn_set_trace(self._h, _addr(records), int(nrecords)))
+        addr = _buf(records, int(nrecords) * TRACE_REC_BYTES, self.device, "set_trace: records")
+        check(lib().xfer_conn_set_trace(self._h, addr, int(nrecords)))
 
     def launch_shape(self) -> tuple[int, int]:
         g, b = C.c_int(), C.c_int()
@@ -305,16 +357,24 @@ def trace_records(raw):
 
 def run_batch(conns, srcs, dsts, nbytes, stream=None) -> None:
     n = len(conns)
+    if not (len(srcs) == len(dsts) == len(nbytes) == n):
+        raise ValueError("run_batch: conns, srcs, dsts and nbytes differ in length")
     hs = (_vp * n)(*[c.handle for c in conns])
-    ss = (_vp * n)(*[_addr(s) for s in srcs])
-    ds = (_vp * n)(*[_addr(d) for d in dsts])
+    ss = (_vp * n)(*[_buf(s, int(k), c.device, "run_batch: src[%d]" % i)
+                     for i, (c, s, k) in enumerate(zip(conns, srcs, nbytes))])
+    ds = (_vp * n)(*[_buf(d, int(k), c.device, "run_batch: dst[%d]" % i)
+                     for i, (c, d, k) in enumerate(zip(conns, dsts, nbytes))])
     ns = (C.c_size_t * n)(*[int(x) for x in nbytes])
     check(lib().xfer_run_batch(hs, ss, ds, ns, n, _stream_handle(stream)))
 
 
 def run_pingpong(fwd: Conn, rev: Conn, a, b, c, nbytes: int, iters: int, stream=None) -> None:
-    check(lib().xfer_run_pingpong(fwd.handle, rev.handle, _addr(a), _addr(b), _addr(c),
-                                  int(nbytes), int(iters), _stream_handle(stream)))
+    n = int(nbytes)
+    pa = _buf(a, n, fwd.device, "run_pingpong: a")
+    pb = _buf(b, n, fwd.device, "run_pingpong: b")
+    pc = _buf(c, n, fwd.device, "run_pingpong: c")
+    check(lib().xfer_run_pingpong(fwd.handle, rev.handle, pa, pb, pc, n, int(iters),
+                                  _stream_handle(stream)))
 
 
 # ---------------------------------------------------------------- schedule

@@ -179,3 +179,19 @@ def test_set_trace_rejects_a_null_connection():
 def test_set_jitter_rejects_a_null_connection():
     from recv_fifo_plane_amd import xfer as X
     assert X.lib().xfer_conn_set_jitter(None, 1) == X.XFER_ERR_INVALID_ARG
+
+
+def test_library_loads_where_torch_brought_the_hip_runtime():
+    # torch ships its own HIP runtime under the same soname; imported first,
+    # it is the runtime libxfer.so binds to, so the library must not need a
+    # symbol (or symbol version) newer than that runtime has
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import torch\n"
+            "import recv_fifo_plane_amd as xf\n"
+            "xf.lib()\n"
+            "print('loaded')\n" % root)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "loaded" in r.stdout, r.stderr[-2000:]

@@ -133,3 +133,40 @@ def test_batch_rejects_transfers_that_overlap_each_other():
     assert torch.equal(a[:3 * n], b[:3 * n])
     c0.close()
     c1.close()
+
+
+@pytest.mark.parametrize("proto,roles", [("zc", 2), ("simple", 1), ("ll", 1), ("zcd", 2)])
+def test_run_queued_behind_a_failed_one_changes_nothing(proto, roles):
+    # The second run is queued before the first has failed, so the host
+    # accepts it; on the device it must find the failure on entry and leave
+    # every word where the failed run left it (a lone zero-copy receiver
+    # leaves its first address in ptrExchange: a producer of a later run
+    # must never take it).  `ref` shows where the failed run alone leaves
+    # the words.
+    import torch
+    log("case: run queued behind a failure %s roles=%d" % (proto, roles))
+    n = 1 << 16
+    ref = xf.Conn(proto, 2, 2, 4096, timeout_ms=200, roles=roles)
+    c = xf.Conn(proto, 2, 2, 4096, timeout_ms=200, roles=roles)
+    a1, b1 = _bufs(n)
+    a2, b2 = _bufs(n)
+    a1.random_(0, 255)
+    a2.random_(0, 255)
+    ref.run(a1, b1, n)
+    torch.cuda.synchronize()
+    b1.zero_()
+    c.run(a1, b1, n)
+    c.run(a2, b2, n)
+    torch.cuda.synchronize()
+    for ch in range(2):
+        qr, qc = ref.query(ch), c.query(ch)
+        assert qr["error"] == X.XFER_ERR_TIMEOUT and qc["error"] == X.XFER_ERR_TIMEOUT, (qr, qc)
+        for k in ("head", "tail", "ptr_exchange", "lanes_agree"):
+            assert qc[k] == qr[k], (proto, ch, k, qr, qc)
+        if proto in ("simple", "ll"):
+            assert (c.read_fifo(ch) == ref.read_fifo(ch)).all(), (proto, ch)
+    if proto == "zc":
+        assert c.query(0)["ptr_exchange"] == b1.data_ptr()  # the failed run's first address
+    assert not b2.any()
+    ref.close()
+    c.close()
