@@ -39,10 +39,11 @@
  *     the device's previous launch first waits on the host until the device
  *     has finished its work (hipDeviceSynchronize), so switching streams
  *     costs a host-side wait and is not allowed under stream capture (keep
- *     captured runs on one stream).  Kernels of
+ *     captured runs on one stream, or use xfer_run_noalloc).  Kernels of
  *     other code running beside a launch only delay the dispatch of its
  *     workgroups; a kernel that waits on one of this library's launches must
- *     not hold the GPU's resources meanwhile.
+ *     not hold the GPU's resources meanwhile.  xfer_run_noalloc does not
+ *     take part in this order (see there).
  *   - Step counters are 64-bit, start at 0 when the connection is created,
  *     and persist across runs; step g (0-based) publishes tail = g+1.
  *   - Runs on one connection must be serialised (same stream, or synchronised
@@ -272,6 +273,42 @@ int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nbytes, int i
  * ping-pong latency test ("RDMA and GPUDirect", section 十.3). */
 int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, void* b, void* cbuf,
                       size_t nbytes, int iters, void* stream);
+
+/* xfer_run_noalloc: for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  One transfer of nbytes from src to dst, like xfer_run on a
+ * new connection created with (proto, nchannels, nslots, slot_bytes, attr,
+ * FIFO in HBM): the same kernels, the same destination bytes.  Its FIFO,
+ * control blocks and status words live in a fixed array of
+ * XFER_NOALLOC_SCRATCH_BYTES in each GPU's memory, owned by the library and
+ * held until the process ends; no connection is made and nothing is
+ * allocated (the first call on a device takes the array's address there and
+ * queries the device's clock rate and, per kernel variant, its resident
+ * capacity).
+ *   The array's FIFO room is XFER_NOALLOC_SCRATCH_BYTES less 1 MiB:
+ *   nchannels x nslots x slot_bytes beyond it is INVALID_ARG (zero-copy uses
+ *   no FIFO).  attr: NULL or wgs_per_channel, block_threads, timeout_ms,
+ *   xcd_pairing (-1: dispatch order; 0 or 1: pairs on one XCD by block id)
+ *   and ordering; ctrl_loc must be DEFAULT or DEVICE, roles and p2p_read 0,
+ *   place_trials 0 or 1 (otherwise INVALID_ARG).
+ *   src, dst, nbytes as for xfer_run.  stream as everywhere.
+ *   status: NULL, or a word the device can write (device memory, or mapped
+ *   pinned host memory); when a transfer is queued, the in-kernel failure
+ *   code (0 = none, else XFER_ERR_TIMEOUT or XFER_ERR_ABORTED ...) is
+ *   written there after it, in stream order.
+ * Every call queues a small clearing kernel, the transfer, and (with
+ * status) a one-thread report kernel on `stream`.  Every call on a GPU uses
+ * that GPU's one array, which keeps the last call's contents until the next
+ * call clears it: calls that overlap in time on one GPU race and must be
+ * ordered by the caller (one stream, or events).  These calls do not take
+ * part in the ordering of the library's other launches (below, "Launch
+ * order"): the caller must not run them alongside another launch of this
+ * library whose grid together with this one exceeds what the GPU holds
+ * resident.  Errors: INVALID_ARG, RANGE, HIP; nothing is queued then. */
+#define XFER_NOALLOC_SCRATCH_BYTES (16u << 20)
+int xfer_run_noalloc(int proto, int nchannels, int nslots, size_t slot_bytes,
+                     const xfer_attr* attr, const void* src, void* dst, size_t nbytes,
+                     uint32_t* status, void* stream);
 
 /* --------------------------------------------------------------- inspect */
 /* Synchronous read of one channel's control words (lane 0 reported; the

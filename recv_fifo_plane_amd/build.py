@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libxfer.so")
 SOURCES = [os.path.join(CSRC, f)
-           for f in ("kernels.hip", "conn.cpp", "relay.cpp", "sched.cpp")]
+           for f in ("kernels.hip", "noalloc.hip", "conn.cpp", "relay.cpp", "sched.cpp")]
 HEADERS = [os.path.join(CSRC, "xfer_internal.h"), os.path.join(CSRC, "relay.h"),
            os.path.join(ROOT, "include", "xfer.h")]
 ARCH = os.environ.get("XFER_OFFLOAD_ARCH", "gfx950")

@@ -102,6 +102,8 @@ SIGNATURES = {
     "xfer_run_messages": (C.c_int, [_vp, _vp, _vp, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t),
                                     C.c_int, _vp]),
     "xfer_run_pingpong": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_size_t, C.c_int, _vp]),
+    "xfer_run_noalloc": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_size_t, C.POINTER(xfer_attr),
+                                   _vp, _vp, C.c_size_t, _vp, _vp]),
     "xfer_conn_query": (C.c_int, [_vp, C.c_int, C.POINTER(xfer_chan_state)]),
     "xfer_conn_fifo": (C.c_int, [_vp, C.c_int, C.POINTER(_vp), C.POINTER(C.c_size_t)]),
     "xfer_conn_read_fifo": (C.c_int, [_vp, C.c_int, _vp, C.c_size_t]),
@@ -375,6 +377,26 @@ def run_pingpong(fwd: Conn, rev: Conn, a, b, c, nbytes: int, iters: int, stream=
     pc = _buf(c, n, fwd.device, "run_pingpong: c")
     check(lib().xfer_run_pingpong(fwd.handle, rev.handle, pa, pb, pc, n, int(iters),
                                   _stream_handle(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # XFER_NOALLOC_SCRATCH_BYTES
+
+
+def run_noalloc(proto, nchannels: int, nslots: int, slot_bytes: int, src, dst, nbytes: int,
+                status=None, stream=None, **attr) -> None:
+    """xfer_run_noalloc: one transfer through the library's fixed device
+    array (no connection, nothing allocated).  status: None, or a device
+    tensor of at least 4 bytes (or an address) that receives the in-kernel
+    failure code after the transfer."""
+    p = PROTOS[proto] if isinstance(proto, str) else int(proto)
+    a = make_attr(**attr)
+    dev = _current_device()
+    n = int(nbytes)
+    s = _buf(src, n, dev, "run_noalloc: src")
+    d = _buf(dst, n, dev, "run_noalloc: dst")
+    st = _buf(status, 4, dev, "run_noalloc: status") if status is not None else None
+    check(lib().xfer_run_noalloc(p, int(nchannels), int(nslots), int(slot_bytes), C.byref(a), s,
+                                 d, n, st, _stream_handle(stream)))
 
 
 # ---------------------------------------------------------------- schedule

@@ -195,3 +195,26 @@ def test_library_loads_where_torch_brought_the_hip_runtime():
             "print('loaded')\n" % root)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and "loaded" in r.stdout, r.stderr[-2000:]
+
+
+@pytest.mark.parametrize("args,attr", [
+    ((4, 1, 8, 4096), {}),                                  # unknown protocol
+    ((0, 0, 8, 4096), {}),                                  # no channels
+    ((0, 1, 8, 24), {}),                                    # SIMPLE slot not a multiple of 16
+    ((0, 2, 8, (15 << 20) // 8), {}),                       # FIFO twice the array's room
+    ((0, 1, 8, 4096), dict(roles=1)),                       # both sides always run
+    ((0, 1, 8, 4096), dict(p2p_read=1)),
+    ((0, 1, 8, 4096), dict(ctrl_loc=X.XFER_CTRL_HOST)),
+    ((1, 1, 8, 4096), dict(place_trials=2)),
+    ((0, 1, 8, 4096), dict(wgs_per_channel=17)),
+])
+def test_noalloc_rejects_bad_arguments_before_touching_a_gpu(args, attr):
+    a = X.make_attr(**attr)
+    rc = xf.lib().xfer_run_noalloc(*args, C_byref(a), 1 << 20, 1 << 21, 4096, None, None)
+    assert rc == X.XFER_ERR_INVALID_ARG, (args, attr, xf.last_error())
+    assert "xfer_run_noalloc" in xf.last_error()
+
+
+def C_byref(x):
+    import ctypes
+    return ctypes.byref(x)

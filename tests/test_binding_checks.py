@@ -89,6 +89,17 @@ def test_batch_and_pingpong_are_checked(no_library):
                        torch.zeros(64, dtype=torch.uint8), 64, 10)
 
 
+def test_noalloc_tensors_are_checked(monkeypatch):
+    monkeypatch.setattr(X, "_lib", Unreachable())
+    monkeypatch.setattr(X, "_current_device", lambda: 0)
+    with pytest.raises(ValueError, match="not in GPU memory"):
+        X.run_noalloc("simple", 1, 8, 4096, torch.zeros(64, dtype=torch.uint8),
+                      FakeDeviceTensor(64), 64)
+    with pytest.raises(ValueError, match="status"):
+        X.run_noalloc("simple", 1, 8, 4096, FakeDeviceTensor(64), FakeDeviceTensor(64), 64,
+                      status=FakeDeviceTensor(3))
+
+
 def test_integer_addresses_and_empty_transfers_pass_through():
     # raw addresses are the caller's to get right; a zero-byte transfer
     # touches nothing, so any buffer passes
