@@ -128,10 +128,12 @@ typedef struct {
   int ctrl_loc;         /* xfer_ctrl_loc */
   uint32_t timeout_ms;  /* bound on every in-kernel wait; default 10000 */
   int xcd_pairing;      /* 0 (default) or 1: place each producer/consumer pair on one XCD,
-                           an XCD's producers dispatched before its consumers (zero-copy
-                           through ptrExchange: its receivers first, since each producer
-                           waits for its receiver's first address) (the grid is
+                           an XCD's producers dispatched before its consumers (the grid is
                            padded to a multiple of 16 workgroups; padding exits at once).
+                           Zero-copy launches have no pairs and ignore this: each thread
+                           of a few receiver workgroups, dispatched first, is the
+                           receiver of one lane, and one producer workgroup per lane
+                           follows.
                            Each hardware queue starts dealing blocks to the XCDs at an XCD
                            of its own; where a one-time check at the first creation on a
                            device sees a strict rotation over 8 XCDs on every stream,

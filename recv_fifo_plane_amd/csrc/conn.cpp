@@ -225,12 +225,17 @@ void commit_steps(xfer_conn* c, const std::vector<uint64_t>& add) {
 
 // Device view of one launch of c; numbers the launch (debug launches check
 // with it that no two blocks take one logical workgroup).
-ConnArgs conn_args(xfer_conn* c, const void* src, void* dst, uint64_t nbytes, uint32_t wg_begin) {
+ConnArgs conn_args(xfer_conn* c, const void* src, void* dst, uint64_t nbytes, uint32_t wg_begin,
+                   uint32_t rx_begin = 0) {
   ConnArgs a;
   memset(&a, 0, sizeof(a));
+  a.rx_begin = rx_begin;
   a.err_dev = c->err_dev;
   a.claims = c->claims;
   a.launch_seq = ++c->launch_seq;
+  if (c->proto == XFER_PROTO_LL)
+    ll_layout(c->step_bytes, uint32_t(c->lanes), uint32_t(c->block), uint32_t(c->nslots),
+              &a.ll_stripe_log2, &a.ll_group);
   a.fifo = c->fifo;
   a.fifo_rx = c->fifo_rx ? c->fifo_rx : c->fifo;
   a.relay = c->fifo_rx ? 1u : 0u;
@@ -258,13 +263,47 @@ bool zero_copy(int proto) {
   return proto == XFER_PROTO_ZEROCOPY || proto == XFER_PROTO_ZEROCOPY_DIRECT;
 }
 
-uint32_t wgs_of(const xfer_conn* c) { return uint32_t(c->nch) * uint32_t(c->lanes) * 2u; }
+uint32_t wgs_of(const xfer_conn* c) {
+  return conn_wgs(c->proto, uint32_t(c->nch), uint32_t(c->lanes), uint32_t(c->block));
+}
+
+// Zero-copy: the connection's receiver workgroups (each thread one lane).
+uint32_t rx_wgs_of(const xfer_conn* c) {
+  return zero_copy(c->proto) ? zc_receiver_wgs(uint32_t(c->nch), uint32_t(c->lanes),
+                                               uint32_t(c->block))
+                             : 0u;
+}
+
+uint32_t round8(uint32_t x) { return (x + 7u) & ~7u; }
+
+// Zero-copy grid of rx receiver and p producer workgroups: with grouping
+// by XCD each region is padded to a multiple of 8 blocks (the padding exits
+// at once); *rx_region receives the receiver region's size.
+uint32_t zc_grid(const xfer_conn* c, uint32_t rx, uint32_t p, uint32_t* rx_region) {
+  *rx_region = c->xcd_pairing ? round8(rx) : rx;
+  return *rx_region + (c->xcd_pairing ? round8(p) : p);
+}
 
 // Launched grid.  Pairing keeps a pair (producer 2q, consumer 2q+1) on one
 // XCD, producers first in each XCD's dispatch order (the kernel's
 // logical_wg); its remap needs a grid of a multiple of 16, so the grid is
-// padded with workgroups that exit at once.
-uint32_t grid_of(int pairing, uint32_t total) { return pairing ? (total + 15u) & ~15u : total; }
+// padded with workgroups that exit at once.  Zero-copy launches have no
+// pairs: their receiver workgroups come first, then the producers (zc_grid).
+uint32_t grid_of(const xfer_conn* c, uint32_t total) {
+  if (zero_copy(c->proto)) {
+    uint32_t rx = 0;
+    return zc_grid(c, rx_wgs_of(c), total - rx_wgs_of(c), &rx);
+  }
+  return c->xcd_pairing ? (total + 15u) & ~15u : total;
+}
+
+// The receiver region of a single connection's zero-copy launch (0 otherwise).
+uint32_t rx_region_of(const xfer_conn* c) {
+  if (!zero_copy(c->proto)) return 0;
+  uint32_t rx = 0;
+  (void)zc_grid(c, rx_wgs_of(c), wgs_of(c) - rx_wgs_of(c), &rx);
+  return rx;
+}
 
 // Whether blocks may take their place from their XCD id on this device
 // (xcc_rotation_ok), checked once per device.
@@ -847,8 +886,18 @@ extern "C" int xfer_conn_destroy(xfer_conn* c) {
 // Runs of a traced or jittered connection take the debug kernel variant.
 static bool debug_of(const xfer_conn* c) { return c->trace != nullptr || c->jitter != 0; }
 
+// The kernel protocol of c: LL connections in the striped line layout run
+// kernels of their own.
+static int kernel_proto(const xfer_conn* c) {
+  if (c->proto != XFER_PROTO_LL) return c->proto;
+  uint32_t l2 = 0, group = 0;
+  ll_layout(c->step_bytes, uint32_t(c->lanes), uint32_t(c->block), uint32_t(c->nslots), &l2,
+            &group);
+  return l2 ? int(kProtoLLStriped) : int(kProtoLL);
+}
+
 Variant variant_of(const xfer_conn* c, bool aligned) {
-  return Variant{c->proto, c->scope, c->ordering, aligned ? 1 : 0, debug_of(c) ? 1 : 0};
+  return Variant{kernel_proto(c), c->scope, c->ordering, aligned ? 1 : 0, debug_of(c) ? 1 : 0};
 }
 
 extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nbytes, int iters,
@@ -864,7 +913,7 @@ extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nb
   rc = plan_steps(c, nbytes, uint64_t(iters), add, "xfer_run");
   if (rc) return rc;
   DeviceGuard g(c->device);
-  const uint32_t total = grid_of(c->xcd_pairing, wgs_of(c));
+  const uint32_t total = grid_of(c, wgs_of(c));
   const Variant v = variant_of(c, aligned16(src) && aligned16(dst));
   rc = check_resident(c->device, v, 0, c->block, total, "xfer_run",
                       &c->cap_one[v.aligned][v.debug]);
@@ -877,6 +926,7 @@ extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nb
   args.total_wgs = total;
   args.xcd_remap = c->xcd_remap;
   args.timeout_ticks = c->timeout_ticks;
+  args.rx_wgs = rx_region_of(c);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = gate().run(c->device, s, [&] { return launch_run1(v, args, c->block, s); });
   if (e != hipSuccess) return hip_fail(e, "xfer_run launch");
@@ -936,7 +986,7 @@ extern "C" int xfer_run_messages(xfer_conn* c, const void* src, void* dst, const
     aligned = aligned && (m.off & 15u) == 0;
   }
   DeviceGuard g(c->device);
-  const uint32_t total = grid_of(c->xcd_pairing, wgs_of(c));
+  const uint32_t total = grid_of(c, wgs_of(c));
   const Variant v = variant_of(c, aligned);
   rc = check_resident(c->device, v, 3, c->block, total, "xfer_run_messages");
   if (rc) return rc;
@@ -951,6 +1001,7 @@ extern "C" int xfer_run_messages(xfer_conn* c, const void* src, void* dst, const
     args.xcd_remap = c->xcd_remap;
     args.timeout_ticks = c->timeout_ticks;
     args.nmsgs = uint32_t(cnt);
+    args.rx_wgs = rx_region_of(c);
     for (size_t i = 0; i < cnt; ++i) args.msgs[i] = msgs[first + i];
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = gate().run(c->device, s, [&] { return launch_runL(v, args, c->block, s); });
@@ -973,7 +1024,8 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
   std::vector<std::vector<uint64_t>> adds(static_cast<size_t>(n));
   RunBatch args;
   memset(&args, 0, sizeof(args));
-  uint32_t total = 0;
+  uint32_t total = 0;  // workgroups (zero-copy: producer workgroups)
+  uint32_t rx_total = 0;  // zero-copy: receiver workgroups, dispatched before every producer
   bool aligned = true;
   int live = 0;
   const xfer_conn* first = nullptr;
@@ -984,12 +1036,12 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
     for (int j = 0; j < i; ++j)
       if (conns[j] == c) return fail(XFER_ERR_INVALID_ARG, "xfer_run_batch: a connection appears twice");
     if (!first) first = c;
-    if (c->proto != first->proto || c->scope != first->scope || c->ordering != first->ordering ||
-        c->block != first->block || c->timeout_ticks != first->timeout_ticks ||
-        c->device != first->device)
+    if (kernel_proto(c) != kernel_proto(first) || c->scope != first->scope ||
+        c->ordering != first->ordering || c->block != first->block ||
+        c->timeout_ticks != first->timeout_ticks || c->device != first->device)
       return fail(XFER_ERR_INVALID_ARG,
-                  "xfer_run_batch: connections must share protocol, memory scope, ordering, "
-                  "block size, timeout and device");
+                  "xfer_run_batch: connections must share protocol (for LL, its line layout), "
+                  "memory scope, ordering, block size, timeout and device");
     if (nbytes[i] == 0) continue;
     if (!src[i] || !dst[i])
       return fail(XFER_ERR_INVALID_ARG, "xfer_run_batch: NULL src or dst with nbytes > 0");
@@ -998,8 +1050,9 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
     rc = plan_steps(c, nbytes[i], 1, adds[size_t(i)], "xfer_run_batch");
     if (rc) return rc;
     aligned = aligned && aligned16(src[i]) && aligned16(dst[i]);
-    args.conn[live] = conn_args(c, src[i], dst[i], nbytes[i], total);
-    total += wgs_of(c);
+    args.conn[live] = conn_args(c, src[i], dst[i], nbytes[i], total, rx_total);
+    rx_total += rx_wgs_of(c);
+    total += wgs_of(c) - rx_wgs_of(c);
     ++live;
   }
   if (!live) return XFER_OK;
@@ -1022,7 +1075,9 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
   Variant v = variant_of(first, aligned);
   for (int i = 0; i < n; ++i)
     if (debug_of(conns[i])) v.debug = 1;  // the others pass no buffer and no seed
-  const uint32_t grid = grid_of(first->xcd_pairing, total);
+  uint32_t rx_region = 0;
+  const uint32_t grid = zero_copy(first->proto) ? zc_grid(first, rx_total, total, &rx_region)
+                                                : grid_of(first, total);
   int rc = check_resident(first->device, v, 1, first->block, grid, "xfer_run_batch");
   if (rc) return rc;
   args.nconn = uint32_t(live);
@@ -1030,6 +1085,7 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
   args.total_wgs = grid;
   args.xcd_remap = first->xcd_remap;
   args.timeout_ticks = first->timeout_ticks;
+  args.rx_wgs = rx_region;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e =
       gate().run(first->device, s, [&] { return launch_runB(v, args, first->block, s); });
@@ -1068,10 +1124,10 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
   rc = plan_steps(rev, nbytes, uint64_t(iters), addr, "xfer_run_pingpong");
   if (rc) return rc;
   DeviceGuard g(fwd->device);
-  const uint32_t total = grid_of(fwd->xcd_pairing, wgs_of(fwd));
+  const uint32_t total = grid_of(fwd, wgs_of(fwd));
   const int scope = (fwd->scope == kScopeSystem || rev->scope == kScopeSystem) ? kScopeSystem
                                                                                : kScopeAgent;
-  const Variant v{fwd->proto, scope, fwd->ordering,
+  const Variant v{kernel_proto(fwd), scope, fwd->ordering,
                   (aligned16(a) && aligned16(b) && aligned16(cbuf)) ? 1 : 0,
                   (debug_of(fwd) || debug_of(rev)) ? 1 : 0};
   rc = check_resident(fwd->device, v, 2, fwd->block, total, "xfer_run_pingpong");
@@ -1222,7 +1278,7 @@ extern "C" int xfer_conn_abort(xfer_conn* c) {
 extern "C" int xfer_conn_launch_shape(const xfer_conn* c, int* workgroups, int* block_threads) {
   if (!c || !workgroups || !block_threads)
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_launch_shape: NULL argument");
-  *workgroups = int(grid_of(c->xcd_pairing, wgs_of(c)));
+  *workgroups = int(grid_of(c, wgs_of(c)));
   *block_threads = c->block;
   return XFER_OK;
 }

@@ -184,7 +184,9 @@ __device__ __forceinline__ Range chan_range(uint64_t n, uint32_t nch, uint32_t c
 // always written and drained by the same lane pair and that lane's head
 // covers every byte its producer will overwrite.  A short chunk still
 // spreads over as many lanes as it has blocks.  LL uses the same map over
-// lines (a block is blockDim.x lines).
+// lines (a block is blockDim.x lines), except on connections whose whole
+// step fits the lanes at one line per thread: their lanes own stripes of
+// lines (ll_striped).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer descriptor over n bytes: the buffer unit checks every access
@@ -343,8 +345,10 @@ struct Side {
 
 // DBG: the debug kernel variant, which writes the step trace and applies
 // the jitter.  Without it the trace ring and the jitter seed are constants
-// (null, 0), so every debug branch folds away.
-template <bool DBG>
+// (null, 0), so every debug branch folds away.  UNIFORM: the side is a
+// whole workgroup (its values are made wave-uniform); otherwise one thread
+// (a zero-copy receiver lane).
+template <bool DBG, bool UNIFORM = true>
 __device__ __forceinline__ Side make_side(const ConnArgs& A, uint32_t c, uint32_t w, bool producer,
                                           int sc) {
   Side s;
@@ -372,8 +376,13 @@ __device__ __forceinline__ Side make_side(const ConnArgs& A, uint32_t c, uint32_
     v = ld_u64<kScopeAgent>(own);
     e = ld_u32<kScopeAgent>(A.err_dev);
   }
-  s.base = uniform_u64(v);
-  s.dead = __builtin_amdgcn_readfirstlane(e) != 0;
+  if constexpr (UNIFORM) {
+    s.base = uniform_u64(v);
+    s.dead = __builtin_amdgcn_readfirstlane(e) != 0;
+  } else {
+    s.base = v;
+    s.dead = e != 0;
+  }
   s.seen = 0;
   return s;
 }
@@ -650,9 +659,100 @@ __device__ __forceinline__ void ll_dst_word(uint8_t* p, uint32_t L, uint32_t lin
   for (uint32_t b = 0; b < 4u && off + b < L; ++b) p[off + b] = static_cast<uint8_t>(v >> (8u * b));
 }
 
+// The striped LL layout (ll_layout, on the host): lane w owns lines
+// [w q, (w + 1) q) of every slot, and its threads cover `group` consecutive
+// steps at once, thread t taking line w q + t mod q of step t / q of the
+// group.  Vector memory operations complete in issue order, so one thread
+// looping over the steps of a message would hold each step's source load
+// behind the previous step's line store and each flag poll behind the
+// previous step's destination and head stores: a round trip per step.
+// Here the steps of a group go to different waves and overlap.  The
+// consumer frees a group with one head store, for its last step (its steps'
+// slots are distinct, and the producer has credit for all of them once head
+// reaches the group's first step).  Striped connections run kernels of
+// their own (kProtoLLStriped), so each kernel holds one layout only.
+
 template <int SC, int ORD, bool AL>
-__device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t g0,
+__device__ __forceinline__ bool ll_send_striped(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
+                                                uint64_t g0, const uint8_t* src, uint64_t ticks,
+                                                Shared& sh) {
+  const uint64_t S = A.step_bytes;
+  const uint32_t m = A.ll_group;
+  const uint32_t u = threadIdx.x >> A.ll_stripe_log2;  // (wave-uniform)
+  const uint32_t li = threadIdx.x & ((1u << A.ll_stripe_log2) - 1u);
+  const uint32_t i = (w << A.ll_stripe_log2) + li;     // this thread's line of a step
+  uint32_t err = 0;
+  for (uint64_t j0 = 0; j0 < sd.r.k && !err; j0 += m) {
+    const uint64_t j = j0 + u;
+    if (u >= m || j >= sd.r.k) continue;
+    const uint64_t g = g0 + j;
+    if ((err = wait_credit<SC, ORD, false>(A, sd, g, ticks, sh))) break;
+    const uint32_t L = chunk_len(sd, S, j);
+    if (li == 0) {  // the lines are the publication: stamp before this thread's
+      trace_step(A, sd, g, 0, sd.seen);
+      trace_step(A, sd, g, 1, g + 1);
+    }
+    jitter(sd, g, 0);
+    if (i < (L + 3u) / 4u) {
+      uint64_t* lines = reinterpret_cast<uint64_t*>(slot_of(A, c, g));
+      const uint64_t flag = static_cast<uint64_t>(static_cast<uint32_t>(g + 1)) << 32;
+      st_u64<SC>(&lines[i], flag | ll_src_word<AL>(src + sd.r.beg + j * S, L, i));
+    }
+  }
+  return !wg_failed(sh, err, A);
+}
+
+template <int SC, int ORD, bool AL>
+__device__ __forceinline__ bool ll_recv_striped(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
+                                                uint64_t g0, uint8_t* dst, uint64_t ticks,
+                                                Shared& sh) {
+  using O = Order<SC, ORD>;
+  const uint64_t S = A.step_bytes;
+  const uint32_t m = A.ll_group;
+  const uint32_t u = threadIdx.x >> A.ll_stripe_log2;
+  const uint32_t li = threadIdx.x & ((1u << A.ll_stripe_log2) - 1u);
+  const uint32_t i = (w << A.ll_stripe_log2) + li;
+  for (uint64_t j0 = 0; j0 < sd.r.k; j0 += m) {
+    const uint32_t nb = static_cast<uint32_t>(min(static_cast<uint64_t>(m), sd.r.k - j0));
+    const uint64_t j = j0 + u, g = g0 + j;
+    uint32_t err = 0;
+    if (u < nb) {
+      jitter(sd, g, 0);
+      const uint32_t L = chunk_len(sd, S, j);
+      if (i < (L + 3u) / 4u) {
+        const uint32_t want = static_cast<uint32_t>(g + 1);
+        const uint64_t* line = reinterpret_cast<const uint64_t*>(slot_of(A, c, g)) + i;
+        uint64_t v = ld_u64<SC>(line);
+        if (static_cast<uint32_t>(v >> 32) != want) {
+          Deadline dl(ticks, A.status);
+          do {
+            v = ld_u64<SC>(line);
+          } while (static_cast<uint32_t>(v >> 32) != want && !(err = dl.expired()));
+        }
+        if (!err) ll_dst_word<AL>(dst + sd.r.beg + j * S, L, i, static_cast<uint32_t>(v));
+      }
+    }
+    // Our line reads are complete before the slots go back: every value has
+    // fed its flag test.  Fenced ordering keeps its release fence.
+    if constexpr (ORD == kOrdFenced) O::release();
+    if (u < nb) jitter(sd, g, 1);
+    if (wg_failed(sh, err, A)) return false;
+    if (threadIdx.x == 0) {
+      const uint64_t gb = g0 + j0;
+      for (uint32_t x = 0; sd.tr != nullptr && x < nb; ++x) {
+        trace_step(A, sd, gb + x, 0, gb + x + 1);  // every line of the step seen
+        trace_step(A, sd, gb + x, 1, gb + nb);     // the head that hands it back
+      }
+      st_u64<SC>(&sd.tx->head, gb + nb);
+    }
+  }
+  return true;
+}
+
+template <int SC, int ORD, bool AL, bool STRIPED>
+__device__ __forceinline__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t g0,
                         const uint8_t* src, uint64_t ticks, Shared& sh) {
+  if constexpr (STRIPED) return ll_send_striped<SC, ORD, AL>(A, c, w, sd, g0, src, ticks, sh);
   const uint64_t S = A.step_bytes;
   const uint32_t P = A.lanes, nthr = blockDim.x;
   uint32_t err = 0;
@@ -682,9 +782,10 @@ __device__ bool ll_send(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uin
   return !wg_failed(sh, err, A);
 }
 
-template <int SC, int ORD, bool AL>
-__device__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t g0,
+template <int SC, int ORD, bool AL, bool STRIPED>
+__device__ __forceinline__ bool ll_recv(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd, uint64_t g0,
                         uint8_t* dst, uint64_t ticks, Shared& sh) {
+  if constexpr (STRIPED) return ll_recv_striped<SC, ORD, AL>(A, c, w, sd, g0, dst, ticks, sh);
   using O = Order<SC, ORD>;
   const uint64_t S = A.step_bytes;
   const uint32_t P = A.lanes, nthr = blockDim.x;
@@ -927,38 +1028,6 @@ __device__ bool zcd_send(const ConnArgs& A, uint32_t w, Side& sd, uint64_t g0,
   return true;
 }
 
-// Receiver of zero-copy direct (one thread): answer tail with head until the
-// message's last step has landed.
-template <int SC, int ORD>
-__device__ bool zcd_recv(const ConnArgs& A, Side& sd, uint64_t g0, uint64_t ticks) {
-  if (threadIdx.x != 0) return true;
-  const uint64_t end = g0 + sd.r.k;
-  uint64_t done = g0;
-  Deadline dl(ticks, A.status);
-  while (done < end) {
-    const uint64_t t = ld_u64<SC>(&sd.rx->tail);
-    if (t > done) {
-      Order<SC, ORD>::acquire();
-      for (uint64_t q = done; sd.tr != nullptr && q < t; ++q) {
-        trace_step(A, sd, q, 0, t);
-        trace_step(A, sd, q, 1, t);
-      }
-      jitter(sd, t, 1);
-      done = t;
-      st_u64<SC>(&sd.tx->head, t);
-      dl = Deadline(ticks, A.status);
-      continue;
-    }
-    const uint32_t e = dl.expired();
-    if (e) {
-      raise_err(A, e);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  return true;
-}
-
 // The launch's messages of one connection, repeated `iters` times.
 template <int MAXB>
 struct MsgList {
@@ -997,19 +1066,25 @@ struct StepCursor {
   }
 };
 
-// Receiver (one thread): publish the destination of the next step (the base
-// of its chunk in B) whenever the word is clear; complete steps once tail
-// passes them by publishing head.
+// Steps of channel c over every message of the launch.
+template <int MAXB, int NMSG>
+__device__ uint64_t launch_steps(const ConnArgs& A, uint32_t c, const RunArgs<MAXB, NMSG>& args) {
+  const MsgList<MAXB> L{args.msgs, args.nmsgs, A.nbytes};
+  uint64_t per_rep = 0;
+  for (uint32_t i = 0; i < L.count(); ++i) per_rep += chan_range(L.at(i).len, A.nch, c, A.step_bytes).k;
+  return per_rep * args.iters;
+}
+
+// Receiver of one lane, run by one thread: publish the destination of the
+// next step (the base of its chunk in B) whenever the word is clear;
+// complete steps once tail passes them by publishing head.
 template <int SC, int ORD, int MAXB, int NMSG>
 __device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<MAXB, NMSG>& args,
                         uint64_t ticks) {
   using O = Order<SC, ORD>;
-  if (threadIdx.x != 0) return;
   const MsgList<MAXB> L{args.msgs, args.nmsgs, A.nbytes};
   const uint64_t S = A.step_bytes;
-  uint64_t per_rep = 0;
-  for (uint32_t i = 0; i < L.count(); ++i) per_rep += chan_range(L.at(i).len, A.nch, c, S).k;
-  const uint64_t total = per_rep * args.iters;
+  const uint64_t total = launch_steps(A, c, args);
   StepCursor<MAXB> cur{0, 0, 0, 0, Range{0, 0, 0}, total == 0};
   if (!cur.done) {
     cur.load(L, A, c);
@@ -1054,6 +1129,37 @@ __device__ void zc_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<M
       }
       __builtin_amdgcn_s_sleep(1);
     }
+  }
+}
+
+// Receiver of one lane of zero-copy direct, run by one thread: answer tail
+// with head until the launch's last step on the channel has landed.
+template <int SC, int ORD, int MAXB, int NMSG>
+__device__ void zcd_recv(const ConnArgs& A, uint32_t c, Side& sd, const RunArgs<MAXB, NMSG>& args,
+                         uint64_t ticks) {
+  const uint64_t end = sd.base + launch_steps(A, c, args);
+  uint64_t done = sd.base;
+  Deadline dl(ticks, A.status);
+  while (done < end) {
+    const uint64_t t = ld_u64<SC>(&sd.rx->tail);
+    if (t > done) {
+      Order<SC, ORD>::acquire();
+      for (uint64_t q = done; sd.tr != nullptr && q < t; ++q) {
+        trace_step(A, sd, q, 0, t);
+        trace_step(A, sd, q, 1, t);
+      }
+      jitter(sd, t, 1);
+      done = t;
+      st_u64<SC>(&sd.tx->head, t);
+      dl = Deadline(ticks, A.status);
+      continue;
+    }
+    const uint32_t e = dl.expired();
+    if (e) {
+      raise_err(A, e);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
   }
 }
 
@@ -1123,36 +1229,62 @@ __global__ void xcc_probe_kernel(uint32_t* out) {
   if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();
 }
 
+// Zero-copy launches (through ptrExchange, or with the destination known):
+// blocks [0, rx_wgs) are receiver workgroups, in which the first
+// kRxLanesPerWave threads of each wave are the receivers of one lane each
+// (a connection's lanes in channel-major order); they are dispatched first,
+// since every producer waits for its first address.  The blocks after them
+// are the producers, one workgroup per lane, in the connections' order.  A
+// receiver moves a few words per step and no payload, so it takes a thread
+// rather than a workgroup: every CU the launch occupies beyond the
+// receivers' few copies payload.
+// With grouping (xcd_remap != 0) the host pads both regions to multiples
+// of 8 blocks; blocks dealt to one XCD then share their index mod 8, and
+// XCD-slot x takes the x-th eighth of the producers in order, so the lanes
+// of a channel (and of a connection, as far as they fill an eighth) run on
+// one XCD, as the paired layout of the other protocols keeps a pair.
 template <int PROTO, int SC, int ORD, bool AL, int MAXB, int NMSG, bool DBG>
-__global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB, NMSG> args) {
-  __shared__ Shared sh;
-  if (threadIdx.x == 0) sh.err = 0;
-  __syncthreads();
-  // Zero-copy through ptrExchange: each XCD dispatches its receivers first
-  // (the role bit flipped), since every producer waits for its receiver's
-  // first published address and a receiver is one busy thread.
-  const uint32_t lw = logical_wg(args.xcd_remap, args.total_wgs) ^
-                      ((PROTO == kProtoZC && args.xcd_remap) ? 1u : 0u);
+__device__ void zero_copy_wg(const RunArgs<MAXB, NMSG>& args, Shared& sh) {
+  const uint32_t b = blockIdx.x;
+  const uint64_t ticks = args.timeout_ticks;
   uint32_t ci = 0;
+  if (b < args.rx_wgs) {
+    if constexpr (MAXB > 1) {
+      while (ci + 1 < args.nconn && b >= args.conn[ci + 1].rx_begin) ++ci;
+    }
+    const ConnArgs& A = args.conn[ci];
+    const uint32_t r = b - A.rx_begin, nl = A.nch * A.lanes;
+    if (r >= zc_receiver_wgs(A.nch, A.lanes, blockDim.x)) return;  // padding of the region
+    if (!claim_wg<DBG>(A, nl + r, sh)) return;  // (receiver ids follow the producers')
+    const uint32_t li = threadIdx.x % 64u;
+    const uint32_t t = (r * (blockDim.x / 64u) + threadIdx.x / 64u) * kRxLanesPerWave + li;
+    if (li >= kRxLanesPerWave || t >= nl || !((A.roles >> 1) & 1u))
+      return;  // no lane, or receivers switched off
+    const uint32_t c = t / A.lanes, w = t % A.lanes;
+    Side sd = make_side<DBG, false>(A, c, w, false, SC);
+    if (sd.dead) return;
+    if constexpr (PROTO == kProtoZC)
+      zc_recv<SC, ORD, MAXB, NMSG>(A, c, sd, args, ticks);
+    else
+      zcd_recv<SC, ORD, MAXB, NMSG>(A, c, sd, args, ticks);
+    return;
+  }
+  uint32_t pw = b - args.rx_wgs;
+  if (args.xcd_remap) {
+    const uint32_t eighth = (args.total_wgs - args.rx_wgs) / 8u;
+    pw = (pw % 8u) * eighth + pw / 8u;
+  }
   if constexpr (MAXB > 1) {
-    while (ci + 1 < args.nconn && lw >= args.conn[ci + 1].wg_begin) ++ci;
+    while (ci + 1 < args.nconn && pw >= args.conn[ci + 1].wg_begin) ++ci;
   }
   const ConnArgs& A = args.conn[ci];
-  const uint32_t local = lw - A.wg_begin;
-  const uint32_t pair = local >> 1, role = local & 1u;
-  const uint32_t c = pair / A.lanes, w = pair % A.lanes;
-  if (c >= A.nch) return;  // padding of a paired launch (its grid is a multiple of 16)
+  const uint32_t local = pw - A.wg_begin;
+  const uint32_t c = local / A.lanes, w = local % A.lanes;
+  if (c >= A.nch) return;
   if (!claim_wg<DBG>(A, local, sh)) return;
-  if (!((A.roles >> role) & 1u)) return;  // side switched off for fault injection
-  Side sd = make_side<DBG>(A, c, w, role == 0, SC);
+  if (!(A.roles & 1u)) return;  // producers switched off for fault injection
+  Side sd = make_side<DBG>(A, c, w, true, SC);
   if (sd.dead) return;
-  const uint64_t ticks = args.timeout_ticks;
-  if constexpr (PROTO == kProtoZC) {
-    if (role == 1) {
-      zc_recv<SC, ORD, MAXB, NMSG>(A, c, sd, args, ticks);
-      return;
-    }
-  }
   const MsgList<MAXB> L{args.msgs, args.nmsgs, A.nbytes};
   uint64_t g0 = sd.base;
   for (uint32_t rep = 0; rep < args.iters; ++rep) {
@@ -1161,24 +1293,61 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB, NMSG> args) {
       sd.r = chan_range(md.len, A.nch, c, A.step_bytes);
       if (sd.r.k == 0) continue;
       bool ok;
-      if constexpr (PROTO == kProtoSimple)
-        ok = role == 0 ? simple_send<SC, ORD, AL>(A, c, w, sd, g0, A.src + md.off, ticks, sh)
-                       : simple_recv<SC, ORD, AL>(A, c, w, sd, g0, A.dst + md.off, ticks, sh);
-      else if constexpr (PROTO == kProtoZCD)
-        ok = role == 0
-                 ? zcd_send<SC, ORD, AL>(A, w, sd, g0, A.src + md.off, A.dst + md.off, ticks, sh)
-                 : zcd_recv<SC, ORD>(A, sd, g0, ticks);
-      else if constexpr (PROTO == kProtoLL)
-        ok = role == 0 ? ll_send<SC, ORD, AL>(A, c, w, sd, g0, A.src + md.off, ticks, sh)
-                       : ll_recv<SC, ORD, AL>(A, c, w, sd, g0, A.dst + md.off, ticks, sh);
-      else
+      if constexpr (PROTO == kProtoZC)
         ok = zc_send<SC, ORD, AL>(A, c, w, sd, g0, A.src + md.off, ticks, sh);
+      else
+        ok = zcd_send<SC, ORD, AL>(A, w, sd, g0, A.src + md.off, A.dst + md.off, ticks, sh);
       if (!ok) return;
       g0 += sd.r.k;
     }
   }
-  if constexpr (PROTO == kProtoLL) {
-    if (role == 0 && g0 != sd.base) ll_close<SC>(sd, g0);
+}
+
+template <int PROTO, int SC, int ORD, bool AL, int MAXB, int NMSG, bool DBG>
+__global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB, NMSG> args) {
+  constexpr bool kStriped = PROTO == kProtoLLStriped;
+  __shared__ Shared sh;
+  if (threadIdx.x == 0) sh.err = 0;
+  __syncthreads();
+  if constexpr (PROTO == kProtoZC || PROTO == kProtoZCD) {
+    zero_copy_wg<PROTO, SC, ORD, AL, MAXB, NMSG, DBG>(args, sh);
+  } else {
+    const uint32_t lw = logical_wg(args.xcd_remap, args.total_wgs);
+    uint32_t ci = 0;
+    if constexpr (MAXB > 1) {
+      while (ci + 1 < args.nconn && lw >= args.conn[ci + 1].wg_begin) ++ci;
+    }
+    const ConnArgs& A = args.conn[ci];
+    const uint32_t local = lw - A.wg_begin;
+    const uint32_t pair = local >> 1, role = local & 1u;
+    const uint32_t c = pair / A.lanes, w = pair % A.lanes;
+    if (c >= A.nch) return;  // padding of a paired launch (its grid is a multiple of 16)
+    if (!claim_wg<DBG>(A, local, sh)) return;
+    if (!((A.roles >> role) & 1u)) return;  // side switched off for fault injection
+    Side sd = make_side<DBG>(A, c, w, role == 0, SC);
+    if (sd.dead) return;
+    const uint64_t ticks = args.timeout_ticks;
+    const MsgList<MAXB> L{args.msgs, args.nmsgs, A.nbytes};
+    uint64_t g0 = sd.base;
+    for (uint32_t rep = 0; rep < args.iters; ++rep) {
+      for (uint32_t mi = 0; mi < L.count(); ++mi) {
+        const MsgDesc md = L.at(mi);
+        sd.r = chan_range(md.len, A.nch, c, A.step_bytes);
+        if (sd.r.k == 0) continue;
+        bool ok;
+        if constexpr (PROTO == kProtoSimple)
+          ok = role == 0 ? simple_send<SC, ORD, AL>(A, c, w, sd, g0, A.src + md.off, ticks, sh)
+                         : simple_recv<SC, ORD, AL>(A, c, w, sd, g0, A.dst + md.off, ticks, sh);
+        else
+          ok = role == 0 ? ll_send<SC, ORD, AL, kStriped>(A, c, w, sd, g0, A.src + md.off, ticks, sh)
+                         : ll_recv<SC, ORD, AL, kStriped>(A, c, w, sd, g0, A.dst + md.off, ticks, sh);
+        if (!ok) return;
+        g0 += sd.r.k;
+      }
+    }
+    if constexpr (PROTO != kProtoSimple) {
+      if (role == 0 && g0 != sd.base) ll_close<SC>(sd, g0);
+    }
   }
 }
 
@@ -1186,6 +1355,7 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB, NMSG> args) {
 // side 1 is endpoint Y (receive on fwd into b, then send b on rev).
 template <int PROTO, int SC, int ORD, bool AL, bool DBG>
 __global__ void __launch_bounds__(1024) ping_kernel(PingArgs args) {
+  constexpr bool kStriped = PROTO == kProtoLLStriped;
   __shared__ Shared sh;
   if (threadIdx.x == 0) sh.err = 0;
   __syncthreads();
@@ -1208,23 +1378,23 @@ __global__ void __launch_bounds__(1024) ping_kernel(PingArgs args) {
     const uint64_t gf = fs.base + it * k, gr = rs.base + it * k;
     bool ok;
     if (side == 0) {
-      if constexpr (PROTO == kProtoLL)
-        ok = ll_send<SC, ORD, AL>(F, c, w, fs, gf, F.src, ticks, sh) &&
-             ll_recv<SC, ORD, AL>(R, c, w, rs, gr, R.dst, ticks, sh);
+      if constexpr (PROTO != kProtoSimple)
+        ok = ll_send<SC, ORD, AL, kStriped>(F, c, w, fs, gf, F.src, ticks, sh) &&
+             ll_recv<SC, ORD, AL, kStriped>(R, c, w, rs, gr, R.dst, ticks, sh);
       else
         ok = simple_send<SC, ORD, AL>(F, c, w, fs, gf, F.src, ticks, sh) &&
              simple_recv<SC, ORD, AL>(R, c, w, rs, gr, R.dst, ticks, sh);
     } else {
-      if constexpr (PROTO == kProtoLL)
-        ok = ll_recv<SC, ORD, AL>(F, c, w, fs, gf, F.dst, ticks, sh) &&
-             ll_send<SC, ORD, AL>(R, c, w, rs, gr, R.src, ticks, sh);
+      if constexpr (PROTO != kProtoSimple)
+        ok = ll_recv<SC, ORD, AL, kStriped>(F, c, w, fs, gf, F.dst, ticks, sh) &&
+             ll_send<SC, ORD, AL, kStriped>(R, c, w, rs, gr, R.src, ticks, sh);
       else
         ok = simple_recv<SC, ORD, AL>(F, c, w, fs, gf, F.dst, ticks, sh) &&
              simple_send<SC, ORD, AL>(R, c, w, rs, gr, R.src, ticks, sh);
     }
     if (!ok) return;
   }
-  if constexpr (PROTO == kProtoLL) {
+  if constexpr (PROTO != kProtoSimple) {
     if (side == 0)
       ll_close<SC>(fs, fs.base + args.iters * k);
     else
@@ -1266,6 +1436,7 @@ RunFn<MAXB, NMSG> pick_run(const Variant& v) {
   switch (v.proto) {
     case kProtoSimple: return pick_run_sc<MAXB, NMSG, kProtoSimple>(v);
     case kProtoLL: return pick_run_sc<MAXB, NMSG, kProtoLL>(v);
+    case kProtoLLStriped: return pick_run_sc<MAXB, NMSG, kProtoLLStriped>(v);
     case kProtoZCD: return pick_run_sc<MAXB, NMSG, kProtoZCD>(v);
     default: return pick_run_sc<MAXB, NMSG, kProtoZC>(v);
   }
@@ -1294,7 +1465,9 @@ PingFn pick_ping_sc(const Variant& v) {
 }
 
 PingFn pick_ping(const Variant& v) {
-  return v.proto == kProtoLL ? pick_ping_sc<kProtoLL>(v) : pick_ping_sc<kProtoSimple>(v);
+  return v.proto == kProtoLL          ? pick_ping_sc<kProtoLL>(v)
+         : v.proto == kProtoLLStriped ? pick_ping_sc<kProtoLLStriped>(v)
+                                      : pick_ping_sc<kProtoSimple>(v);
 }
 
 }  // namespace

@@ -71,7 +71,7 @@ struct DevState {
   bool ready;
   uint8_t* base;
   uint64_t khz;
-  int cap[4][2][2][kBlocks];  // [proto][ordering][aligned][block / 64 - 1]; 0 = not queried
+  int cap[5][2][2][kBlocks];  // [kernel proto][ordering][aligned][block / 64 - 1]; 0 = not queried
 };
 DevState g_dev[kMaxDevices];
 std::mutex g_mu;
@@ -202,13 +202,24 @@ extern "C" int xfer_run_noalloc(int proto, int nchannels, int nslots, size_t slo
   if (rc) return rc;
   const bool aligned = (reinterpret_cast<uintptr_t>(src) & 15u) == 0 &&
                        (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
-  // (the public protocol numbers are the kernels' own)
-  const Variant v{proto, kScopeAgent, a.ordering, aligned ? 1 : 0, 0};
+  // (the public protocol numbers are the kernels' own; striped LL has its own)
+  uint32_t ll_l2 = 0, ll_group = 0;
+  if (proto == XFER_PROTO_LL)
+    ll_layout(step, uint32_t(lanes), uint32_t(block), uint32_t(nslots), &ll_l2, &ll_group);
+  const Variant v{ll_l2 ? int(kProtoLLStriped) : proto, kScopeAgent, a.ordering, aligned ? 1 : 0,
+                  0};
   // Pairs placed on one XCD by block id (the XCD-id placement needs a
-  // device probe that allocates, so it is not used here).
+  // device probe that allocates, so it is not used here); zero-copy
+  // launches have no pairs.
   const bool pairing = a.xcd_pairing != -1;
-  const uint32_t wgs = uint32_t(nchannels) * uint32_t(lanes) * 2u;
-  const uint32_t grid = pairing ? (wgs + 15u) & ~15u : wgs;
+  const uint32_t wgs = conn_wgs(proto, uint32_t(nchannels), uint32_t(lanes), uint32_t(block));
+  const uint32_t rx = zc ? zc_receiver_wgs(uint32_t(nchannels), uint32_t(lanes), uint32_t(block))
+                         : 0u;
+  // zero-copy grouping pads the receiver and producer regions to 8 blocks each
+  const uint32_t rx_region = pairing ? (rx + 7u) & ~7u : rx;
+  const uint32_t grid = !pairing ? wgs
+                        : zc     ? rx_region + ((wgs - rx + 7u) & ~7u)
+                                 : (wgs + 15u) & ~15u;
   int cap = 0;
   rc = capacity(d, v, block, &cap);
   if (rc) return rc;
@@ -217,7 +228,7 @@ extern "C" int xfer_run_noalloc(int proto, int nchannels, int nslots, size_t slo
                 "xfer_run_noalloc: more workgroups than the GPU holds resident at once");
   const hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* base = d->base;
-  const uint64_t ctrl_bytes = uint64_t(wgs / 2u) * sizeof(LaneCtrl);
+  const uint64_t ctrl_bytes = uint64_t(nchannels) * uint64_t(lanes) * sizeof(LaneCtrl);
   const uint64_t na = (kCtrlOff + ctrl_bytes) / 8;
   const uint64_t nb = proto == XFER_PROTO_LL ? fifo_bytes / 8 : 0;
   const uint64_t cblocks = std::min<uint64_t>(1024, (na + nb + 255) / 256);
@@ -242,10 +253,14 @@ extern "C" int xfer_run_noalloc(int proto, int nchannels, int nslots, size_t slo
   c.nslots = uint32_t(nslots);
   c.lanes = uint32_t(lanes);
   c.roles = 3;
+  if (proto == XFER_PROTO_LL)
+    ll_layout(step, uint32_t(lanes), uint32_t(block), uint32_t(nslots), &c.ll_stripe_log2,
+              &c.ll_group);
   args.nconn = 1;
   args.iters = 1;
   args.total_wgs = grid;
   args.xcd_remap = pairing ? 1u : 0u;
+  args.rx_wgs = rx_region;
   args.timeout_ticks = uint64_t(a.timeout_ms ? a.timeout_ms : 10000u) * d->khz;
   e = launch_run1(v, args, block, s);
   if (e != hipSuccess) return hip_fail(e, "xfer_run_noalloc: transfer launch");

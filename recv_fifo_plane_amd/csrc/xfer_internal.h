@@ -59,7 +59,9 @@ struct TraceRec {
 };
 static_assert(sizeof(TraceRec) == 32, "trace record layout");
 
-enum : uint32_t { kProtoSimple = 0, kProtoLL = 1, kProtoZC = 2, kProtoZCD = 3 };
+// Kernel protocols: the public ones, and LL in the striped line layout
+// (ll_layout), which gets kernels of its own.
+enum : uint32_t { kProtoSimple = 0, kProtoLL = 1, kProtoZC = 2, kProtoZCD = 3, kProtoLLStriped = 4 };
 enum : int { kScopeAgent = 0, kScopeSystem = 1 };
 
 // Device view of one connection for one run.
@@ -74,7 +76,10 @@ struct ConnArgs {
   uint64_t nbytes;
   uint64_t slot_bytes;
   uint64_t step_bytes;
-  uint32_t nch, nslots, lanes, wg_begin;
+  uint32_t nch, nslots, lanes;
+  uint32_t wg_begin;   // first logical workgroup of this connection (zero-copy: of its
+                       // producers, counted from the first producer of the launch)
+  uint32_t rx_begin;   // zero-copy: first receiver workgroup of this connection
   uint32_t roles;  // bit 0: producer side runs, bit 1: consumer side runs
   uint32_t relay;  // 1: the consumer waits on gtail and drains fifo_rx
   TraceRec* trace;     // step trace, or nullptr: [nch * lanes * 2] rings of trace_per records
@@ -84,6 +89,9 @@ struct ConnArgs {
                        // read by every workgroup on entry
   uint64_t* claims;    // debug variant: per logical workgroup, the last launch that claimed it
   uint64_t launch_seq; // debug variant: this launch's number on the connection (from 1)
+  uint32_t ll_stripe_log2;  // LL striped layout (ll_layout): log2 of a lane's lines per slot,
+                            // 0 when the connection does not use it
+  uint32_t ll_group;        // LL striped layout: steps a lane's threads cover at once
 };
 
 // One message of a launch: bytes [off, off + len) of the connection's src
@@ -110,7 +118,7 @@ struct RunArgs {
   uint32_t xcd_remap;    // 0: dispatch order; 1: pairs on one XCD; 2: the same by XCD id
   uint64_t timeout_ticks;
   uint32_t nmsgs;        // single-connection launches only
-  uint32_t pad;
+  uint32_t rx_wgs;       // zero-copy: receiver workgroups, blocks [0, rx_wgs) of the grid
   MsgDesc msgs[NMSG];
 };
 using RunOne = RunArgs<1, 1>;           // one transfer (xfer_run, xfer_run_loop)
@@ -128,9 +136,48 @@ struct PingArgs {
   uint32_t pad;
 };
 
+// Workgroups of one connection's launch.  SIMPLE and LL: a producer and a
+// consumer workgroup per lane.  Both zero-copy protocols: a producer
+// workgroup per lane, and receiver workgroups in which the first
+// kRxLanesPerWave threads of each wave serve one lane each (a receiver has
+// a few words to move per step, no payload).
+constexpr uint32_t kRxLanesPerWave = 16;
+__host__ __device__ inline uint32_t zc_receiver_wgs(uint32_t nch, uint32_t lanes, uint32_t block) {
+  const uint32_t per_wg = kRxLanesPerWave * (block / 64u);
+  return (nch * lanes + per_wg - 1) / per_wg;
+}
+__host__ __device__ inline bool zero_copy_proto(int proto) { return proto == kProtoZC || proto == kProtoZCD; }
+__host__ __device__ inline uint32_t conn_wgs(int proto, uint32_t nch, uint32_t lanes, uint32_t block) {
+  return zero_copy_proto(proto) ? nch * lanes + zc_receiver_wgs(nch, lanes, block)
+                                : nch * lanes * 2u;
+}
+
+// LL line layout of a connection.  When a whole step fits the lanes at one
+// line per thread, lane w owns the stripe [w q, (w + 1) q) of every slot's
+// lines, q = the step's lines over the lanes rounded up to a power of two of
+// at least a wave, and its threads cover group = min(block / q, nslots)
+// consecutive steps at once (thread t: step t / q of the group, line
+// w q + t mod q).  Otherwise (*log2q = 0) lanes own blocks of `block` lines
+// dealt round-robin.  Fixed per connection: it depends on the step size,
+// lanes, block size and slot count only.
+__host__ __device__ inline void ll_layout(uint64_t step_bytes, uint32_t lanes, uint32_t block,
+                                          uint32_t nslots, uint32_t* log2q, uint32_t* group) {
+  *log2q = 0;
+  *group = 1;
+  const uint64_t lines = step_bytes / 4u;
+  if (lines > uint64_t(block) * lanes) return;
+  const uint64_t per = (lines + lanes - 1u) / lanes;
+  uint32_t l2 = 6;  // a wave
+  while ((uint64_t(1) << l2) < per) ++l2;
+  if ((1u << l2) > block) return;
+  *log2q = l2;
+  *group = block >> l2;
+  if (*group > nslots) *group = nslots;
+}
+
 // Kernel-variant selector and launchers (kernels.hip).
 struct Variant {
-  int proto;     // kProto*
+  int proto;     // kProto* (LL connections in the striped layout: kProtoLLStriped)
   int scope;     // kScope*
   int ordering;  // 0: coherent accesses, 1: scoped fences
   int aligned;   // all of src/dst 16-byte aligned

@@ -24,15 +24,17 @@ from . import xfer as X
 W1 = dict(name="simple_1ch_4MiB", proto="simple", nchannels=1, nslots=8, slot_bytes=128 << 10,
           fifo_loc="device", wgs_per_channel=1, block_threads=512, nbytes=4 << 20)
 
-# 16 workgroup pairs of 256 threads: a whole 16 KiB step is one line per
-# thread, so messages up to 16 KiB take one pass (swept: 1.0-1.2 us one-way
-# up to 16 KiB and 3.4 us at 64 KiB, against 3.7 and 8.6 us with one
-# 1024-thread pair).  Each connection's FIFO and counters are placed by
-# measured latency at the fastest of eight offsets 2 KiB apart
+# 16 workgroup pairs of 1024 threads: each lane owns a 256-line stripe of
+# every slot (the 4096 lines of a 16 KiB step over 16 lanes), and its 16
+# waves cover 4 steps at once, so a 64 KiB message is one group of 4 steps
+# handed back by one head store (measured 1.65 us one-way at 64 KiB and
+# 0.92 us at 8 B, against 3.39 and 0.99 us with 256-thread lanes that take
+# the steps one after another).  Each connection's FIFO and counters are
+# placed by measured latency at the fastest of eight offsets 2 KiB apart
 # (place_trials): the time of a hand-off depends on the physical granule of
 # the polled lines.
 W2 = dict(name="ll_pingpong", proto="ll", nchannels=1, nslots=8, slot_bytes=32 << 10,
-          fifo_loc="device", wgs_per_channel=16, block_threads=256, iters=10000, place_trials=8)
+          fifo_loc="device", wgs_per_channel=16, block_threads=1024, iters=10000, place_trials=8)
 W2_SIZES = [8 << i for i in range(14)]  # 8 B .. 64 KiB
 
 # 4 workgroups per channel side as the workload fixes them; the block size
@@ -46,15 +48,21 @@ W3 = dict(name="simple_32ch_1GiB", proto="simple", nchannels=32, nslots=8, slot_
 # The same workload with P2P read: the FIFO in the send side's memory.
 W3R = dict(W3, name="simple_32ch_1GiB_p2p_read", p2p_read=1)
 
+# Zero-copy launches run one producer workgroup per lane and a few receiver
+# workgroups (one thread per lane).  Shapes swept (fraction of HBM, 2 x
+# payload): the pair at 16 x 128 with each channel's lanes grouped on one
+# XCD, 0.72 (0.58 in dispatch order); the ring at 8 x 512 in dispatch
+# order, 0.765 (0.72 grouped by XCD, 0.73 at 16 x 128).
 W4_PAIR = dict(name="zc_pair_128MiB", proto="zc", nchannels=32, nslots=1, slot_bytes=512 << 10,
                fifo_loc="device", wgs_per_channel=16, block_threads=128, nbytes=128 << 20)
 
 W4_RING = dict(name="zc_ring_8x128MiB", proto="zc", endpoints=8, channels_per_edge=4,
-               nslots=1, slot_bytes=512 << 10, fifo_loc="device", wgs_per_channel=4,
-               block_threads=512, slice_bytes=128 << 20, max_peers=128)
+               nslots=1, slot_bytes=512 << 10, fifo_loc="device", wgs_per_channel=8,
+               block_threads=512, xcd_pairing=-1, slice_bytes=128 << 20, max_peers=128)
 
 # The same two zero-copy workloads with the destination known before the
-# launch (no ptrExchange hand-off); the ring's launch shape was swept apart.
+# launch (no ptrExchange hand-off): the pair 0.76 grouped, the ring 0.75 at
+# 16 x 128 in dispatch order.
 W4D_PAIR = dict(W4_PAIR, name="zcd_pair_128MiB", proto="zcd")
 W4D_RING = dict(W4_RING, name="zcd_ring_8x128MiB", proto="zcd", wgs_per_channel=16,
                 block_threads=128)

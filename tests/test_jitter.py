@@ -62,27 +62,32 @@ def test_pingpong_under_jitter(proto):
         x.close()
 
 
-def test_zero_copy_ring_batch_under_jitter():
+@pytest.mark.parametrize("proto", ["zc", "zcd"])
+def test_zero_copy_ring_batch_under_jitter(proto):
+    # every edge of the ring, after two batches under jitter, must hold the
+    # oracle's counters (and B the oracle's bytes)
     import torch
 
     from recv_fifo_plane_amd import workloads as W
-    cfg = dict(W.W4_RING, slice_bytes=3 << 20)
-    log("case: zero-copy ring under jitter")
+    cfg = dict(W.W4_RING if proto == "zc" else W.W4D_RING, slice_bytes=3 << 20)
+    log("case: %s ring under jitter" % proto)
     ring = W.make_ring(cfg)
     for i, e in enumerate(ring.edges.values()):
         e.set_jitter(0xA11CE + i)
-    n = 8 * cfg["slice_bytes"]
-    a = torch.from_numpy(synth.uint8_uniform(n, 5)).to("cuda")
+    S = cfg["slice_bytes"]
+    nch = cfg["channels_per_edge"]
+    A = synth.uint8_uniform(8 * S, 5)
+    a = to_dev(A)
     b = torch.zeros_like(a)
+    ocns = {k: oracle.Conn(proto, nch, 1, cfg["slot_bytes"]) for k in ring.edges}
+    B = np.zeros_like(A)
     for _ in range(2):
         ring.run(a, b)
+        for (r, d), o in ocns.items():
+            o.run(np.ascontiguousarray(A[r * S:(r + 1) * S]), B[d * S:(d + 1) * S])
     torch.cuda.synchronize()
-    S = cfg["slice_bytes"]
-    for r in range(8):
-        d = (r + 1) % 8
-        assert torch.equal(a[r * S:(r + 1) * S], b[d * S:(d + 1) * S]), r
-    for e in ring.edges.values():
-        for ch in range(cfg["channels_per_edge"]):
-            st = e.query(ch)
-            assert st["error"] == 0 and st["head"] == st["tail"] and st["ptr_exchange"] == 0
+    assert np.array_equal(to_host(b), B)
+    for k, e in ring.edges.items():
+        compare_state(e, ocns[k], nch, "%s ring under jitter, edge %s" % (proto, k))
+        ocns[k].close()
     ring.close()

@@ -257,3 +257,24 @@ def test_trace_pingpong_orders_the_round_trips():
             assert rev_ready <= ev(F, 0, 0, 0, i + 1, 1)["time"], i
     for c in conns:
         c.close()
+
+
+@pytest.mark.parametrize("jitter", [0, 0x5EED])
+def test_trace_ll_striped_groups(jitter):
+    # the striped layout (1024-thread lanes, a 512-line stripe each, groups
+    # of 2 steps with 3 slots): every step is stamped once per lane and side,
+    # a step's lines are seen after the producer published them, and a slot
+    # is taken again only after the head that handed it back
+    nch, nslots, lanes, slot, n, q = 2, 3, 2, 8192, 90_001, 512
+    log("case: trace ll striped jitter=%#x" % jitter)
+    R, _, S = traced_run("ll", nch, nslots, slot, lanes, n, block=1024, jitter=jitter)
+    ks = check_complete(R, n, nch, lanes, S)
+    for c in range(nch):
+        for w in range(lanes):
+            for g in range(ks[c]):
+                L = min(S, oracle.partition(n, nch)[1][c] - g * S)
+                if w * q >= (L + 3) // 4:
+                    continue
+                assert ev(R, c, w, 0, g, 1)["time"] < ev(R, c, w, 1, g, 0)["time"], (c, w, g)
+                if g >= nslots:
+                    assert ev(R, c, w, 1, g - nslots, 1)["time"] < ev(R, c, w, 0, g, 0)["time"]
