@@ -566,7 +566,7 @@ def main() -> int:
     if args.only == "relay":
         # the duplex copy rate of the link is measured by the host-FIFO mode;
         # alone, the relay reports against PCIe only
-        print(json.dumps({"relay_4ch_4MiB": bench_relay(torch, T, W, synth, None)}),
+        print(json.dumps({W.W5R["name"]: bench_relay(torch, T, W, synth, None)}),
               flush=True)
         return 0
     log("bench: W3 simple 32ch 1GiB, %d warmup + %d steps" % (args.warmup, args.steps))
@@ -626,7 +626,7 @@ def main() -> int:
         modes["host_fifo_16ch_2GiB"] = bench_w5(torch, T, W, synth)
         log("bench: copy-engine relay")
         w5 = modes["host_fifo_16ch_2GiB"]
-        modes["relay_4ch_4MiB"] = bench_relay(
+        modes[W.W5R["name"]] = bench_relay(
             torch, T, W, synth,
             None if w5["pinned_copy_duplex_serialized"] else w5["pinned_copy_duplex_gbs_each_way"])
         modes["plain_copy_1GiB_torch"] = plain

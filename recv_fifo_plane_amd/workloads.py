@@ -73,9 +73,12 @@ W5 = dict(name="host_fifo_16ch_2GiB", proto="simple", nchannels=16, nslots=8,
 
 # The copy-engine relay (SIMPLE through send FIFO -> pinned staging FIFO ->
 # receive FIFO, moved by two host proxies on the DMA engines): one 512 MiB
-# transfer, and the host-FIFO workload's message mix.  Few channels of large
-# slots keep the copies large (each step is one DMA copy per direction).
-W5R = dict(name="relay_4ch_4MiB", proto="simple", nchannels=4, nslots=8, slot_bytes=4 << 20,
+# transfer, and the host-FIFO workload's message mix.  Every step is one DMA
+# copy per direction, and a copy has a fixed cost (about 4 us at the least),
+# so the mix's many small messages want few channels: swept, one channel of
+# 8 x 8 MiB slots moved the mix at 42 GB/s and 512 MiB at 46 GB/s, two
+# channels 41 and 45, four channels of 4 MiB 34 and 42, sixteen 16 and 26.
+W5R = dict(name="relay_1ch_8MiB", proto="simple", nchannels=1, nslots=8, slot_bytes=8 << 20,
            fifo_loc="relay", wgs_per_channel=8, block_threads=1024, nbytes=512 << 20,
            total_bytes=2 << 30)
 
