@@ -1,8 +1,10 @@
 /* A plain C caller of the library: no Python, no torch.  It allocates the
  * buffers with the HIP runtime, moves 3 MiB + 5 bytes through a SIMPLE
  * connection (4 channels x 8 slots x 64 KiB in HBM) twice on one stream,
- * and checks the destination, the counters and an error path.  Exit code 0
- * means every check passed; the first failing check prints its reason. */
+ * and checks the destination, the counters and an error path; then it
+ * moves the same bytes with the entry point that allocates nothing, as LL,
+ * and checks the destination and the reported status.  Exit code 0 means
+ * every check passed; the first failing check prints its reason. */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -78,6 +80,26 @@ int main(void) {
   CHECK(rc == XFER_ERR_INVALID_ARG && strlen(xfer_last_error()) > 0, "overlap not refused");
 
   CHECK(xfer_conn_destroy(c) == XFER_OK, "destroy");
+
+  /* no connection, nothing allocated by the library: LL through its fixed
+     array, the failure code written to a device word after the transfer */
+  uint32_t* status = NULL;
+  uint32_t status_host = 0x7777;
+  CHECK(hipMalloc((void**)&status, sizeof(*status)) == hipSuccess, "hipMalloc(status)");
+  CHECK(hipMemset(dst, 0, n) == hipSuccess, "clear");
+  memset(&attr, 0, sizeof(attr));
+  attr.wgs_per_channel = 4;
+  attr.block_threads = 512;
+  rc = xfer_run_noalloc(XFER_PROTO_LL, nch, nslots, 32u << 10, &attr, src, dst, n, status,
+                        (void*)stream);
+  CHECK(rc == XFER_OK, "noalloc: %s (%s)", xfer_status_string(rc), xfer_last_error());
+  CHECK(hipStreamSynchronize(stream) == hipSuccess, "sync");
+  CHECK(hipMemcpy(back, dst, n, hipMemcpyDeviceToHost) == hipSuccess, "download");
+  CHECK(hipMemcpy(&status_host, status, sizeof(status_host), hipMemcpyDeviceToHost) == hipSuccess,
+        "status download");
+  CHECK(status_host == 0, "noalloc status %u", status_host);
+  CHECK(memcmp(host, back, n) == 0, "noalloc destination differs from source");
+  (void)hipFree(status);
   (void)hipStreamDestroy(stream);
   (void)hipFree(src);
   (void)hipFree(dst);
