@@ -31,6 +31,10 @@ ORDER = {
     "pages": 0,
     "zc_take_ahead": 1,  # ZC: take step g+1's address after writing step g, before tail = g+1
 }
+# LL, the striped kernels' order: aligned groups of m steps, step j written by
+# sub-producer j mod m and read by sub-consumer j mod m, one head per group.
+GROUP_MAX = 4
+ORDER.update({"ll_group%d" % m: 0x100 + m for m in range(1, GROUP_MAX + 1)})
 
 MUT = {
     "none": 0,
@@ -43,6 +47,7 @@ MUT = {
     "early_head": 7,
     "zc_ahead_past_end": 8,
     "relay_early": 9,
+    "group_no_barrier": 10,
 }
 VIOLATIONS = {
     0: "ok",

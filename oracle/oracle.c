@@ -241,6 +241,12 @@ typedef struct {
   uint64_t cj, cline, cnpub;
   uint32_t cphase, pad;
   uint64_t sj, rj; /* RELAY: next step of the send proxy and of the receive proxy */
+  /* LL group order: for sub-producer and sub-consumer x < m, the next step
+   * (x, x + m, ...) and the line within it; cbar is the first step of the
+   * group the sub-consumers read (the one past their last barrier), and cj
+   * the first step of the group whose head is still to be published */
+  uint64_t gpj[ORC_GROUP_MAX], gpl[ORC_GROUP_MAX], gcj[ORC_GROUP_MAX], gcl[ORC_GROUP_MAX];
+  uint64_t cbar;
 } orc_cur;
 
 typedef struct {
@@ -298,6 +304,7 @@ static int world_begin(world* w, const orc_conn* c, const uint8_t* A, uint64_t n
     u[ch].len = len[ch];
     u[ch].k = (len[ch] + c->step_bytes - 1) / c->step_bytes;
     if (c->proto == ORC_LL && q[ch].base + u[ch].k > 0xFFFFFFFFull) return ORC_E_RANGE;
+    for (int x = 0; x < ORC_GROUP_MAX; ++x) u[ch].gpj[x] = u[ch].gcj[x] = (uint64_t)x;
   }
   int64_t* fill = W_fill(w); /* every FIFO's fill and drain marks, contiguous */
   for (int i = 0; i < 2 * ntrack(c) * c->nch * c->nslots; ++i) fill[i] = -1;
@@ -316,10 +323,11 @@ static uint8_t* slot_ptr_in(const world* w, int f, int ch, uint64_t g) {
 }
 static uint8_t* slot_ptr(const world* w, int ch, uint64_t g) { return slot_ptr_in(w, 0, ch, g); }
 
-/* Reading R2: the credit test. */
+/* Reading R2: the credit test, g - head < nslots over the integers (a head
+ * already past g, which only a broken consumer publishes, is credit too). */
 static int credit_ok(const world* w, const orc_ctrl* q, uint64_t g) {
-  uint64_t inflight = g - q->head, ns = (uint64_t)w->cfg->nslots;
-  return w->cfg->mutation == ORC_MUT_WEAK_CREDIT ? inflight <= ns : inflight < ns;
+  uint64_t ns = (uint64_t)w->cfg->nslots;
+  return w->cfg->mutation == ORC_MUT_WEAK_CREDIT ? g <= q->head + ns : g < q->head + ns;
 }
 
 static size_t slot_index(const world* w, int ch, uint64_t g) {
@@ -361,6 +369,23 @@ static uint32_t get32(const uint8_t* p) {
 
 /* ------------------------------------------------------------------ actors */
 enum { ACT_PROD = 0, ACT_CONS = 1, ACT_PUB = 2, ACT_SPROXY = 3, ACT_RPROXY = 4, N_ACT = 5 };
+/* LL group order: sub-producers and sub-consumers x < m are actors of their
+ * own; ACT_PROD then only writes the bookkeeping tail and ACT_PUB is the
+ * group's head store. */
+enum { ACT_GPROD = N_ACT, ACT_GCONS = N_ACT + ORC_GROUP_MAX, N_ACT_ALL = N_ACT + 2 * ORC_GROUP_MAX };
+
+/* Group size m of the LL group order, 0 in every other order. */
+static int ll_group(const orc_conn* c) {
+  if (c->proto != ORC_LL || c->order <= ORC_ORDER_LL_GROUP(0) ||
+      c->order > ORC_ORDER_LL_GROUP(ORC_GROUP_MAX))
+    return 0;
+  return c->order - ORC_ORDER_LL_GROUP(0);
+}
+
+/* One past the last step of the aligned group that starts at step s. */
+static uint64_t group_end(const orc_cur* u, int m, uint64_t s) {
+  return s + (uint64_t)m < u->k ? s + (uint64_t)m : u->k;
+}
 
 /* Whether the ZC producer, having written step pj, takes step pj+1's
  * address before it publishes tail (the kernels' pipelined order). */
@@ -379,6 +404,11 @@ static int prod_enabled(const world* w, int ch) {
     case ORC_RELAY:
       return u->pj < u->k && (u->pphase != 0 || credit_ok(w, q, g));
     case ORC_LL:
+      if (ll_group(c)) { /* the bookkeeping tail, once every sub-producer is done */
+        for (int x = 0; x < ll_group(c); ++x)
+          if (u->gpj[x] < u->k) return 0;
+        return !u->pfinal;
+      }
       if (u->pj == u->k) return !u->pfinal;
       return u->pline > 0 || u->pphase != 0 || credit_ok(w, q, g);
     case ORC_ZCD: /* the destination is known: nothing to wait for */
@@ -403,6 +433,7 @@ static int cons_enabled(const world* w, int ch) {
       if (c->mutation == ORC_MUT_EARLY_HEAD) return u->cphase == 0 ? q->tail > g : 1;
       return u->cphase == 0 ? q->tail > g : 1;
     case ORC_LL: {
+      if (ll_group(c)) return 0; /* the sub-consumers read instead */
       if (u->cphase == 1) return 1;
       const uint8_t* line = slot_ptr(w, ch, g) + 8 * u->cline;
       return get32(line + 4) == (uint32_t)(g + 1);
@@ -416,9 +447,13 @@ static int cons_enabled(const world* w, int ch) {
 
 static int pub_enabled(const world* w, int ch) {
   const orc_conn* c = w->cfg;
-  if (c->proto != ORC_ZC) return 0;
   const orc_ctrl* q = &W_ctrl(w)[ch];
   const orc_cur* u = &W_cur(w)[ch];
+  if (ll_group(c)) { /* the group's head store: after the barrier, or (mutation) after step cj */
+    if (u->cj >= u->k) return 0;
+    return c->mutation == ORC_MUT_GROUP_NO_BARRIER ? u->gcj[0] > u->cj : u->cj < u->cbar;
+  }
+  if (c->proto != ORC_ZC) return 0;
   return u->cnpub < u->k && (c->mutation == ORC_MUT_ZC_NO_WAIT || q->ptrx == 0);
 }
 
@@ -434,7 +469,12 @@ static int proxy_enabled(const world* w, int ch, int act) {
   return u->rj < u->k && q->ytail > q->base + u->rj;
 }
 
+static int gprod_enabled(const world* w, int ch, int x);
+static int gcons_enabled(const world* w, int ch, int x);
+
 static int enabled(const world* w, int ch, int act) {
+  if (act >= ACT_GCONS) return gcons_enabled(w, ch, act - ACT_GCONS);
+  if (act >= ACT_GPROD) return gprod_enabled(w, ch, act - ACT_GPROD);
   switch (act) {
     case ACT_PROD: return prod_enabled(w, ch);
     case ACT_CONS: return cons_enabled(w, ch);
@@ -600,6 +640,110 @@ static int ll_cons(world* w, int ch, uint64_t budget) {
   return 0;
 }
 
+/* LL in groups of m steps (the striped kernels' order, ORC_ORDER_LL_GROUP):
+ * the lines and flags are those of Reading R4; what changes is who writes
+ * and reads which step, and when a slot is handed back.  Sub-producer x
+ * writes steps x, x+m, ... in order, each only on credit (Reading R2), so
+ * different sub-producers may be in different groups at once.  Sub-consumer
+ * x reads step (group start) + x of the group its barrier released it into;
+ * the group's last reader completes the barrier, and one head store, head =
+ * (group end), then frees every slot of the group. */
+static int gprod_enabled(const world* w, int ch, int x) {
+  const orc_conn* c = w->cfg;
+  if (x >= ll_group(c)) return 0;
+  const orc_ctrl* q = &W_ctrl(w)[ch];
+  const orc_cur* u = &W_cur(w)[ch];
+  if (u->gpj[x] >= u->k) return 0;
+  return u->gpl[x] > 0 || credit_ok(w, q, q->base + u->gpj[x]);
+}
+
+static int gprod(world* w, int ch, int x, uint64_t budget) {
+  const orc_conn* c = w->cfg;
+  orc_ctrl* q = &W_ctrl(w)[ch];
+  orc_cur* u = &W_cur(w)[ch];
+  uint64_t j = u->gpj[x], g = q->base + j, L = chunk_len(w, u, j), nl = ll_lines(L);
+  const uint8_t* src = w->A + u->beg + j * c->step_bytes;
+  uint8_t* slot = slot_ptr(w, ch, g);
+  if (u->gpl[x] == 0) {
+    if (!slot_free(w, ch, g)) return ORC_V_OVERWRITE;
+    mark_fill(w, ch, g);
+  }
+  while (budget--) {
+    uint8_t* line = slot + 8 * u->gpl[x];
+    put32(line, ll_word(src, L, u->gpl[x]));
+    put32(line + 4, (uint32_t)(g + 1));
+    if (++u->gpl[x] == nl) {
+      u->gpl[x] = 0;
+      u->gpj[x] += (uint64_t)ll_group(c);
+      break;
+    }
+  }
+  return 0;
+}
+
+static int gcons_enabled(const world* w, int ch, int x) {
+  const orc_conn* c = w->cfg;
+  if (x >= ll_group(c)) return 0;
+  const orc_ctrl* q = &W_ctrl(w)[ch];
+  const orc_cur* u = &W_cur(w)[ch];
+  uint64_t j = u->gcj[x];
+  if (j >= group_end(u, ll_group(c), u->cbar)) return 0; /* done, or waiting at the barrier */
+  if (x == 0 && u->cj < u->cbar) return 0; /* sub-consumer 0 stores the last group's head first */
+  const uint8_t* line = slot_ptr(w, ch, q->base + j) + 8 * u->gcl[x];
+  return get32(line + 4) == (uint32_t)(q->base + j + 1);
+}
+
+static int gcons(world* w, int ch, int x, uint64_t budget) {
+  const orc_conn* c = w->cfg;
+  const int m = ll_group(c);
+  orc_ctrl* q = &W_ctrl(w)[ch];
+  orc_cur* u = &W_cur(w)[ch];
+  uint64_t j = u->gcj[x], g = q->base + j, L = chunk_len(w, u, j), nl = ll_lines(L);
+  const uint8_t* slot = slot_ptr(w, ch, g);
+  const uint8_t* src = w->A + u->beg + j * c->step_bytes;
+  uint8_t* dst = w->B + u->beg + j * c->step_bytes;
+  while (budget--) {
+    const uint8_t* line = slot + 8 * u->gcl[x];
+    if (get32(line + 4) != (uint32_t)(g + 1)) break;
+    uint32_t wv = get32(line);
+    if (wv != ll_word(src, L, u->gcl[x])) return ORC_V_READ_UNFILLED;
+    for (uint64_t b = 0; b < 4 && 4 * u->gcl[x] + b < L; ++b)
+      dst[4 * u->gcl[x] + b] = (uint8_t)(wv >> (8 * b));
+    if (++u->gcl[x] == nl) {
+      mark_drain(w, ch, g);
+      u->gcl[x] = 0;
+      u->gcj[x] += (uint64_t)m;
+      uint64_t s = u->cbar, e = group_end(u, m, s);
+      int all = 1; /* the barrier: every step of the group read */
+      for (int y = 0; y < m && s + (uint64_t)y < e; ++y)
+        if (u->gcj[y] < s + (uint64_t)m) all = 0;
+      if (all) u->cbar = e;
+      break;
+    }
+  }
+  return 0;
+}
+
+/* The group's head store frees every slot of the group at once. */
+static int ghead(world* w, int ch) {
+  orc_ctrl* q = &W_ctrl(w)[ch];
+  orc_cur* u = &W_cur(w)[ch];
+  uint64_t e = group_end(u, ll_group(w->cfg), u->cj);
+  q->head = q->base + e;
+  u->cj = e;
+  return 0;
+}
+
+/* Reading R4's bookkeeping tail, once every sub-producer is done. */
+static int gfinal(world* w, int ch) {
+  orc_ctrl* q = &W_ctrl(w)[ch];
+  orc_cur* u = &W_cur(w)[ch];
+  q->tail = q->base + u->k;
+  u->pj = u->k;
+  u->pfinal = 1;
+  return 0;
+}
+
 /* Zero-copy producer (Reading R7): take the published address, clear the
  * word, write the chunk straight into B there, publish tail = g+1.  In the
  * take-ahead order the producer takes step g+1's address between writing
@@ -730,6 +874,11 @@ static int fire(world* w, int ch, int act, uint64_t budget) {
     case ORC_SIMPLE:
       return act == ACT_PROD ? simple_prod(w, ch) : simple_cons(w, ch);
     case ORC_LL:
+      if (ll_group(w->cfg)) {
+        if (act >= ACT_GCONS) return gcons(w, ch, act - ACT_GCONS, budget);
+        if (act >= ACT_GPROD) return gprod(w, ch, act - ACT_GPROD, budget);
+        return act == ACT_PROD ? gfinal(w, ch) : ghead(w, ch);
+      }
       return act == ACT_PROD ? ll_prod(w, ch, budget) : ll_cons(w, ch, budget);
     case ORC_ZCD:
       return act == ACT_PROD ? zcd_prod(w, ch) : zc_done(w, ch);
@@ -751,9 +900,19 @@ static int window_ok(const world* w, int ch) {
   if (!has_fifo(c->proto)) return 1;
   const orc_ctrl* q = &W_ctrl(w)[ch];
   const orc_cur* u = &W_cur(w)[ch];
+  const int m = ll_group(c);
+  if (m) { /* one past the highest step any sub-producer has begun */
+    uint64_t top = 0;
+    for (int x = 0; x < m; ++x) {
+      uint64_t j = u->gpj[x];
+      uint64_t t = u->gpl[x] > 0 ? j + 1 : (j >= (uint64_t)m ? j - (uint64_t)m + 1 : 0);
+      if (t > top) top = t;
+    }
+    return q->base + top <= q->head + (uint64_t)c->nslots;
+  }
   uint64_t begun = u->pj;
   if (u->pj < u->k && (u->pphase != 0 || (c->proto == ORC_LL && u->pline > 0))) ++begun;
-  return q->base + begun - q->head <= (uint64_t)c->nslots;
+  return q->base + begun <= q->head + (uint64_t)c->nslots;
 }
 
 static int world_done(const world* w) {
@@ -762,6 +921,8 @@ static int world_done(const world* w) {
   for (int ch = 0; ch < c->nch; ++ch) {
     if (u[ch].pj != u[ch].k || u[ch].cj != u[ch].k) return 0;
     if (c->proto == ORC_LL && !u[ch].pfinal) return 0;
+    for (int x = 0; x < ll_group(c); ++x) /* no sub-consumer still reading */
+      if (u[ch].gcj[x] < u[ch].k) return 0;
     if (c->proto == ORC_RELAY && (u[ch].sj != u[ch].k || u[ch].rj != u[ch].k)) return 0;
   }
   return 1;
@@ -812,8 +973,10 @@ int orc_run(orc_conn* c, const uint8_t* A, uint8_t* B, uint64_t n) {
   while (!world_done(&w)) {
     int moved = 0;
     for (int ch = 0; ch < c->nch && !rc; ++ch) {
-      static const int order[N_ACT] = {ACT_PROD, ACT_PUB, ACT_SPROXY, ACT_RPROXY, ACT_CONS};
-      for (int a = 0; a < N_ACT && !rc; ++a) {
+      static const int order[N_ACT_ALL] = {
+          ACT_GPROD, ACT_GPROD + 1, ACT_GPROD + 2, ACT_GPROD + 3, ACT_PROD, ACT_PUB, ACT_SPROXY,
+          ACT_RPROXY, ACT_GCONS, ACT_GCONS + 1, ACT_GCONS + 2, ACT_GCONS + 3, ACT_CONS};
+      for (int a = 0; a < N_ACT_ALL && !rc; ++a) {
         if (!enabled(&w, ch, order[a])) continue;
         rc = fire(&w, ch, order[a], ~0ull);
         if (!rc && !window_ok(&w, ch)) rc = ORC_V_WINDOW;
@@ -927,9 +1090,11 @@ static const char* vname(int v) {
 }
 
 static const char* aname(int act) {
-  static const char* names[N_ACT] = {"producer", "consumer", "publisher", "send proxy",
-                                     "receive proxy"};
-  return act >= 0 && act < N_ACT ? names[act] : "?";
+  static const char* names[N_ACT_ALL] = {
+      "producer",       "consumer",       "publisher",      "send proxy",     "receive proxy",
+      "sub-producer 0", "sub-producer 1", "sub-producer 2", "sub-producer 3", "sub-consumer 0",
+      "sub-consumer 1", "sub-consumer 2", "sub-consumer 3"};
+  return act >= 0 && act < N_ACT_ALL ? names[act] : "?";
 }
 
 typedef struct {
@@ -955,7 +1120,10 @@ int orc_enumerate(int proto, int nch, int nslots, uint64_t slot_bytes, const uin
                   int mutation, int order, int prior_runs, uint64_t max_states,
                   orc_enum_result* out) {
   if (!out || (n && !A) || prior_runs < 0) return ORC_E_ARG;
-  if (order != ORC_ORDER_PAGES && order != ORC_ORDER_ZC_TAKE_AHEAD) return ORC_E_ARG;
+  int group_order = order > ORC_ORDER_LL_GROUP(0) && order <= ORC_ORDER_LL_GROUP(ORC_GROUP_MAX);
+  if (order != ORC_ORDER_PAGES && order != ORC_ORDER_ZC_TAKE_AHEAD && !group_order)
+    return ORC_E_ARG;
+  if (group_order && proto != ORC_LL) return ORC_E_ARG;
   memset(out, 0, sizeof(*out));
   out->channel = -1;
   orc_conn* c = orc_conn_new(proto, nch, nslots, slot_bytes);
@@ -1039,7 +1207,7 @@ int orc_enumerate(int proto, int nch, int nslots, uint64_t slot_bytes, const uin
     }
     int any = 0;
     for (int ch = 0; ch < nch && !rc; ++ch) {
-      for (int act = 0; act < N_ACT && !rc; ++act) {
+      for (int act = 0; act < N_ACT_ALL && !rc; ++act) {
         if (!enabled(&v, ch, act)) continue;
         any = 1;
         uint8_t* nxt = (uint8_t*)malloc((size_t)blob);

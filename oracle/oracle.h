@@ -74,6 +74,8 @@ extern "C" {
 #define ORC_MUT_ZC_AHEAD_PAST_END 8 /* ZC take-ahead order: also waits for an address after the
                                        transfer's last step */
 #define ORC_MUT_RELAY_EARLY 9 /* RELAY: the send proxy copies a slot without waiting for tail */
+#define ORC_MUT_GROUP_NO_BARRIER 10 /* LL group order: head for a group is published once the
+                                       group's first step is read, not all of its steps */
 
 /* producer program orders: the pages' order, and the orders the GPU kernels
  * use where they differ from it (each must stay safe and confluent) */
@@ -81,6 +83,19 @@ extern "C" {
 #define ORC_ORDER_ZC_TAKE_AHEAD 1 /* ZC: the producer takes step g+1's address, when g+1 is a step
                                      of the same transfer, after writing step g and before it
                                      publishes tail = g+1 */
+/* LL, the striped kernels' order with groups of m steps (1 <= m <= ORC_GROUP_MAX):
+ * steps are taken in aligned groups of m; on the producer side, step j is
+ * written by sub-producer j mod m, which takes its steps in order and each
+ * only on credit, independently of the other sub-producers; on the consumer
+ * side, sub-consumer j mod m reads step j's lines, the sub-consumers of a
+ * group meet at a barrier once all of the group's steps are read, and then
+ * one head store, head = the group's last step + 1, frees the whole group
+ * (issued by sub-consumer 0 before it reads its next step; the others go on
+ * to the next group's steps at once).  m may exceed nslots in the model (the
+ * kernels never build that): the enumerator then finds the deadlock that
+ * rules it out. */
+#define ORC_GROUP_MAX 4
+#define ORC_ORDER_LL_GROUP(m) (0x100 + (m))
 
 /* setup-plan op kinds */
 #define ORC_OP_RECV_SETUP 0

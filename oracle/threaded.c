@@ -404,6 +404,8 @@ static void commit(orc_conn* c, const tconn* t, const tside* prod) {
 
 int orc_run_threaded(orc_conn* c, const uint8_t* A, uint8_t* B, uint64_t n, int nthreads) {
   if (!c || (n && (!A || !B)) || nthreads < 1) return ORC_E_ARG;
+  /* the threads run the pages' program order; the LL group order is the enumerator's */
+  if (c->proto == ORC_LL && c->order != ORC_ORDER_PAGES) return ORC_E_ARG;
   const int per_ch = c->proto == ORC_RELAY ? 4 : 2; /* actors per channel */
   if (nthreads > per_ch * c->nch) nthreads = per_ch * c->nch;
   uint64_t base[64];

@@ -332,6 +332,98 @@ def test_enumerator_catches_broken_rules_under_take_ahead(mutation, expected):
     assert r["violation"] in expected, r
 
 
+# The striped LL kernels take a transfer's steps in aligned groups of m <=
+# nslots: step j is written by sub-producer j mod m (its own waves, each step
+# on its own credit) and read by sub-consumer j mod m; the readers of a group
+# meet at a barrier and one head store frees the whole group.  That order
+# must be as safe and confluent as the pages' step-at-a-time order, end in
+# the same state, and the enumerator must catch the mistakes it invites.
+@pytest.mark.parametrize("nch,nslots,m,slot", [(1, 1, 1, 16), (1, 2, 2, 16), (1, 3, 2, 16),
+                                               (1, 3, 3, 16), (1, 4, 4, 16), (1, 8, 4, 8),
+                                               (1, 6, 3, 16), (2, 2, 2, 16), (2, 4, 2, 16)])
+def test_ll_group_order_is_safe_and_confluent(nch, nslots, m, slot):
+    S = slot // 2
+    steps = (3 * m + 1) if nch == 1 else (2 * m + 1)
+    for n in sorted({1, S - 1, S, S + 1, m * S, m * S + 1, nch * (steps * S - 3),
+                     nch * steps * S}):
+        A = synth.uint8_uniform(n, 5000 + n)
+        for prior in (0, 2):
+            r = oracle.enumerate_interleavings("ll", nch, nslots, slot, A, prior_runs=prior,
+                                               order="ll_group%d" % m)
+            assert r["violation"] == "ok" and r["terminals"] == 1, (n, prior, r)
+
+
+def test_ll_group_of_one_step_is_the_pages_order():
+    # With m = 1 the group order is the pages' order action for action: the
+    # enumerator visits exactly as many states and transitions.
+    for nch, nslots, slot in [(1, 1, 16), (1, 2, 16), (1, 3, 32), (2, 2, 16)]:
+        for n in (1, 9, 40, 77):
+            A = synth.uint8_uniform(n, 6000 + n)
+            a = oracle.enumerate_interleavings("ll", nch, nslots, slot, A)
+            b = oracle.enumerate_interleavings("ll", nch, nslots, slot, A, order="ll_group1")
+            assert (a["states"], a["transitions"]) == (b["states"], b["transitions"]), (nch, n)
+            assert a["violation"] == b["violation"] == "ok"
+
+
+@pytest.mark.parametrize("nslots,m", [(8, 4), (4, 4), (3, 2), (16, 4)])
+def test_ll_group_order_ends_in_the_pages_state(nslots, m):
+    for n in (0, 5, 16, 100, 1000, 4099):
+        A = synth.uint8_uniform(n, 7000 + n)
+        ends = []
+        for order in ("pages", "ll_group%d" % m):
+            c = oracle.Conn("ll", 3, nslots, 64)
+            c.set_order(order)
+            B = np.zeros(n, dtype=np.uint8)
+            for _ in range(3):
+                B[:] = 0
+                c.run(A, B)
+            ends.append((B.tobytes(), [sorted(c.state(ch).items()) for ch in range(3)],
+                         [c.fifo(ch).tobytes() for ch in range(3)]))
+            c.close()
+        assert ends[0] == ends[1], (nslots, m, n)
+        assert ends[1][0] == A.tobytes()
+
+
+@pytest.mark.parametrize("nslots,m", [(1, 2), (2, 3), (3, 4)])
+def test_ll_group_larger_than_the_fifo_deadlocks(nslots, m):
+    # A group's head comes only after all of its steps are read, and its last
+    # step needs credit from that head once m > nslots: no group may
+    # outnumber the slots (the kernels cap m at nslots).
+    A = synth.uint8_uniform((m + 1) * 8, 8)
+    r = oracle.enumerate_interleavings("ll", 1, nslots, 16, A, order="ll_group%d" % m)
+    assert r["violation"] == "deadlock", r
+    # a transfer of at most nslots steps (one partial group) still goes through
+    r = oracle.enumerate_interleavings("ll", 1, nslots, 16, A[: nslots * 8],
+                                       order="ll_group%d" % m)
+    assert r["violation"] == "ok", r
+
+
+@pytest.mark.parametrize("nslots,m", [(2, 2), (3, 2), (4, 4), (8, 4)])
+def test_enumerator_catches_a_group_head_without_its_barrier(nslots, m):
+    # head for the group stored once its first step is read, the others
+    # still being read: the producer then refills one of their slots.
+    A = synth.uint8_uniform((2 * m + 2) * 8 + 3, 9)
+    r = oracle.enumerate_interleavings("ll", 1, nslots, 16, A, mutation="group_no_barrier",
+                                       order="ll_group%d" % m)
+    assert r["violation"] == "overwrite", r
+    r = oracle.enumerate_interleavings("ll", 1, nslots, 16, A, mutation="weak_credit",
+                                       order="ll_group%d" % m)
+    assert r["violation"] in {"overwrite", "window"}, r
+
+
+def test_ll_group_order_is_for_ll_on_the_sequential_modes_only():
+    A = synth.uint8_uniform(40, 1)
+    with pytest.raises(oracle.OracleError):
+        oracle.enumerate_interleavings("simple", 1, 2, 16, A, order="ll_group2")
+    c = oracle.Conn("ll", 1, 4, 16)
+    try:
+        c.set_order("ll_group2")
+        with pytest.raises(oracle.OracleError):
+            c.run_threaded(A, np.zeros_like(A), 2)
+    finally:
+        c.close()
+
+
 def test_conn_rejects_bad_shapes():
     for args in [("simple", 0, 8, 16), ("simple", 65, 8, 16), ("simple", 1, 0, 16),
                  ("simple", 1, 8, 24), ("ll", 1, 8, 12), ("zc", 1, 8, 8), ("zcd", 1, 8, 8),
