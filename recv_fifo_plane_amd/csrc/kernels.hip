@@ -672,10 +672,37 @@ __device__ __forceinline__ void ll_dst_word(uint8_t* p, uint32_t L, uint32_t lin
 // reaches the group's first step).  Striped connections run kernels of
 // their own (kProtoLLStriped), so each kernel holds one layout only.
 
+// A source word of a striped send loaded ahead of it: the word of this
+// thread's line in the first group of the send (`ok` false: none).  The
+// ping-pong's endpoint X sends the same buffer a every round and never
+// writes it (its receive writes c, which may not overlap a), so it loads
+// the next round's word before it polls for the reply: the load then does
+// not wait, in issue order, behind the reply's destination and head stores.
+struct NextWord {
+  bool ok;
+  uint32_t word;
+};
+
+template <bool AL>
+__device__ __forceinline__ NextWord ll_striped_first_word(const ConnArgs& A, uint32_t w,
+                                                          const Side& sd, const uint8_t* src) {
+  const uint32_t u = threadIdx.x >> A.ll_stripe_log2;
+  const uint32_t i = (w << A.ll_stripe_log2) + (threadIdx.x & ((1u << A.ll_stripe_log2) - 1u));
+  NextWord nw{false, 0u};
+  if (u < A.ll_group && u < sd.r.k) {
+    const uint32_t L = chunk_len(sd, A.step_bytes, u);
+    if (i < (L + 3u) / 4u) {
+      nw.word = ll_src_word<AL>(src + sd.r.beg + u * A.step_bytes, L, i);
+      nw.ok = true;
+    }
+  }
+  return nw;
+}
+
 template <int SC, int ORD, bool AL>
 __device__ __forceinline__ bool ll_send_striped(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
                                                 uint64_t g0, const uint8_t* src, uint64_t ticks,
-                                                Shared& sh) {
+                                                Shared& sh, const NextWord* pre = nullptr) {
   const uint64_t S = A.step_bytes;
   const uint32_t m = A.ll_group;
   const uint32_t u = threadIdx.x >> A.ll_stripe_log2;  // (wave-uniform)
@@ -696,17 +723,31 @@ __device__ __forceinline__ bool ll_send_striped(const ConnArgs& A, uint32_t c, u
     if (i < (L + 3u) / 4u) {
       uint64_t* lines = reinterpret_cast<uint64_t*>(slot_of(A, c, g));
       const uint64_t flag = static_cast<uint64_t>(static_cast<uint32_t>(g + 1)) << 32;
-      st_u64<SC>(&lines[i], flag | ll_src_word<AL>(src + sd.r.beg + j * S, L, i));
+      const uint32_t v = pre != nullptr && j0 == 0 && pre->ok
+                             ? pre->word
+                             : ll_src_word<AL>(src + sd.r.beg + j * S, L, i);
+      st_u64<SC>(&lines[i], flag | v);
     }
   }
   return !wg_failed(sh, err, A);
 }
 
-template <int SC, int ORD, bool AL>
+// What a striped receive does before its first poll: nothing, or (the
+// ping-pong's endpoint X) load its next send's source word.
+struct NoAhead {
+  static constexpr bool kActive = false;
+  __device__ void operator()() const {}
+};
+
+template <int SC, int ORD, bool AL, typename Ahead = NoAhead>
 __device__ __forceinline__ bool ll_recv_striped(const ConnArgs& A, uint32_t c, uint32_t w, Side& sd,
                                                 uint64_t g0, uint8_t* dst, uint64_t ticks,
-                                                Shared& sh) {
+                                                Shared& sh, Ahead ahead = Ahead()) {
   using O = Order<SC, ORD>;
+  if constexpr (Ahead::kActive) {
+    ahead();
+    compiler_fence();  // issued before the polls below
+  }
   const uint64_t S = A.step_bytes;
   const uint32_t m = A.ll_group;
   const uint32_t u = threadIdx.x >> A.ll_stripe_log2;
@@ -1351,6 +1392,21 @@ __global__ void __launch_bounds__(1024) run_kernel(RunArgs<MAXB, NMSG> args) {
   }
 }
 
+// Endpoint X's action before it polls for a reply: load the source word of
+// its next send (when there is one).
+template <bool AL>
+struct LoadNext {
+  static constexpr bool kActive = true;
+  const ConnArgs* F;
+  const Side* fs;
+  uint32_t w;
+  bool more;
+  NextWord* out;
+  __device__ void operator()() const {
+    *out = more ? ll_striped_first_word<AL>(*F, w, *fs, F->src) : NextWord{false, 0u};
+  }
+};
+
 // Ping-pong: pair side 0 is endpoint X (send on fwd, then receive on rev),
 // side 1 is endpoint Y (receive on fwd into b, then send b on rev).
 template <int PROTO, int SC, int ORD, bool AL, bool DBG>
@@ -1374,16 +1430,24 @@ __global__ void __launch_bounds__(1024) ping_kernel(PingArgs args) {
   const uint64_t k = fs.r.k;
   if (k == 0) return;
   const uint64_t ticks = args.timeout_ticks;
+  NextWord next{false, 0u};  // endpoint X's source word of its next send, loaded ahead
   for (uint32_t it = 0; it < args.iters; ++it) {
     const uint64_t gf = fs.base + it * k, gr = rs.base + it * k;
     bool ok;
     if (side == 0) {
-      if constexpr (PROTO != kProtoSimple)
+      if constexpr (kStriped) {
+        // the next round's source word is loaded before the reply's polls
+        ok = ll_send_striped<SC, ORD, AL>(F, c, w, fs, gf, F.src, ticks, sh, &next);
+        if (ok)
+          ok = ll_recv_striped<SC, ORD, AL>(R, c, w, rs, gr, R.dst, ticks, sh,
+                                            LoadNext<AL>{&F, &fs, w, it + 1 < args.iters, &next});
+      } else if constexpr (PROTO != kProtoSimple) {
         ok = ll_send<SC, ORD, AL, kStriped>(F, c, w, fs, gf, F.src, ticks, sh) &&
              ll_recv<SC, ORD, AL, kStriped>(R, c, w, rs, gr, R.dst, ticks, sh);
-      else
+      } else {
         ok = simple_send<SC, ORD, AL>(F, c, w, fs, gf, F.src, ticks, sh) &&
              simple_recv<SC, ORD, AL>(R, c, w, rs, gr, R.dst, ticks, sh);
+      }
     } else {
       if constexpr (PROTO != kProtoSimple)
         ok = ll_recv<SC, ORD, AL, kStriped>(F, c, w, fs, gf, F.dst, ticks, sh) &&
