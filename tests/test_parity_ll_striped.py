@@ -65,7 +65,9 @@ def test_striped_message_list():
     run_message_list("ll", 2, 3, 8192, sizes, lanes=2, block=1024, repeat=2)
 
 
-@pytest.mark.parametrize("size", [8, 16384, 16385, 65536])
+# 100 003 bytes: seven steps, so a round is two groups of the four steps a
+# lane's waves cover (endpoint X loads the first group's source words ahead)
+@pytest.mark.parametrize("size", [8, 16384, 16385, 65536, 100_003])
 @pytest.mark.parametrize("jitter", [0, 0x7A11])
 def test_striped_pingpong_matches_oracle(size, jitter):
     import torch
