@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
 SHAPES = [
     ("simple", 4, 4, 65536, 2, 256),
     ("ll", 4, 4, 32768, 2, 256),
+    ("ll", 2, 4, 8192, 2, 1024),  # striped lines: 512-line stripes, groups of 2 steps
     ("zc", 4, 1, 65536, 2, 128),
     ("zcd", 3, 1, 65536, 1, 256),
 ]
@@ -50,7 +51,7 @@ def _run_both(proto, nch, nslots, slot, lanes, block, n, src_off, dst_off, seed)
     conn.close()
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+@pytest.mark.parametrize("shape", SHAPES, ids=["-".join(map(str, s)) for s in SHAPES])
 def test_noalloc_matches_run_on_two_calls(shape):
     proto, nch, nslots, slot, lanes, block = shape
     log("case: noalloc %s nch=%d nslots=%d slot=%d lanes=%d" % shape[:5])
