@@ -167,6 +167,15 @@ typedef struct {
                            a new one.  Creation takes a few milliseconds longer.  SIMPLE or
                            LL in write mode with the FIFO and control words in HBM;
                            otherwise INVALID_ARG. */
+  int cooperative;      /* 0 (default) or 1: launch this connection's transfers as cooperative
+                           grids (hipLaunchCooperativeKernel), which the runtime starts only
+                           with every workgroup resident at once and otherwise refuses with
+                           XFER_ERR_HIP, whatever else holds the GPU.  Without it, the library
+                           checks the grid against the GPU's capacity and orders its own
+                           launches (see "Launch order"), but kernels of other code can still
+                           delay part of a grid.  Costs about 15-18 us per launch on MI355X.
+                           A batch or ping-pong needs the same setting on all its
+                           connections.  Not with xfer_run_noalloc.  Otherwise INVALID_ARG. */
 } xfer_attr;
 
 /* State of one channel, read back after the stream has been synchronised. */
@@ -292,7 +301,7 @@ int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, void* b, vo
  *   no FIFO).  attr: NULL or wgs_per_channel, block_threads, timeout_ms,
  *   xcd_pairing (-1: dispatch order; 0 or 1: pairs on one XCD by block id)
  *   and ordering; ctrl_loc must be DEFAULT or DEVICE, roles and p2p_read 0,
- *   place_trials 0 or 1 (otherwise INVALID_ARG).
+ *   place_trials 0 or 1, cooperative 0 (otherwise INVALID_ARG).
  *   src, dst, nbytes as for xfer_run.  stream as everywhere.
  *   status: NULL, or a word the device can write (device memory, or mapped
  *   pinned host memory); when a transfer is queued, the in-kernel failure

@@ -23,6 +23,7 @@
 struct xfer_conn {
   int proto = 0, nch = 0, nslots = 0, fifo_loc = 0, ctrl_loc = 0;
   int lanes = 1, block = 256, xcd_pairing = 0, roles = 3, ordering = 0, p2p_read = 0;
+  bool coop = false;  // cooperative launches (xfer_attr.cooperative)
   uint32_t xcd_remap = 0;  // the kernels' remap: 0 dispatch order, 1 paired, 2 paired by XCD id
   size_t slot_bytes = 0, step_bytes = 0;
   uint32_t timeout_ms = 0;
@@ -608,6 +609,8 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
                 "send side (SIMPLE, FIFO and control words in HBM)");
   if (a.place_trials < 0 || a.place_trials > 8)
     return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: place_trials must be in 0..8");
+  if (a.cooperative != 0 && a.cooperative != 1)
+    return fail(XFER_ERR_INVALID_ARG, "xfer_conn_create: cooperative must be 0 or 1");
   if (a.place_trials > 1 && (zero_copy(proto) || fifo_loc != XFER_FIFO_DEVICE ||
                              a.ctrl_loc == XFER_CTRL_HOST || a.p2p_read))
     return fail(XFER_ERR_INVALID_ARG,
@@ -638,6 +641,7 @@ extern "C" int xfer_conn_create_ex(int proto, int nchannels, int nslots, size_t 
   c->roles = a.roles == 0 ? 3 : a.roles;
   c->ordering = a.ordering;
   c->p2p_read = a.p2p_read;
+  c->coop = a.cooperative == 1;
   c->slot_bytes = slot_bytes;
   c->step_bytes = proto == XFER_PROTO_LL ? slot_bytes / 2 : slot_bytes;
   c->timeout_ms = a.timeout_ms ? a.timeout_ms : kDefaultTimeoutMs;
@@ -928,7 +932,8 @@ extern "C" int xfer_run_loop(xfer_conn* c, const void* src, void* dst, size_t nb
   args.timeout_ticks = c->timeout_ticks;
   args.rx_wgs = rx_region_of(c);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = gate().run(c->device, s, [&] { return launch_run1(v, args, c->block, s); });
+  hipError_t e =
+      gate().run(c->device, s, [&] { return launch_run1(v, args, c->block, s, c->coop); });
   if (e != hipSuccess) return hip_fail(e, "xfer_run launch");
   relay_job(c, {uint64_t(nbytes)}, uint64_t(iters));
   commit_steps(c, add);
@@ -1004,7 +1009,8 @@ extern "C" int xfer_run_messages(xfer_conn* c, const void* src, void* dst, const
     args.rx_wgs = rx_region_of(c);
     for (size_t i = 0; i < cnt; ++i) args.msgs[i] = msgs[first + i];
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = gate().run(c->device, s, [&] { return launch_runL(v, args, c->block, s); });
+    hipError_t e =
+        gate().run(c->device, s, [&] { return launch_runL(v, args, c->block, s, c->coop); });
     if (e != hipSuccess) return hip_fail(e, "xfer_run_messages launch");
   }
   if (c->relay) {
@@ -1037,7 +1043,7 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
       if (conns[j] == c) return fail(XFER_ERR_INVALID_ARG, "xfer_run_batch: a connection appears twice");
     if (!first) first = c;
     if (kernel_proto(c) != kernel_proto(first) || c->scope != first->scope ||
-        c->ordering != first->ordering || c->block != first->block ||
+        c->ordering != first->ordering || c->block != first->block || c->coop != first->coop ||
         c->timeout_ticks != first->timeout_ticks || c->device != first->device)
       return fail(XFER_ERR_INVALID_ARG,
                   "xfer_run_batch: connections must share protocol (for LL, its line layout), "
@@ -1088,7 +1094,8 @@ extern "C" int xfer_run_batch(xfer_conn* const* conns, const void* const* src, v
   args.rx_wgs = rx_region;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e =
-      gate().run(first->device, s, [&] { return launch_runB(v, args, first->block, s); });
+      gate().run(first->device, s,
+                 [&] { return launch_runB(v, args, first->block, s, first->coop); });
   if (e != hipSuccess) return hip_fail(e, "xfer_run_batch launch");
   for (int i = 0; i < n; ++i) {
     if (!nbytes[i]) continue;
@@ -1107,7 +1114,8 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
   if (fwd == rev) return fail(XFER_ERR_INVALID_ARG, "xfer_run_pingpong: fwd and rev must differ");
   if (zero_copy(fwd->proto) || fwd->proto != rev->proto || fwd->nch != rev->nch ||
       fwd->slot_bytes != rev->slot_bytes || fwd->lanes != rev->lanes || fwd->block != rev->block ||
-      fwd->ordering != rev->ordering || fwd->device != rev->device || fwd->relay || rev->relay)
+      fwd->ordering != rev->ordering || fwd->device != rev->device || fwd->relay || rev->relay ||
+      fwd->coop != rev->coop)
     return fail(XFER_ERR_INVALID_ARG,
                 "xfer_run_pingpong: fwd and rev must be SIMPLE or LL with equal channels, slot "
                 "size, lanes, block size, ordering and device, and no relay");
@@ -1141,7 +1149,8 @@ extern "C" int xfer_run_pingpong(xfer_conn* fwd, xfer_conn* rev, const void* a, 
   args.xcd_remap = fwd->xcd_remap;
   args.timeout_ticks = std::max(fwd->timeout_ticks, rev->timeout_ticks);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = gate().run(fwd->device, s, [&] { return launch_ping(v, args, fwd->block, s); });
+  hipError_t e =
+      gate().run(fwd->device, s, [&] { return launch_ping(v, args, fwd->block, s, fwd->coop); });
   if (e != hipSuccess) return hip_fail(e, "xfer_run_pingpong launch");
   commit_steps(fwd, addf);
   commit_steps(rev, addr);

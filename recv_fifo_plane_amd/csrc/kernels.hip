@@ -1536,27 +1536,31 @@ PingFn pick_ping(const Variant& v) {
 
 }  // namespace
 
-// hipLaunchKernel reports this launch's own status (no sticky error state).
+// hipLaunchKernel and hipLaunchCooperativeKernel report this launch's own
+// status (no sticky error state).
 template <typename Fn, typename Args>
-static hipError_t launch(Fn fn, const Args& a, uint32_t grid, int block, hipStream_t s) {
+static hipError_t launch(Fn fn, const Args& a, uint32_t grid, int block, hipStream_t s,
+                         bool coop = false) {
   void* kargs[] = {const_cast<Args*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(block), kargs, 0, s);
+  const void* f = reinterpret_cast<const void*>(fn);
+  return coop ? hipLaunchCooperativeKernel(f, dim3(grid), dim3(block), kargs, 0, s)
+              : hipLaunchKernel(f, dim3(grid), dim3(block), kargs, 0, s);
 }
 
-hipError_t launch_run1(const Variant& v, const RunOne& a, int block, hipStream_t s) {
-  return launch(pick_run<1, 1>(v), a, a.total_wgs, block, s);
+hipError_t launch_run1(const Variant& v, const RunOne& a, int block, hipStream_t s, bool coop) {
+  return launch(pick_run<1, 1>(v), a, a.total_wgs, block, s, coop);
 }
 
-hipError_t launch_runL(const Variant& v, const RunList& a, int block, hipStream_t s) {
-  return launch(pick_run<1, kMaxMsgs>(v), a, a.total_wgs, block, s);
+hipError_t launch_runL(const Variant& v, const RunList& a, int block, hipStream_t s, bool coop) {
+  return launch(pick_run<1, kMaxMsgs>(v), a, a.total_wgs, block, s, coop);
 }
 
-hipError_t launch_runB(const Variant& v, const RunBatch& a, int block, hipStream_t s) {
-  return launch(pick_run<16, 1>(v), a, a.total_wgs, block, s);
+hipError_t launch_runB(const Variant& v, const RunBatch& a, int block, hipStream_t s, bool coop) {
+  return launch(pick_run<16, 1>(v), a, a.total_wgs, block, s, coop);
 }
 
-hipError_t launch_ping(const Variant& v, const PingArgs& a, int block, hipStream_t s) {
-  return launch(pick_ping(v), a, a.total_wgs, block, s);
+hipError_t launch_ping(const Variant& v, const PingArgs& a, int block, hipStream_t s, bool coop) {
+  return launch(pick_ping(v), a, a.total_wgs, block, s, coop);
 }
 
 // Whether the current device deals blocks to 8 XCDs in strict rotation on

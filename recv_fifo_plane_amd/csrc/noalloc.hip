@@ -167,10 +167,10 @@ extern "C" int xfer_run_noalloc(int proto, int nchannels, int nslots, size_t slo
   if (a.ordering != XFER_ORDER_COHERENT && a.ordering != XFER_ORDER_FENCED)
     return fail(XFER_ERR_INVALID_ARG, "xfer_run_noalloc: ordering must be COHERENT or FENCED");
   if ((a.ctrl_loc != XFER_CTRL_DEFAULT && a.ctrl_loc != XFER_CTRL_DEVICE) || a.roles != 0 ||
-      a.p2p_read != 0 || a.place_trials < 0 || a.place_trials > 1)
+      a.p2p_read != 0 || a.place_trials < 0 || a.place_trials > 1 || a.cooperative != 0)
     return fail(XFER_ERR_INVALID_ARG,
-                "xfer_run_noalloc: control words stay in HBM, both roles run, no P2P read and no "
-                "placement trials");
+                "xfer_run_noalloc: control words stay in HBM, both roles run, no P2P read, no "
+                "placement trials and no cooperative launch");
   const bool zc = proto == XFER_PROTO_ZEROCOPY || proto == XFER_PROTO_ZEROCOPY_DIRECT;
   const uint64_t room = kScratchBytes - kFifoOff;
   const uint64_t per_ch = zc ? 0 : uint64_t(nslots) * slot_bytes;

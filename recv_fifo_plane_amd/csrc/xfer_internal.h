@@ -184,10 +184,15 @@ struct Variant {
   int debug;     // 1: the debug variant (step trace, jitter)
 };
 
-hipError_t launch_run1(const Variant& v, const RunOne& a, int block, hipStream_t s);
-hipError_t launch_runL(const Variant& v, const RunList& a, int block, hipStream_t s);
-hipError_t launch_runB(const Variant& v, const RunBatch& a, int block, hipStream_t s);
-hipError_t launch_ping(const Variant& v, const PingArgs& a, int block, hipStream_t s);
+// coop: a cooperative grid (every workgroup resident at once, or refused).
+hipError_t launch_run1(const Variant& v, const RunOne& a, int block, hipStream_t s,
+                       bool coop = false);
+hipError_t launch_runL(const Variant& v, const RunList& a, int block, hipStream_t s,
+                       bool coop = false);
+hipError_t launch_runB(const Variant& v, const RunBatch& a, int block, hipStream_t s,
+                       bool coop = false);
+hipError_t launch_ping(const Variant& v, const PingArgs& a, int block, hipStream_t s,
+                       bool coop = false);
 // Workgroups of `block` threads the device can hold resident at once for
 // the variant's kernel of launch kind 0 (one transfer), 1 (a batch of
 // connections), 2 (the ping-pong) or 3 (a message list).

@@ -83,7 +83,7 @@ W5R = dict(name="relay_1ch_8MiB", proto="simple", nchannels=1, nslots=8, slot_by
            total_bytes=2 << 30)
 
 _ATTRS = ("wgs_per_channel", "block_threads", "ctrl_loc", "timeout_ms", "xcd_pairing", "ordering",
-          "p2p_read", "place_trials")
+          "p2p_read", "place_trials", "cooperative")
 
 
 def make_conn(cfg: dict, **override) -> X.Conn:

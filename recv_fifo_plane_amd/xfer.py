@@ -57,6 +57,7 @@ class xfer_attr(C.Structure):
         ("ordering", C.c_int),
         ("p2p_read", C.c_int),
         ("place_trials", C.c_int),
+        ("cooperative", C.c_int),
     ]
 
 
@@ -229,7 +230,7 @@ class Conn:
     def __init__(self, proto="simple", nchannels=1, nslots=8, slot_bytes=128 << 10,
                  fifo_loc="device", wgs_per_channel=0, block_threads=0, ctrl_loc=0,
                  timeout_ms=0, xcd_pairing=0, roles=0, ordering=0, p2p_read=0, place_trials=0,
-                 _handle=None):
+                 cooperative=0, _handle=None):
         self.proto = PROTOS[proto] if isinstance(proto, str) else int(proto)
         self.nchannels = int(nchannels)
         self.nslots = int(nslots)
@@ -243,7 +244,7 @@ class Conn:
         attr = make_attr(wgs_per_channel=wgs_per_channel, block_threads=block_threads,
                          ctrl_loc=ctrl_loc, timeout_ms=timeout_ms, xcd_pairing=xcd_pairing,
                          roles=roles, ordering=ordering, p2p_read=p2p_read,
-                         place_trials=place_trials)
+                         place_trials=place_trials, cooperative=cooperative)
         h = _vp()
         check(lib().xfer_conn_create_ex(self.proto, self.nchannels, self.nslots, self.slot_bytes,
                                         self.fifo_loc, C.byref(attr), C.byref(h)))

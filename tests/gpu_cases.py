@@ -93,7 +93,7 @@ def compare_state(conn, oconn, nch: int, what: str) -> None:
 def run_transfers(proto: str, nch: int, nslots: int, slot_bytes: int, sizes, *,
                   fifo_loc="device", lanes=1, block=0, src_off=0, dst_off=0, kind="uint8",
                   seed=1, ctrl_loc=0, xcd_pairing=0, ordering=0, p2p_read=0, jitter=0,
-                  place_trials=0, oracle_order="pages", label="") -> None:
+                  place_trials=0, oracle_order="pages", cooperative=0, label="") -> None:
     """Each size is one xfer_run on the same connection; after every run the
     whole destination buffer (guards included) must equal the oracle's (the
     oracle in program order `oracle_order`)."""
@@ -102,11 +102,13 @@ def run_transfers(proto: str, nch: int, nslots: int, slot_bytes: int, sizes, *,
     what = "%s %s nch=%d nslots=%d slot=%d lanes=%d block=%d off=(%d,%d) %s ord=%d read=%d" % (
         label, proto, nch, nslots, slot_bytes, lanes, block, src_off, dst_off, fifo_loc, ordering,
         p2p_read) + (" jitter=%#x" % jitter if jitter else "") + (
-        " place_trials=%d" % place_trials if place_trials else "")
+        " place_trials=%d" % place_trials if place_trials else "") + (
+        " cooperative" if cooperative else "")
     log("case: " + what + " sizes=" + str(list(sizes)[:6]))
     conn = xf.Conn(proto, nch, nslots, slot_bytes, fifo_loc, wgs_per_channel=lanes,
                    block_threads=block, ctrl_loc=ctrl_loc, xcd_pairing=xcd_pairing,
-                   ordering=ordering, p2p_read=p2p_read, place_trials=place_trials)
+                   ordering=ordering, p2p_read=p2p_read, place_trials=place_trials,
+                   cooperative=cooperative)
     if place_trials:
         # the kept candidate must look like a new connection
         for c in range(nch):

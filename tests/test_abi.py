@@ -117,7 +117,8 @@ def test_attribute_struct_matches_the_header():
 
 @pytest.mark.parametrize("attr", [dict(wgs_per_channel=17), dict(block_threads=96),
                                   dict(block_threads=2048), dict(ctrl_loc=3), dict(roles=3),
-                                  dict(xcd_pairing=2)])
+                                  dict(xcd_pairing=2), dict(cooperative=2),
+                                  dict(cooperative=-1)])
 def test_create_rejects_bad_attributes(attr):
     with pytest.raises(xf.XferError) as e:
         xf.Conn("simple", 1, 8, 128, **attr)
@@ -207,6 +208,7 @@ def test_library_loads_where_torch_brought_the_hip_runtime():
     ((0, 1, 8, 4096), dict(ctrl_loc=X.XFER_CTRL_HOST)),
     ((1, 1, 8, 4096), dict(place_trials=2)),
     ((0, 1, 8, 4096), dict(wgs_per_channel=17)),
+    ((0, 1, 8, 4096), dict(cooperative=1)),                 # no cooperative grids
 ])
 def test_noalloc_rejects_bad_arguments_before_touching_a_gpu(args, attr):
     a = X.make_attr(**attr)
