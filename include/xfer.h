@@ -42,7 +42,9 @@
  *     captured runs on one stream, or use xfer_run_noalloc).  Kernels of
  *     other code running beside a launch only delay the dispatch of its
  *     workgroups; a kernel that waits on one of this library's launches must
- *     not hold the GPU's resources meanwhile.  xfer_run_noalloc does not
+ *     not hold the GPU's resources meanwhile.  Connections created with
+ *     xfer_attr.cooperative launch cooperative grids, which the runtime
+ *     starts only with every workgroup resident.  xfer_run_noalloc does not
  *     take part in this order (see there).
  *   - Step counters are 64-bit, start at 0 when the connection is created,
  *     and persist across runs; step g (0-based) publishes tail = g+1.
