@@ -72,3 +72,39 @@ def test_noalloc_rejects_a_fifo_beyond_its_array():
     X.run_noalloc("simple", 1, 8, room // 8, a, b, 4096)  # exactly the room: accepted
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# The callers the entry point is for include code under HIP graph capture:
+# one call captured (its clearing kernel, the transfer and the report kernel
+# become graph nodes) must redo the whole transfer on every replay, with the
+# program's own eager work and synchronisations between the replays.
+@pytest.mark.parametrize("proto,nch,nslots,slot,lanes,block", [
+    ("simple", 4, 4, 65536, 2, 256),
+    ("ll", 2, 4, 8192, 2, 1024),
+    ("zc", 4, 1, 65536, 2, 128),
+])
+def test_noalloc_replays_in_a_captured_graph(proto, nch, nslots, slot, lanes, block):
+    import torch
+    n = (1 << 20) + 37
+    log("case: graph %s" % proto)
+    a = to_dev(synth.uint8_uniform(n, 9))
+    b = torch.zeros_like(a)
+    status = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    kw = dict(wgs_per_channel=lanes, block_threads=block)
+    # the first call on a device takes the array's address and the capacity
+    X.run_noalloc(proto, nch, nslots, slot, a, b, n, status=status, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and int(status.item()) == 0
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        X.run_noalloc(proto, nch, nslots, slot, a, b, n, status=status, **kw)
+    for r in range(4):
+        # eager work between replays: new source bytes, cleared destination
+        a.copy_(to_dev(synth.uint8_uniform(n, 100 + r)))
+        b.zero_()
+        status.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), (proto, "replay", r)
+        assert int(status.item()) == 0, (proto, "replay", r, int(status.item()))
