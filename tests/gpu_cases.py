@@ -93,10 +93,9 @@ def compare_state(conn, oconn, nch: int, what: str) -> None:
 def run_transfers(proto: str, nch: int, nslots: int, slot_bytes: int, sizes, *,
                   fifo_loc="device", lanes=1, block=0, src_off=0, dst_off=0, kind="uint8",
                   seed=1, ctrl_loc=0, xcd_pairing=0, ordering=0, p2p_read=0, jitter=0,
-                  place_trials=0, oracle_order="pages", cooperative=0, label="") -> None:
+                  place_trials=0, cooperative=0, label="") -> None:
     """Each size is one xfer_run on the same connection; after every run the
-    whole destination buffer (guards included) must equal the oracle's (the
-    oracle in program order `oracle_order`)."""
+    whole destination buffer (guards included) must equal the oracle's."""
     import recv_fifo_plane_amd as xf
     torch = torch_mod()
     what = "%s %s nch=%d nslots=%d slot=%d lanes=%d block=%d off=(%d,%d) %s ord=%d read=%d" % (
@@ -118,7 +117,6 @@ def run_transfers(proto: str, nch: int, nslots: int, slot_bytes: int, sizes, *,
     if jitter:
         conn.set_jitter(jitter)
     ocn = oracle.Conn(oracle_proto(proto, fifo_loc), nch, nslots, slot_bytes)
-    ocn.set_order(oracle_order)
     try:
         for t, n in enumerate(sizes):
             A = payload(kind, n, seed * 7919 + t)

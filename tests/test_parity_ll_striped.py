@@ -31,25 +31,11 @@ def _sizes(slot, nch):
     return [1, 7, 4099, nch * S * 5 + 5, 100_001, nch * S * 2]
 
 
-def _group(nslots, slot, lanes, block):
-    """Steps a striped lane covers at once: its stripe q is the step's lines
-    over the lanes, rounded up to a power of two of at least a wave, and
-    its block holds block / q of them, capped at nslots."""
-    q = 64
-    while q * lanes < slot // 8:
-        q *= 2
-    return min(block // q, nslots)
-
-
 @pytest.mark.parametrize("shape", SHAPES, ids=["-".join(map(str, s)) for s in SHAPES])
-@pytest.mark.parametrize("order", ["pages", "kernel"])
-def test_striped_transfers_match_oracle(shape, order):
-    # against the pages' step-at-a-time order, and against the oracle run
-    # in the kernels' own order (aligned groups, one head store per group)
+def test_striped_transfers_match_oracle(shape):
     nch, nslots, slot, lanes, block, loc = shape
-    oo = "pages" if order == "pages" else "ll_group%d" % _group(nslots, slot, lanes, block)
     run_transfers("ll", nch, nslots, slot, _sizes(slot, nch), fifo_loc=loc, lanes=lanes,
-                  block=block, kind="int32", oracle_order=oo, label="striped " + oo)
+                  block=block, kind="int32", label="striped")
 
 
 @pytest.mark.parametrize("shape", SHAPES[:3], ids=["-".join(map(str, s)) for s in SHAPES[:3]])
